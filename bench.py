@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse paged attention forward on one MI355X.
+
+One step = one call of the whole hot path (KV-set metadata, page-table
+gather, scores, online softmax with the sink, PV, epilogue and, with split-KV,
+the exact LSE merge) over one batch of synthetic input already resident in
+HBM.  The default workload is "Decode CSA": batch 32, one query per sequence
+at context 4096, 128 query heads sharing one KV head, D 128, bf16, page 64,
+window 128 + top-k 512 of 1024 ratio-4 groups.
+
+Inputs are replicated on the device and the timed steps rotate through the
+replicas, so the KV rows each step reads are not resident in the 256 MB
+memory-side cache (the working set rotated through is > 512 MB).
+
+Prints one JSON line (see --help for options).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def algorithmic_work(p, counts):
+    """Bytes and FLOPs the method must move / compute for one call.
+
+    Per query: Q and O (bf16), LSE (fp32), every KV entry of its set once
+    (K and V rows, plus the fp32 per-token scales for e4m3 rows) and the list
+    indices; FLOPs = 4 * Hq * D * |KV set|.  Page-table reads, split
+    partials and masked work are overhead and not counted."""
+    Hq, Hkv, D = p.num_q_heads, p.num_kv_heads, p.head_dim
+    raw_entry = Hkv * 2 * D * 2
+    cmp_entry = Hkv * 2 * D * (1 if p.cmp_fp8 else 2) + (Hkv * 2 * 4 if p.cmp_fp8 else 0)
+    win_len = counts[:, 1].astype("int64")
+    n_sel = counts[:, 3].astype("int64")
+    nq = counts.shape[0]
+    kv_bytes = int((win_len * raw_entry).sum() + (n_sel * cmp_entry).sum())
+    idx_bytes = int(n_sel.sum() * 4) if p.topk > 0 else 0
+    qo_bytes = nq * Hq * D * 2 * 2 + nq * Hq * 4
+    flops = int(4 * Hq * D * (win_len + n_sel).sum())
+    return kv_bytes + idx_bytes + qo_bytes, flops, int((win_len + n_sel).sum())
+
+
+def cpu_baseline(p, budget_s):
+    """Time the FP64 oracle on the host cores over a bounded sample."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    nq = p.num_queries
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        for i in range(nq):
+            oracle.attention(p, [i])
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} queries of the same workload (first {min(done, nq)} distinct), "
+                      f"{dt:.1f} s single process, numpy fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_csa",
+                    choices=["decode_csa", "decode_hca", "mixed_fp8", "prefill_csa", "tiny"])
+    ap.add_argument("--splits", type=int, default=0, help="0 = the default for the workload")
+    ap.add_argument("--rotate-mb", type=float, default=640.0,
+                    help="total size of the input replicas the timed steps rotate through")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--no-json-extra", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from sparse_paged_attention_amd import api, synth, _lib
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    _lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    p = synth.make_workload(args.workload)
+    default_splits = {"decode_csa": 8, "decode_hca": 4, "mixed_fp8": 8, "prefill_csa": 1, "tiny": 1}
+    splits = args.splits or default_splits[args.workload]
+    base = api.DeviceProblem.from_problem(p, device=dev)
+
+    # metadata from the library itself, for the byte/FLOP accounting
+    cap = p.window + (p.topk if p.topk else max(int(n) // max(p.ratio, 1) for n in p.seq_lens)) + 1
+    _, counts = api.build_gather(base, cap)
+    counts = counts.cpu().numpy()
+    alg_bytes, alg_flops, kv_entries = algorithmic_work(p, counts)
+
+    # replicas: the KV rows read per step plus Q/O, rotated so the set is HBM-cold
+    touched = alg_bytes
+    reps = max(1, math.ceil(args.rotate_mb * 1e6 / max(touched, 1)))
+    pool_bytes = sum(t.numel() * t.element_size() for t in (base.k_raw, base.v_raw, base.k_cmp, base.v_cmp)
+                     if t is not None)
+    reps = min(reps, max(1, int(64e9 // max(pool_bytes, 1))))
+    replicas = []
+    for r in range(reps):
+        if r == 0:
+            dp = base
+        else:
+            dp = api.DeviceProblem(**{k: (v.clone() if isinstance(v, torch.Tensor) else v)
+                                      for k, v in base.__dict__.items()})
+        a = dp.args(splits)
+        o = torch.empty((p.num_queries, p.num_q_heads, p.head_dim), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((p.num_queries, p.num_q_heads), dtype=torch.float32, device=dev)
+        need = api.workspace_size(a)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if need else None
+        replicas.append((dp, a, o, lse, ws))
+
+    lib = _lib.load()
+    fn = lib.attn_fwd_decode if p.mode == "decode" else lib.attn_fwd_prefill
+    import ctypes
+    stream = torch.cuda.current_stream().cuda_stream
+
+    prepared = []
+    for dp, a, o, lse, ws in replicas:
+        a.o = o.data_ptr()
+        a.lse = lse.data_ptr()
+        a.workspace = ws.data_ptr() if ws is not None else None
+        a.workspace_bytes = ws.numel() if ws is not None else 0
+        prepared.append(ctypes.byref(a))
+
+    def step(k):
+        st = fn(prepared[k % reps], stream)
+        if st != 0:
+            _lib.check(st)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    t_wall0 = time.perf_counter()
+    ev[0].record()
+    for k in range(K):
+        step(k)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    per = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(K)])   # ms
+    total_ms = ev[0].elapsed_time(ev[K])
+    ms_per_step = total_ms / K
+
+    # the merge kernel alone, timed the same way, to isolate the attention kernel
+    merge_ms = 0.0
+    if splits > 1:
+        dp, a, o, lse, ws = replicas[0]
+        rows = p.num_queries * p.num_q_heads
+        o_bytes = rows * p.head_dim * 4 * splits
+        lse_off = ((o_bytes + 255) // 256) * 256
+        me0, me1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(5):
+            lib.attn_merge_lse(ws.data_ptr(), ws.data_ptr() + lse_off, splits, rows, p.head_dim,
+                               p.num_q_heads, dp.sink.data_ptr() if dp.sink is not None else None,
+                               o.data_ptr(), lse.data_ptr(), stream)
+        me0.record()
+        for _ in range(K):
+            lib.attn_merge_lse(ws.data_ptr(), ws.data_ptr() + lse_off, splits, rows, p.head_dim,
+                               p.num_q_heads, dp.sink.data_ptr() if dp.sink is not None else None,
+                               o.data_ptr(), lse.data_ptr(), stream)
+        me1.record()
+        torch.cuda.synchronize()
+        merge_ms = me0.elapsed_time(me1) / K
+    attn_ms = max(ms_per_step - merge_ms, 1e-9)
+
+    nq = p.num_queries
+    value = nq / (ms_per_step / 1e3)
+    decode = p.mode == "decode"
+    if decode:
+        roof = {"bound": "hbm", "achieved": alg_bytes / (attn_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": alg_flops / (attn_ms / 1e3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "attn_fwd_kernel"
+    roof["kernel_ms"] = attn_ms
+    roof["algorithmic_bytes_per_launch"] = alg_bytes
+    roof["algorithmic_flops_per_launch"] = alg_flops
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(p, args.cpu_budget)
+
+    out = {
+        "metric": "decode queries/s + HBM GB/s; prefill TFLOP/s (frac. of MI355X peak)",
+        "value": value,
+        "unit": "queries/s" if decode else "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if not p.cmp_fp8 else "bf16+e4m3",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": p.num_seqs, "queries": nq,
+                   "q_heads": p.num_q_heads, "kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
+                   "page_size": p.page_size, "window": p.window, "ratio": p.ratio, "topk": p.topk,
+                   "kv_entries": kv_entries, "num_splits": splits, "replicas": reps},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if not args.no_json_extra:
+        out["timing"] = {"p10_ms": float(np.percentile(per, 10)), "p50_ms": float(np.percentile(per, 50)),
+                         "p90_ms": float(np.percentile(per, 90)), "merge_ms": merge_ms,
+                         "host_wall_ms_per_step": wall / K * 1e3,
+                         "tflops": alg_flops / (ms_per_step / 1e3) / 1e12,
+                         "gbs_step": alg_bytes / (ms_per_step / 1e3) / 1e9}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * spa.h — C ABI of the MI355X (gfx950) sparse paged attention library.
+ *
+ * The operation (RL-Kernel PR "Roadmap item 24: joint compressed/window
+ * attention with sink", section "Reuse and arithmetic"; ATOM PR "test: add
+ * block-level DeepSeek-V4 attention test", sections "What the reference
+ * proves" and "Validation"): for every query token t of sequence b and every
+ * query head h (KV head g = h / (Hq / Hkv)), the KV set is
+ *
+ *   compressed rows  the ids listed for the query (a top-k "CSA" layer), or
+ *                    every complete group (an all-groups "HCA" layer), where
+ *                    group c of ratio r is complete at t when r*(c+1) <= t+1;
+ *                    none when ratio = 0 (a dense layer);
+ *   window rows      raw positions max(0, t-W+1) .. t,
+ *
+ * in this canonical order ([compressed in list order || window ascending]).
+ * Each logical position p (or compressed id c) is translated through its
+ * sequence's page table: row = page_table[b][p / P] * P + p % P, in 64-bit
+ * arithmetic (RL-Kernel "Fixed paged CK attention on ROCm").  Then
+ *
+ *   s_j = scale * <q_h, k_j>
+ *   O   = sum_j exp(s_j) v_j / (sum_j exp(s_j) + exp(sink_h))
+ *   LSE = ln(sum_j exp(s_j) + exp(sink_h))
+ *
+ * The sink logit is per head, is not scaled, and has no value row.  O is
+ * written as bf16 (round to nearest even), LSE as fp32 natural log.
+ *
+ * Conventions for every call:
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, keeps no global state except a thread-local error
+ *    string, never synchronises, and enqueues its kernels on `stream` (a
+ *    hipStream_t; NULL = the null stream).  Calls may be captured in a HIP
+ *    graph.
+ *  - Host-side validation runs before any HIP call and returns a distinct
+ *    negative status per fault class (RL-Kernel joint attention PR, review of
+ *    the guard matrix: one distinct error per fault).  attn_last_error()
+ *    returns a message naming the offending argument.  Nothing is retried and
+ *    there is no fallback path.
+ *  - Per-element metadata (sequence ids, positions, compressed ids, page ids,
+ *    list counts) is checked on the device.  A violating entry is masked
+ *    (never dereferenced) and, when err_flag is not NULL, a bit is OR-ed into
+ *    *err_flag: 1 = query sequence/position, 2 = compressed id outside the
+ *    complete groups, 4 = page id outside the pool or page-table column out of
+ *    range, 8 = list count outside [0, topk].  Page-table columns past the
+ *    last page a query needs are never read (RL-Kernel "Fixed paged CK
+ *    attention on ROCm": unused page-table columns are not loaded).
+ *  - Inputs are read-only.  After SPA_ERR_LAUNCH the outputs and the
+ *    workspace are undefined.
+ */
+#ifndef SPA_H_
+#define SPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spa_status {
+  SPA_OK = 0,
+  SPA_ERR_NULL = -1,        /* a required pointer is NULL                          */
+  SPA_ERR_SHAPE = -2,       /* a count or dimension is out of range / inconsistent */
+  SPA_ERR_DTYPE = -3,       /* unknown dtype code, or raw KV not bf16              */
+  SPA_ERR_UNSUPPORTED = -4, /* valid request this library does not implement
+                               (head_dim other than 64/128, ...)                  */
+  SPA_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                    */
+  SPA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than attn_workspace_size  */
+  SPA_ERR_SPLITS = -7,      /* num_splits outside [1, SPA_MAX_SPLITS]              */
+  SPA_ERR_LAUNCH = -8,      /* HIP reported an error when launching                */
+  SPA_ERR_MODE = -9         /* decode/prefill query arguments do not match the call */
+} spa_status;
+
+typedef enum spa_dtype {
+  SPA_BF16 = 0,
+  SPA_FP8_E4M3_OCP = 1      /* OCP e4m3: bias 7, no inf, 0x7F/0xFF NaN, max 448 */
+} spa_dtype;
+
+#define SPA_MAX_SPLITS 64
+
+typedef struct spa_fwd_args {
+  int32_t num_seqs;       /* B                                                   */
+  int32_t num_queries;    /* Nq; decode: must equal B                            */
+  int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads                      */
+  int32_t num_kv_heads;   /* Hkv                                                 */
+  int32_t head_dim;       /* D in {64, 128}                                      */
+  int32_t page_size;      /* P >= 1 tokens (rows) per page, same for both caches */
+  int32_t window;         /* W >= 0 raw tokens ending at the query token         */
+  int32_t ratio;          /* r >= 0 tokens per compressed group; 0 = no groups   */
+  int32_t topk;           /* list capacity (row stride of cmp_idx); 0 = every
+                             complete group, no list                              */
+  float scale;            /* multiplies q.k; not applied to the sink             */
+  int32_t raw_dtype;      /* spa_dtype: must be SPA_BF16                         */
+  int32_t cmp_dtype;      /* spa_dtype: SPA_BF16 or SPA_FP8_E4M3_OCP             */
+  int32_t num_splits;     /* 1 = one pass; >1 = split-KV partials + LSE merge    */
+
+  const void *q;          /* bf16 [Nq, Hq, D]                                    */
+  const void *k_raw;      /* bf16 [raw_pages, P, Hkv, D]                         */
+  const void *v_raw;      /* bf16 [raw_pages, P, Hkv, D] (may alias k_raw)       */
+  const void *k_cmp;      /* bf16 or e4m3 [cmp_pages, P, Hkv, D]; NULL if r = 0  */
+  const void *v_cmp;      /* same layout as k_cmp (may alias it)                 */
+  const float *k_cmp_scale; /* f32 [cmp_pages, P, Hkv]: FP8 only, else NULL     */
+  const float *v_cmp_scale; /* f32 [cmp_pages, P, Hkv]: FP8 only, else NULL     */
+  int64_t raw_pages;      /* pages in the raw pool (bound for page ids)          */
+  int64_t cmp_pages;      /* pages in the compressed pool                        */
+  const int32_t *raw_pt;  /* [B, raw_pt_stride] page ids                         */
+  const int32_t *cmp_pt;  /* [B, cmp_pt_stride]; NULL if r = 0                   */
+  int32_t raw_pt_stride;
+  int32_t cmp_pt_stride;
+  const int32_t *seq_lens;  /* [B] tokens in each sequence's raw cache           */
+  const int32_t *query_seq; /* prefill [Nq] sequence of each query; decode NULL  */
+  const int32_t *query_pos; /* prefill [Nq] position of each query; decode NULL
+                               (decode query b sits at position seq_lens[b]-1)    */
+  const int32_t *cmp_idx;   /* [Nq, topk] logical compressed ids (list order),
+                               when topk > 0                                      */
+  const int32_t *cmp_cnt;   /* [Nq] entries used in each list, when topk > 0     */
+  const float *sink;        /* f32 [Hq] sink logits, or NULL (= -inf, no sink)   */
+
+  void *o;                  /* out: bf16 [Nq, Hq, D]                             */
+  float *lse;               /* out: f32 [Nq, Hq], natural log, sink included;
+                               may be NULL                                        */
+  int32_t *err_flag;        /* device i32 or NULL, see the conventions above     */
+  void *workspace;          /* num_splits > 1: attn_workspace_size() bytes       */
+  size_t workspace_bytes;
+} spa_fwd_args;
+
+/* Bytes of workspace the call needs: 0 when num_splits == 1, otherwise the
+   sink-free split partials f32 O [S, Nq, Hq, D] and f32 LSE [S, Nq, Hq].
+   Returns 0 for a NULL or inconsistent argument block. */
+size_t attn_workspace_size(const spa_fwd_args *args);
+
+/* Decode: one query per sequence at position seq_lens[b] - 1
+   (query_seq = query_pos = NULL, num_queries = num_seqs).  With num_splits
+   S > 1 every query's canonical KV list is cut into S contiguous slices, each
+   slice yields a sink-free partial (O_s, LSE_s) in the workspace, and the
+   partials plus the sink are combined exactly as attn_merge_lse does. */
+spa_status attn_fwd_decode(const spa_fwd_args *args, void *stream);
+
+/* Prefill / chunked prefill / multi-token decode: query i sits at
+   (query_seq[i], query_pos[i]); every KV row it needs, its own and those of
+   tokens of the same chunk included, is already in the paged caches. */
+spa_status attn_fwd_prefill(const spa_fwd_args *args, void *stream);
+
+/* Exact merge of sink-free partials (RL-Kernel PR "[WS2] CP-aware Attention
+   contract", Behavior: deterministic (out, lse) reduction; tessera "Block
+   AttnRes" PR: softmax_merge).  For every row r (r = query * Hq + head):
+     LSE[r] = ln(sum_s exp(lse_parts[s][r]) + exp(sink[r % num_q_heads]))
+     O[r]   = sum_s exp(lse_parts[s][r] - LSE[r]) * o_parts[s][r]
+   An empty part has LSE = -inf and weight 0.  If every term is -inf the row
+   gets O = 0, LSE = -inf.  o_parts f32 [num_parts, rows, head_dim],
+   lse_parts f32 [num_parts, rows] (device); sink f32 [num_q_heads] or NULL;
+   o_out bf16 [rows, head_dim]; lse_out f32 [rows] or NULL.
+   head_dim in {64, 128}; 1 <= num_parts <= SPA_MAX_SPLITS. */
+spa_status attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t num_parts,
+                          int64_t rows, int32_t head_dim, int32_t num_q_heads,
+                          const float *sink, void *o_out, float *lse_out, void *stream);
+
+/* Gather metadata, computed on the device by the same translation code the
+   attention kernels use: for each query, rows_out[i, :] holds the physical
+   row index (within its pool) of every KV entry in canonical order — the
+   n_sel compressed rows, then the win_len window rows — padded with -1 up to
+   cap; counts_out[i] = {win_lo, win_len, n_c, n_sel}.  A masked (invalid)
+   entry is reported as -2.  `decode` selects the decode query convention.
+   rows_out int64 [Nq, cap], counts_out int32 [Nq, 4] (device).  Entries past
+   cap are not written; cap >= window + max list length suffices. */
+spa_status attn_build_gather(const spa_fwd_args *args, int32_t decode, int32_t cap,
+                             int64_t *rows_out, int32_t *counts_out, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *attn_last_error(void);
+
+/* Library ABI version (this header: 1). */
+int32_t attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPA_H_ */

@@ -1,0 +1,62 @@
+"""Build libspa.so (the HIP library behind include/spa.h) for gfx950, in-tree.
+
+Usage: python -m sparse_paged_attention_amd.build   (or build() from Python)
+"""
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libspa.so")
+BUILD_DIR = os.path.join(PKG, "_build")
+
+SOURCES = ["spa_api.cpp", "spa_attention.hip", "spa_merge.hip", "spa_gather.hip"]
+ARCH = "gfx950"
+# Packed fp32 VALU ops are disabled for every HIP source file.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+          "-Wall", "-Wno-unused-result"]
+
+
+def _hipcc():
+    cand = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(cand):
+        raise RuntimeError("hipcc not found")
+    return cand
+
+
+def _compile(src):
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{out}")
+    return obj, out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libspa.so; always rebuilds."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    for _, out in results:
+        if verbose and out.strip():
+            print(out)
+    objs = [o for o, _ in results]
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,232 @@
+// C-ABI entry points of libspa: host-side validation, workspace sizing and
+// kernel launches.  See include/spa.h for the contract of every call.
+//
+// Validation follows the guard-matrix discussion in the RL-Kernel joint
+// attention PR (review of test_joint_attention_rocm.py): every fault class
+// returns its own status code before any HIP call, and the message names the
+// argument.  There are no retries and no fallback path.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "spa.h"
+#include "spa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+spa_status fail(spa_status code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+spa_status ok() {
+  g_last_error.clear();
+  return SPA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape/dtype/pointer checks shared by the attention calls and the gather
+// export.  `need_outputs` is false for the gather export.
+spa_status validate(const spa_fwd_args *a, bool decode, bool need_outputs) {
+  if (a == nullptr) return fail(SPA_ERR_NULL, "args is NULL");
+  if (a->num_seqs < 1) return fail(SPA_ERR_SHAPE, "num_seqs must be >= 1 (got %d)", a->num_seqs);
+  if (a->num_queries < 0) return fail(SPA_ERR_SHAPE, "num_queries must be >= 0 (got %d)", a->num_queries);
+  if (a->num_q_heads < 1 || a->num_kv_heads < 1)
+    return fail(SPA_ERR_SHAPE, "num_q_heads (%d) and num_kv_heads (%d) must be >= 1", a->num_q_heads,
+                a->num_kv_heads);
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return fail(SPA_ERR_SHAPE, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", a->num_q_heads,
+                a->num_kv_heads);
+  if (a->page_size < 1) return fail(SPA_ERR_SHAPE, "page_size must be >= 1 (got %d)", a->page_size);
+  if (a->window < 0) return fail(SPA_ERR_SHAPE, "window must be >= 0 (got %d)", a->window);
+  if (a->ratio < 0) return fail(SPA_ERR_SHAPE, "ratio must be >= 0 (got %d)", a->ratio);
+  if (a->topk < 0) return fail(SPA_ERR_SHAPE, "topk must be >= 0 (got %d)", a->topk);
+  if (a->topk > 0 && a->ratio == 0) return fail(SPA_ERR_SHAPE, "topk > 0 needs ratio > 0");
+  if (a->raw_pt_stride < 1) return fail(SPA_ERR_SHAPE, "raw_pt_stride must be >= 1");
+  if (a->raw_pages < 1) return fail(SPA_ERR_SHAPE, "raw_pages must be >= 1");
+  if (a->ratio > 0 && (a->cmp_pt_stride < 1 || a->cmp_pages < 1))
+    return fail(SPA_ERR_SHAPE, "ratio > 0 needs cmp_pt_stride >= 1 and cmp_pages >= 1");
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(SPA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", a->head_dim);
+  if (a->raw_dtype != SPA_BF16) return fail(SPA_ERR_DTYPE, "raw_dtype must be SPA_BF16 (got %d)", a->raw_dtype);
+  if (a->cmp_dtype != SPA_BF16 && a->cmp_dtype != SPA_FP8_E4M3_OCP)
+    return fail(SPA_ERR_DTYPE, "cmp_dtype %d unknown", a->cmp_dtype);
+  if (a->num_splits < 1 || a->num_splits > SPA_MAX_SPLITS)
+    return fail(SPA_ERR_SPLITS, "num_splits %d outside [1, %d]", a->num_splits, SPA_MAX_SPLITS);
+  if ((int64_t)a->num_queries * a->num_splits > 0x7FFFFFFFLL)
+    return fail(SPA_ERR_SHAPE, "num_queries * num_splits exceeds the launch grid");
+
+  if (a->q == nullptr) return fail(SPA_ERR_NULL, "q is NULL");
+  if (a->k_raw == nullptr || a->v_raw == nullptr) return fail(SPA_ERR_NULL, "k_raw/v_raw is NULL");
+  if (a->raw_pt == nullptr) return fail(SPA_ERR_NULL, "raw_pt is NULL");
+  if (a->seq_lens == nullptr) return fail(SPA_ERR_NULL, "seq_lens is NULL");
+  if (a->ratio > 0) {
+    if (a->k_cmp == nullptr || a->v_cmp == nullptr) return fail(SPA_ERR_NULL, "k_cmp/v_cmp is NULL");
+    if (a->cmp_pt == nullptr) return fail(SPA_ERR_NULL, "cmp_pt is NULL");
+    if (a->cmp_dtype == SPA_FP8_E4M3_OCP && (a->k_cmp_scale == nullptr || a->v_cmp_scale == nullptr))
+      return fail(SPA_ERR_NULL, "FP8 compressed KV needs k_cmp_scale and v_cmp_scale");
+  }
+  if (a->topk > 0 && (a->cmp_idx == nullptr || a->cmp_cnt == nullptr))
+    return fail(SPA_ERR_NULL, "topk > 0 needs cmp_idx and cmp_cnt");
+  if (need_outputs && a->o == nullptr) return fail(SPA_ERR_NULL, "o is NULL");
+
+  if (decode) {
+    if (a->query_seq != nullptr || a->query_pos != nullptr)
+      return fail(SPA_ERR_MODE, "decode takes no query_seq/query_pos (queries sit at seq_lens-1)");
+    if (a->num_queries != a->num_seqs)
+      return fail(SPA_ERR_MODE, "decode needs num_queries == num_seqs (%d vs %d)", a->num_queries, a->num_seqs);
+  } else {
+    if (a->query_seq == nullptr || a->query_pos == nullptr)
+      return fail(SPA_ERR_MODE, "prefill needs query_seq and query_pos");
+  }
+
+  if (!aligned16(a->q) || !aligned16(a->k_raw) || !aligned16(a->v_raw))
+    return fail(SPA_ERR_ALIGN, "q, k_raw and v_raw must be 16-byte aligned");
+  if (a->ratio > 0 && (!aligned16(a->k_cmp) || !aligned16(a->v_cmp)))
+    return fail(SPA_ERR_ALIGN, "k_cmp and v_cmp must be 16-byte aligned");
+  if (need_outputs && !aligned16(a->o)) return fail(SPA_ERR_ALIGN, "o must be 16-byte aligned");
+  return SPA_OK;
+}
+
+size_t workspace_bytes_for(const spa_fwd_args *a) {
+  if (a->num_splits <= 1) return 0;
+  const size_t rows = (size_t)a->num_queries * (size_t)a->num_q_heads;
+  const size_t o = rows * (size_t)a->head_dim * sizeof(float) * (size_t)a->num_splits;
+  const size_t l = rows * sizeof(float) * (size_t)a->num_splits;
+  return ((o + 255) / 256) * 256 + l;
+}
+
+spa::Params make_params(const spa_fwd_args *a) {
+  spa::Params p{};
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.k_raw = static_cast<const uint8_t *>(a->k_raw);
+  p.v_raw = static_cast<const uint8_t *>(a->v_raw);
+  p.k_cmp = static_cast<const uint8_t *>(a->k_cmp);
+  p.v_cmp = static_cast<const uint8_t *>(a->v_cmp);
+  p.k_cmp_scale = a->k_cmp_scale;
+  p.v_cmp_scale = a->v_cmp_scale;
+  p.raw_pages = a->raw_pages;
+  p.cmp_pages = a->ratio > 0 ? a->cmp_pages : 0;
+  p.raw_pt = a->raw_pt;
+  p.cmp_pt = a->cmp_pt;
+  p.seq_lens = a->seq_lens;
+  p.query_seq = a->query_seq;
+  p.query_pos = a->query_pos;
+  p.cmp_idx = a->cmp_idx;
+  p.cmp_cnt = a->cmp_cnt;
+  p.sink = a->sink;
+  p.o = static_cast<uint16_t *>(a->o);
+  p.lse = a->lse;
+  p.err_flag = a->err_flag;
+  p.raw_pt_stride = a->raw_pt_stride;
+  p.cmp_pt_stride = a->ratio > 0 ? a->cmp_pt_stride : 1;
+  p.num_seqs = a->num_seqs;
+  p.num_queries = a->num_queries;
+  p.hq = a->num_q_heads;
+  p.hkv = a->num_kv_heads;
+  p.head_dim = a->head_dim;
+  p.page_size = a->page_size;
+  p.window = a->window;
+  p.ratio = a->ratio;
+  p.topk = a->ratio > 0 ? a->topk : 0;
+  p.num_splits = a->num_splits;
+  p.group = a->num_q_heads / a->num_kv_heads;
+  p.head_groups = (p.group + 127) / 128;
+  p.cmp_fp8 = (a->ratio > 0 && a->cmp_dtype == SPA_FP8_E4M3_OCP) ? 1 : 0;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  return p;
+}
+
+spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
+  spa_status st = validate(a, decode, true);
+  if (st != SPA_OK) return st;
+  if (!std::isfinite(a->scale)) return fail(SPA_ERR_SHAPE, "scale must be finite");
+  spa::Params p = make_params(a);
+  const size_t need = workspace_bytes_for(a);
+  if (need > 0) {
+    if (a->workspace == nullptr) return fail(SPA_ERR_WORKSPACE, "num_splits > 1 needs a workspace");
+    if (a->workspace_bytes < need)
+      return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a->workspace_bytes, need);
+    if (!aligned16(a->workspace)) return fail(SPA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t rows = (size_t)a->num_queries * (size_t)a->num_q_heads;
+    const size_t o_bytes = rows * (size_t)a->head_dim * sizeof(float) * (size_t)a->num_splits;
+    p.part_o = static_cast<float *>(a->workspace);
+    p.part_lse = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + ((o_bytes + 255) / 256) * 256);
+  }
+  if (a->num_queries == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = spa::launch_attention(p, s);
+  if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
+  if (a->num_splits > 1) {
+    e = spa::launch_merge(p.part_o, p.part_lse, a->num_splits, (int64_t)a->num_queries * a->num_q_heads,
+                          a->head_dim, a->num_q_heads, a->sink, p.o, a->lse, s);
+    if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_workspace_size(const spa_fwd_args *args) {
+  if (args == nullptr || args->num_splits < 1 || args->num_queries < 0 || args->num_q_heads < 1) return 0;
+  if (args->head_dim != 64 && args->head_dim != 128) return 0;
+  return workspace_bytes_for(args);
+}
+
+spa_status attn_fwd_decode(const spa_fwd_args *args, void *stream) { return run_forward(args, true, stream); }
+
+spa_status attn_fwd_prefill(const spa_fwd_args *args, void *stream) { return run_forward(args, false, stream); }
+
+spa_status attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t num_parts, int64_t rows,
+                          int32_t head_dim, int32_t num_q_heads, const float *sink, void *o_out,
+                          float *lse_out, void *stream) {
+  if (o_parts == nullptr || lse_parts == nullptr || o_out == nullptr)
+    return fail(SPA_ERR_NULL, "o_parts, lse_parts and o_out must not be NULL");
+  if (num_parts < 1 || num_parts > SPA_MAX_SPLITS)
+    return fail(SPA_ERR_SPLITS, "num_parts %d outside [1, %d]", num_parts, SPA_MAX_SPLITS);
+  if (rows < 0) return fail(SPA_ERR_SHAPE, "rows must be >= 0");
+  if (num_q_heads < 1) return fail(SPA_ERR_SHAPE, "num_q_heads must be >= 1");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SPA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if ((rows + 3) / 4 > 0x7FFFFFFFLL) return fail(SPA_ERR_SHAPE, "rows exceed the launch grid");
+  if ((reinterpret_cast<uintptr_t>(o_parts) & 7u) != 0) return fail(SPA_ERR_ALIGN, "o_parts must be 8-byte aligned");
+  hipError_t e = spa::launch_merge(o_parts, lse_parts, num_parts, rows, head_dim, num_q_heads, sink,
+                                   static_cast<uint16_t *>(o_out), lse_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+spa_status attn_build_gather(const spa_fwd_args *args, int32_t decode, int32_t cap, int64_t *rows_out,
+                             int32_t *counts_out, void *stream) {
+  spa_status st = validate(args, decode != 0, false);
+  if (st != SPA_OK) return st;
+  if (rows_out == nullptr || counts_out == nullptr) return fail(SPA_ERR_NULL, "rows_out/counts_out is NULL");
+  if (cap < 0) return fail(SPA_ERR_SHAPE, "cap must be >= 0");
+  if ((int64_t)(cap > 0 ? (cap + 255) / 256 : 1) * args->num_queries > 0x7FFFFFFFLL)
+    return fail(SPA_ERR_SHAPE, "cap * num_queries exceeds the launch grid");
+  spa::Params p = make_params(args);
+  hipError_t e = spa::launch_gather(p, cap, rows_out, counts_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "gather launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char *attn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t attn_abi_version(void) { return 1; }
+
+}  // extern "C"

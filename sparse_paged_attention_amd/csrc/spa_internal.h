@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI host code (spa_api.cpp) and the HIP
+// kernels.  Not installed; the public interface is include/spa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace spa {
+
+// Device error bits (mirrors the err_flag convention of include/spa.h).
+enum : int32_t { kErrQuery = 1, kErrCmpId = 2, kErrPage = 4, kErrCount = 8 };
+
+// Everything a kernel needs, passed by value as a kernel argument.
+struct Params {
+  const uint16_t *q;                  // bf16 [Nq, Hq, D]
+  const uint8_t *k_raw, *v_raw;       // bf16 rows
+  const uint8_t *k_cmp, *v_cmp;       // bf16 or e4m3 rows
+  const float *k_cmp_scale, *v_cmp_scale;
+  int64_t raw_pages, cmp_pages;
+  const int32_t *raw_pt, *cmp_pt;
+  const int32_t *seq_lens, *query_seq, *query_pos;
+  const int32_t *cmp_idx, *cmp_cnt;
+  const float *sink;
+  uint16_t *o;
+  float *lse;
+  float *part_o, *part_lse;           // split partials (num_splits > 1)
+  int32_t *counters;                  // per (query, KV head, head block) arrival counts
+  int32_t *err_flag;
+  int32_t raw_pt_stride, cmp_pt_stride;
+  int32_t num_seqs, num_queries, hq, hkv, head_dim, page_size, window, ratio, topk, num_splits;
+  int32_t group;                      // Hq / Hkv
+  int32_t heads_per_block;            // query heads per workgroup: 32, 64 or 128
+  int32_t head_groups;                // ceil(group / heads_per_block)
+  int32_t total_jobs;                 // Nq * Hkv * num_splits * head_groups
+  int32_t jobs_per_xcd;               // ceil(total_jobs / 8)
+  int32_t cmp_fp8;
+  float scale_log2;                   // scale * log2(e)
+};
+
+hipError_t launch_attention(const Params &p, hipStream_t stream);
+hipError_t launch_merge(const float *o_parts, const float *lse_parts, int32_t num_parts,
+                        int64_t rows, int32_t head_dim, int32_t num_q_heads, const float *sink,
+                        uint16_t *o_out, float *lse_out, hipStream_t stream);
+hipError_t launch_gather(const Params &p, int32_t cap, int64_t *rows_out, int32_t *counts_out,
+                         hipStream_t stream);
+
+}  // namespace spa

@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, the ctypes mirror of spa_fwd_args matches the C layout, and
+host-side validation returns the documented status for each fault class
+(validation runs before any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_paged_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libspa.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    fields = [f[0] for f in _lib.SpaFwdArgs._fields_]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(spa_fwd_args, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "spa.h"\nint main(void){\n'
+                   + body + '\n  printf("SIZE %zu\\n", sizeof(spa_fwd_args));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = dict(line.split() for line in out if line)
+    for f in fields:
+        assert int(got[f]) == getattr(_lib.SpaFwdArgs, f).offset, f
+    assert int(got["SIZE"]) == ctypes.sizeof(_lib.SpaFwdArgs)
+
+
+def _good_args():
+    """A well-formed decode argument block with fake (never dereferenced)
+    16-byte aligned device addresses."""
+    a = _lib.SpaFwdArgs()
+    a.num_seqs = 2
+    a.num_queries = 2
+    a.num_q_heads = 8
+    a.num_kv_heads = 1
+    a.head_dim = 128
+    a.page_size = 16
+    a.window = 16
+    a.ratio = 4
+    a.topk = 8
+    a.scale = 0.125
+    a.raw_dtype = _lib.SPA_BF16
+    a.cmp_dtype = _lib.SPA_BF16
+    a.num_splits = 1
+    base = 0x10000000
+    for i, f in enumerate(["q", "k_raw", "v_raw", "k_cmp", "v_cmp", "raw_pt", "cmp_pt", "seq_lens",
+                           "cmp_idx", "cmp_cnt", "sink", "o", "lse"]):
+        setattr(a, f, base + 0x1000 * i)
+    a.raw_pages = 4
+    a.cmp_pages = 4
+    a.raw_pt_stride = 2
+    a.cmp_pt_stride = 2
+    return a
+
+
+FAULTS = [
+    ("null_q", lambda a: setattr(a, "q", None), -1),
+    ("null_raw_pt", lambda a: setattr(a, "raw_pt", None), -1),
+    ("null_cmp_when_ratio", lambda a: setattr(a, "k_cmp", None), -1),
+    ("null_list_when_topk", lambda a: setattr(a, "cmp_idx", None), -1),
+    ("null_out", lambda a: setattr(a, "o", None), -1),
+    ("fp8_without_scales", lambda a: setattr(a, "cmp_dtype", _lib.SPA_FP8_E4M3_OCP), -1),
+    ("zero_seqs", lambda a: setattr(a, "num_seqs", 0), -2),
+    ("heads_not_multiple", lambda a: setattr(a, "num_kv_heads", 3), -2),
+    ("page_size_zero", lambda a: setattr(a, "page_size", 0), -2),
+    ("negative_window", lambda a: setattr(a, "window", -1), -2),
+    ("topk_without_ratio", lambda a: setattr(a, "ratio", 0), -2),
+    ("raw_pages_zero", lambda a: setattr(a, "raw_pages", 0), -2),
+    ("raw_dtype_fp8", lambda a: setattr(a, "raw_dtype", _lib.SPA_FP8_E4M3_OCP), -3),
+    ("cmp_dtype_unknown", lambda a: setattr(a, "cmp_dtype", 7), -3),
+    ("head_dim_96", lambda a: setattr(a, "head_dim", 96), -4),
+    ("misaligned_q", lambda a: setattr(a, "q", a.q + 2), -5),
+    ("misaligned_out", lambda a: setattr(a, "o", a.o + 8), -5),
+    ("splits_zero", lambda a: setattr(a, "num_splits", 0), -7),
+    ("splits_too_many", lambda a: setattr(a, "num_splits", 65), -7),
+    ("decode_with_positions", lambda a: setattr(a, "query_pos", 0x20000000), -9),
+    ("decode_count_mismatch", lambda a: setattr(a, "num_queries", 3), -9),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", FAULTS, ids=[f[0] for f in FAULTS])
+def test_decode_validation(lib, name, mutate, code):
+    a = _good_args()
+    mutate(a)
+    st = lib.attn_fwd_decode(ctypes.byref(a), None)
+    assert st == code, (name, st, lib.attn_last_error())
+    assert lib.attn_last_error().decode()
+
+
+def test_null_args(lib):
+    assert lib.attn_fwd_decode(None, None) == -1
+    assert lib.attn_fwd_prefill(None, None) == -1
+    assert lib.attn_workspace_size(None) == 0
+
+
+def test_prefill_needs_positions(lib):
+    a = _good_args()
+    assert lib.attn_fwd_prefill(ctypes.byref(a), None) == -9
+
+
+def test_workspace_rules(lib):
+    a = _good_args()
+    a.num_splits = 4
+    need = lib.attn_workspace_size(ctypes.byref(a))
+    rows = a.num_queries * a.num_q_heads
+    assert need >= rows * 128 * 4 * 4 + rows * 4 * 4
+    assert lib.attn_fwd_decode(ctypes.byref(a), None) == -6       # missing
+    a.workspace = 0x30000000
+    a.workspace_bytes = need - 1
+    assert lib.attn_fwd_decode(ctypes.byref(a), None) == -6       # too small
+    a.num_splits = 1
+    assert lib.attn_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_merge_validation(lib):
+    good = dict(o=0x10000000, l=0x10010000, out=0x10020000)
+    assert lib.attn_merge_lse(None, good["l"], 2, 10, 128, 4, None, good["out"], None, None) == -1
+    assert lib.attn_merge_lse(good["o"], good["l"], 0, 10, 128, 4, None, good["out"], None, None) == -7
+    assert lib.attn_merge_lse(good["o"], good["l"], 65, 10, 128, 4, None, good["out"], None, None) == -7
+    assert lib.attn_merge_lse(good["o"], good["l"], 2, -1, 128, 4, None, good["out"], None, None) == -2
+    assert lib.attn_merge_lse(good["o"], good["l"], 2, 10, 96, 4, None, good["out"], None, None) == -4
+
+
+def test_gather_validation(lib):
+    a = _good_args()
+    assert lib.attn_build_gather(ctypes.byref(a), 1, 16, None, 0x10000000, None) == -1
+    assert lib.attn_build_gather(ctypes.byref(a), 1, -1, 0x10000000, 0x10000000, None) == -2
+    a.head_dim = 32
+    assert lib.attn_build_gather(ctypes.byref(a), 1, 16, 0x10000000, 0x10000000, None) == -4
