@@ -75,39 +75,43 @@ def cpu_baseline(p, budget_s):
                       f"{dt:.1f} s single process, numpy fp64"}
 
 
-def main():
+def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_csa",
                     choices=["decode_csa", "decode_hca", "mixed_fp8", "prefill_csa", "tiny"])
+    ap.add_argument("--batch", type=int, default=0, help="decode batch override (0 = the workload's)")
     ap.add_argument("--splits", type=int, default=0, help="0 = the default for the workload")
+    ap.add_argument("--heads-per-block", type=int, default=-1,
+                    help="query heads per workgroup (32/64/128, 0 = library choice, -1 = workload default)")
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="total size of the input replicas the timed steps rotate through")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")
-    ap.add_argument("--no-json-extra", action="store_true")
-    args = ap.parse_args()
+    return ap.parse_args(argv)
 
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
-              f"multi-GPU path", file=sys.stderr)
-        sys.exit(2)
+
+DEFAULTS = {   # (num_splits, heads_per_block) per workload
+    "decode_csa": (8, 128), "decode_hca": (4, 0), "mixed_fp8": (8, 128), "prefill_csa": (1, 0), "tiny": (1, 0),
+}
+
+
+def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, rotate_mb=640.0, batch=0,
+        cpu_budget=0.0, problem=None):
+    """Time `steps` calls of the hot path; returns the result dict."""
+    import ctypes
 
     import numpy as np
     import torch
     from sparse_paged_attention_amd import api, synth, _lib
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    _lib.load()
+    lib = _lib.load()
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    p = synth.make_workload(args.workload)
-    default_splits = {"decode_csa": 8, "decode_hca": 4, "mixed_fp8": 8, "prefill_csa": 1, "tiny": 1}
-    splits = args.splits or default_splits[args.workload]
+    p = problem if problem is not None else synth.make_workload(workload, batch=batch or None)
+    d_splits, d_hpb = DEFAULTS.get(workload, (1, 0))
+    splits = splits or d_splits
+    hpb = d_hpb if heads_per_block < 0 else heads_per_block
     base = api.DeviceProblem.from_problem(p, device=dev)
 
     # metadata from the library itself, for the byte/FLOP accounting
@@ -117,128 +121,134 @@ def main():
     alg_bytes, alg_flops, kv_entries = algorithmic_work(p, counts)
 
     # replicas: the KV rows read per step plus Q/O, rotated so the set is HBM-cold
-    touched = alg_bytes
-    reps = max(1, math.ceil(args.rotate_mb * 1e6 / max(touched, 1)))
+    reps = max(1, math.ceil(rotate_mb * 1e6 / max(alg_bytes, 1)))
     pool_bytes = sum(t.numel() * t.element_size() for t in (base.k_raw, base.v_raw, base.k_cmp, base.v_cmp)
                      if t is not None)
-    reps = min(reps, max(1, int(64e9 // max(pool_bytes, 1))))
+    reps = min(reps, max(1, int(48e9 // max(pool_bytes, 1))))
     replicas = []
     for r in range(reps):
-        if r == 0:
-            dp = base
-        else:
-            dp = api.DeviceProblem(**{k: (v.clone() if isinstance(v, torch.Tensor) else v)
-                                      for k, v in base.__dict__.items()})
-        a = dp.args(splits)
+        dp = base if r == 0 else api.DeviceProblem(
+            **{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in base.__dict__.items()})
+        a = dp.args(splits, hpb)
         o = torch.empty((p.num_queries, p.num_q_heads, p.head_dim), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((p.num_queries, p.num_q_heads), dtype=torch.float32, device=dev)
         need = api.workspace_size(a)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if need else None
-        replicas.append((dp, a, o, lse, ws))
-
-    lib = _lib.load()
-    fn = lib.attn_fwd_decode if p.mode == "decode" else lib.attn_fwd_prefill
-    import ctypes
-    stream = torch.cuda.current_stream().cuda_stream
-
-    prepared = []
-    for dp, a, o, lse, ws in replicas:
         a.o = o.data_ptr()
         a.lse = lse.data_ptr()
         a.workspace = ws.data_ptr() if ws is not None else None
         a.workspace_bytes = ws.numel() if ws is not None else 0
-        prepared.append(ctypes.byref(a))
+        replicas.append((dp, a, o, lse, ws))
+    fn = lib.attn_fwd_decode if p.mode == "decode" else lib.attn_fwd_prefill
+    stream = torch.cuda.current_stream().cuda_stream
+    prepared = [ctypes.byref(r[1]) for r in replicas]
 
     def step(k):
         st = fn(prepared[k % reps], stream)
         if st != 0:
             _lib.check(st)
 
-    for k in range(args.warmup):
+    for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
 
-    K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    # eager: host launches back to back (includes the Python + HIP launch cost)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall0 = time.perf_counter()
-    ev[0].record()
-    for k in range(K):
+    e0.record()
+    for k in range(steps):
         step(k)
-        ev[k + 1].record()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    per = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(K)])   # ms
-    total_ms = ev[0].elapsed_time(ev[K])
-    ms_per_step = total_ms / K
+    eager_ms = e0.elapsed_time(e1) / steps
 
-    # the merge kernel alone, timed the same way, to isolate the attention kernel
-    merge_ms = 0.0
-    if splits > 1:
-        dp, a, o, lse, ws = replicas[0]
-        rows = p.num_queries * p.num_q_heads
-        o_bytes = rows * p.head_dim * 4 * splits
-        lse_off = ((o_bytes + 255) // 256) * 256
-        me0, me1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(5):
-            lib.attn_merge_lse(ws.data_ptr(), ws.data_ptr() + lse_off, splits, rows, p.head_dim,
-                               p.num_q_heads, dp.sink.data_ptr() if dp.sink is not None else None,
-                               o.data_ptr(), lse.data_ptr(), stream)
-        me0.record()
-        for _ in range(K):
-            lib.attn_merge_lse(ws.data_ptr(), ws.data_ptr() + lse_off, splits, rows, p.head_dim,
-                               p.num_q_heads, dp.sink.data_ptr() if dp.sink is not None else None,
-                               o.data_ptr(), lse.data_ptr(), stream)
-        me1.record()
-        torch.cuda.synchronize()
-        merge_ms = me0.elapsed_time(me1) / K
-    attn_ms = max(ms_per_step - merge_ms, 1e-9)
+    # graph: the same `steps` launches captured once and replayed, so the GPU
+    # runs them back to back with no host in the loop
+    cap_stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap_stream):
+        stream = cap_stream.cuda_stream
+        for k in range(3):
+            step(k)
+        cap_stream.synchronize()
+        with torch.cuda.graph(graph, stream=cap_stream):
+            stream = torch.cuda.current_stream().cuda_stream
+            for k in range(steps):
+                step(k)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps_g = 5
+    ge = [torch.cuda.Event(enable_timing=True) for _ in range(reps_g + 1)]
+    ge[0].record()
+    for r in range(reps_g):
+        graph.replay()
+        ge[r + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ge[r].elapsed_time(ge[r + 1]) / steps for r in range(reps_g)])   # ms per launch
+    ms_per_step = float(ge[0].elapsed_time(ge[reps_g]) / (steps * reps_g))
+    kernel_ms = ms_per_step
 
     nq = p.num_queries
-    value = nq / (ms_per_step / 1e3)
     decode = p.mode == "decode"
     if decode:
-        roof = {"bound": "hbm", "achieved": alg_bytes / (attn_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+        roof = {"bound": "hbm", "achieved": alg_bytes / (kernel_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": alg_flops / (attn_ms / 1e3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "achieved": alg_flops / (kernel_ms / 1e3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
     roof["kernel"] = "attn_fwd_kernel"
-    roof["kernel_ms"] = attn_ms
+    roof["kernel_ms"] = kernel_ms
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["algorithmic_flops_per_launch"] = alg_flops
 
-    cpu = None
-    if args.cpu_budget > 0:
-        cpu = cpu_baseline(p, args.cpu_budget)
-
     out = {
         "metric": "decode queries/s + HBM GB/s; prefill TFLOP/s (frac. of MI355X peak)",
-        "value": value,
+        "value": nq / (ms_per_step / 1e3),
         "unit": "queries/s" if decode else "tokens/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if not p.cmp_fp8 else "bf16+e4m3",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": p.num_seqs, "queries": nq,
+        "config": {"workload": workload, "batch": p.num_seqs, "queries": nq,
                    "q_heads": p.num_q_heads, "kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
                    "page_size": p.page_size, "window": p.window, "ratio": p.ratio, "topk": p.topk,
-                   "kv_entries": kv_entries, "num_splits": splits, "replicas": reps},
+                   "kv_entries": kv_entries, "num_splits": splits, "heads_per_block": hpb,
+                   "replicas": reps},
         "roofline": roof,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_baseline(p, cpu_budget) if cpu_budget > 0 else None,
+        "timing": {"graph_replay_ms_per_step_min": float(per.min()),
+                   "graph_replay_ms_per_step_max": float(per.max()),
+                   "eager_ms_per_step": eager_ms,
+                   "host_wall_ms_per_step": wall / steps * 1e3,
+                   "tflops": alg_flops / (ms_per_step / 1e3) / 1e12,
+                   "gbs_step": alg_bytes / (ms_per_step / 1e3) / 1e9},
     }
-    if not args.no_json_extra:
-        out["timing"] = {"p10_ms": float(np.percentile(per, 10)), "p50_ms": float(np.percentile(per, 50)),
-                         "p90_ms": float(np.percentile(per, 90)), "merge_ms": merge_ms,
-                         "host_wall_ms_per_step": wall / K * 1e3,
-                         "tflops": alg_flops / (ms_per_step / 1e3) / 1e12,
-                         "gbs_step": alg_bytes / (ms_per_step / 1e3) / 1e9}
+    return out
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    out = run(args.workload, steps=args.steps, warmup=args.warmup, splits=args.splits,
+              heads_per_block=args.heads_per_block, rotate_mb=args.rotate_mb, batch=args.batch,
+              cpu_budget=args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

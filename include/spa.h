@@ -89,10 +89,13 @@ typedef struct spa_fwd_args {
   int32_t ratio;          /* r >= 0 tokens per compressed group; 0 = no groups   */
   int32_t topk;           /* list capacity (row stride of cmp_idx); 0 = every
                              complete group, no list                              */
-  float scale;            /* multiplies q.k; not applied to the sink             */
+  float scale;            /* > 0, multiplies q.k; not applied to the sink        */
   int32_t raw_dtype;      /* spa_dtype: must be SPA_BF16                         */
   int32_t cmp_dtype;      /* spa_dtype: SPA_BF16 or SPA_FP8_E4M3_OCP             */
   int32_t num_splits;     /* 1 = one pass; >1 = split-KV partials + LSE merge    */
+  int32_t heads_per_block; /* query heads one workgroup computes: 32, 64 or 128,
+                              or 0 = chosen by the library (a tuning knob; the
+                              result does not depend on it)                       */
 
   const void *q;          /* bf16 [Nq, Hq, D]                                    */
   const void *k_raw;      /* bf16 [raw_pages, P, Hkv, D]                         */
@@ -120,7 +123,9 @@ typedef struct spa_fwd_args {
   float *lse;               /* out: f32 [Nq, Hq], natural log, sink included;
                                may be NULL                                        */
   int32_t *err_flag;        /* device i32 or NULL, see the conventions above     */
-  void *workspace;          /* num_splits > 1: attn_workspace_size() bytes       */
+  void *workspace;          /* num_splits > 1: attn_workspace_size() bytes of
+                               scratch for the split partials (no initial
+                               contents needed); one call at a time          */
   size_t workspace_bytes;
 } spa_fwd_args;
 
@@ -132,8 +137,10 @@ size_t attn_workspace_size(const spa_fwd_args *args);
 /* Decode: one query per sequence at position seq_lens[b] - 1
    (query_seq = query_pos = NULL, num_queries = num_seqs).  With num_splits
    S > 1 every query's canonical KV list is cut into S contiguous slices, each
-   slice yields a sink-free partial (O_s, LSE_s) in the workspace, and the
-   partials plus the sink are combined exactly as attn_merge_lse does. */
+   slice yields a sink-free partial (O_s, LSE_s) in the workspace, and a
+   second kernel on the same stream combines the partials plus the sink
+   exactly as attn_merge_lse does (in slice order, so the result is
+   deterministic). */
 spa_status attn_fwd_decode(const spa_fwd_args *args, void *stream);
 
 /* Prefill / chunked prefill / multi-token decode: query i sits at

@@ -43,6 +43,7 @@ class SpaFwdArgs(ctypes.Structure):
         ("raw_dtype", ctypes.c_int32),
         ("cmp_dtype", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
+        ("heads_per_block", ctypes.c_int32),
         ("q", ctypes.c_void_p),
         ("k_raw", ctypes.c_void_p),
         ("v_raw", ctypes.c_void_p),

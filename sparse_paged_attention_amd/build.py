@@ -18,7 +18,11 @@ BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["spa_api.cpp", "spa_attention.hip", "spa_merge.hip", "spa_gather.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for every HIP source file.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # keep MFMA accumulators in VGPRs: with AGPR accumulators the
+                # compiler copies the whole O tile between the register files
+                # on every KV tile
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]
 

@@ -66,8 +66,14 @@ spa_status validate(const spa_fwd_args *a, bool decode, bool need_outputs) {
     return fail(SPA_ERR_DTYPE, "cmp_dtype %d unknown", a->cmp_dtype);
   if (a->num_splits < 1 || a->num_splits > SPA_MAX_SPLITS)
     return fail(SPA_ERR_SPLITS, "num_splits %d outside [1, %d]", a->num_splits, SPA_MAX_SPLITS);
-  if ((int64_t)a->num_queries * a->num_splits > 0x7FFFFFFFLL)
-    return fail(SPA_ERR_SHAPE, "num_queries * num_splits exceeds the launch grid");
+  if (a->heads_per_block != 0 && a->heads_per_block != 32 && a->heads_per_block != 64 &&
+      a->heads_per_block != 128)
+    return fail(SPA_ERR_UNSUPPORTED, "heads_per_block %d not supported (0, 32, 64 or 128)", a->heads_per_block);
+  {
+    const int64_t group = a->num_q_heads / a->num_kv_heads;
+    const int64_t jobs = (int64_t)a->num_queries * a->num_kv_heads * a->num_splits * ((group + 31) / 32);
+    if (jobs + 8 > 0x7FFFFFFFLL) return fail(SPA_ERR_SHAPE, "the job count exceeds the launch grid");
+  }
 
   if (a->q == nullptr) return fail(SPA_ERR_NULL, "q is NULL");
   if (a->k_raw == nullptr || a->v_raw == nullptr) return fail(SPA_ERR_NULL, "k_raw/v_raw is NULL");
@@ -101,12 +107,37 @@ spa_status validate(const spa_fwd_args *a, bool decode, bool need_outputs) {
   return SPA_OK;
 }
 
-size_t workspace_bytes_for(const spa_fwd_args *a) {
-  if (a->num_splits <= 1) return 0;
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace layout (num_splits > 1): partial O | partial LSE.
+struct WorkspaceLayout {
+  size_t part_o, part_lse, total;
+};
+
+WorkspaceLayout workspace_layout(const spa_fwd_args *a) {
+  WorkspaceLayout w{0, 0, 0};
+  if (a->num_splits <= 1) return w;
   const size_t rows = (size_t)a->num_queries * (size_t)a->num_q_heads;
-  const size_t o = rows * (size_t)a->head_dim * sizeof(float) * (size_t)a->num_splits;
-  const size_t l = rows * sizeof(float) * (size_t)a->num_splits;
-  return ((o + 255) / 256) * 256 + l;
+  w.part_o = 0;
+  w.part_lse = round256(rows * (size_t)a->head_dim * sizeof(float) * (size_t)a->num_splits);
+  w.total = w.part_lse + rows * sizeof(float) * (size_t)a->num_splits;
+  return w;
+}
+
+size_t workspace_bytes_for(const spa_fwd_args *a) { return workspace_layout(a).total; }
+
+// Query heads per workgroup: the requested value, or the largest of
+// 128/64/32 that still yields >= 256 workgroups (one per compute unit).
+int32_t pick_heads_per_block(const spa_fwd_args *a) {
+  if (a->heads_per_block > 0) return a->heads_per_block;
+  const int64_t group = a->num_q_heads / a->num_kv_heads;
+  int32_t hpb = 128;
+  while (hpb > 32) {
+    const int64_t jobs = (int64_t)a->num_queries * a->num_kv_heads * a->num_splits * ((group + hpb - 1) / hpb);
+    if (jobs >= 256) break;
+    hpb /= 2;
+  }
+  return hpb;
 }
 
 spa::Params make_params(const spa_fwd_args *a) {
@@ -144,7 +175,13 @@ spa::Params make_params(const spa_fwd_args *a) {
   p.topk = a->ratio > 0 ? a->topk : 0;
   p.num_splits = a->num_splits;
   p.group = a->num_q_heads / a->num_kv_heads;
-  p.head_groups = (p.group + 127) / 128;
+  p.heads_per_block = pick_heads_per_block(a);
+  p.head_groups = (p.group + p.heads_per_block - 1) / p.heads_per_block;
+  {
+    const int64_t jobs = (int64_t)a->num_queries * a->num_kv_heads * a->num_splits * p.head_groups;
+    p.total_jobs = (int32_t)jobs;
+    p.jobs_per_xcd = (int32_t)((jobs + 7) / 8);
+  }
   p.cmp_fp8 = (a->ratio > 0 && a->cmp_dtype == SPA_FP8_E4M3_OCP) ? 1 : 0;
   p.scale_log2 = a->scale * 1.4426950408889634f;
   return p;
@@ -153,7 +190,7 @@ spa::Params make_params(const spa_fwd_args *a) {
 spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
   spa_status st = validate(a, decode, true);
   if (st != SPA_OK) return st;
-  if (!std::isfinite(a->scale)) return fail(SPA_ERR_SHAPE, "scale must be finite");
+  if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return fail(SPA_ERR_SHAPE, "scale must be finite and > 0");
   spa::Params p = make_params(a);
   const size_t need = workspace_bytes_for(a);
   if (need > 0) {
@@ -161,10 +198,10 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
     if (a->workspace_bytes < need)
       return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a->workspace_bytes, need);
     if (!aligned16(a->workspace)) return fail(SPA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    const size_t rows = (size_t)a->num_queries * (size_t)a->num_q_heads;
-    const size_t o_bytes = rows * (size_t)a->head_dim * sizeof(float) * (size_t)a->num_splits;
-    p.part_o = static_cast<float *>(a->workspace);
-    p.part_lse = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + ((o_bytes + 255) / 256) * 256);
+    const WorkspaceLayout w = workspace_layout(a);
+    char *base = static_cast<char *>(a->workspace);
+    p.part_o = reinterpret_cast<float *>(base + w.part_o);
+    p.part_lse = reinterpret_cast<float *>(base + w.part_lse);
   }
   if (a->num_queries == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);

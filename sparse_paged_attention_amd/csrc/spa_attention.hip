@@ -6,44 +6,52 @@
 // denominator; the sink has no value row; P and O are bf16, LSE is fp32
 // natural log.  The KV set and page translation live in spa_device.h.
 //
-// Work decomposition.  One workgroup owns one (query, KV slice, KV head,
-// group of up to 128 query heads).  All query heads of a KV head read the same
-// KV rows, so they share every KV tile the workgroup stages in LDS: each wave
-// holds 32 query heads and the tile's 32 KV rows feed bf16 MFMAs for all of
-// them.
+// Work decomposition.  A job is (query, KV head, KV slice, block of query
+// heads).  All query heads of a KV head read the same KV rows, so a
+// workgroup stages each KV tile once in LDS and every wave feeds it to bf16
+// MFMAs for its 32 query heads:
 //
 //   S^T[kv, head]  = K[kv, :] . Q^T[:, head]        v_mfma_f32_32x32x16_bf16
 //   O^T[d, head]  += V^T[d, kv] . P^T[kv, head]      v_mfma_f32_32x32x16_bf16
 //
 // With S^T and O^T in the MFMA accumulator layout every lane owns one query
-// head (lane % 32), so the online-softmax state (m, l) is per lane; the
-// row max needs one exchange with lane ^ 32, and P^T goes from the S^T
+// head (lane % 32), so the online-softmax state (m, l) is per lane; the row
+// max needs one exchange with lane ^ 32, and P^T goes from the S^T
 // accumulators straight into the B operand of the PV MFMA (the KV order inside
-// a 16-row step is permuted identically on both operands).  V^T comes from
-// the row-major V tile through the gfx950 LDS transpose read
-// (ds_read_b64_tr_b16), so no transposition pass is needed.
+// a 16-row step is permuted identically on both operands).  V^T comes from the
+// row-major V tile through the gfx950 LDS transpose read (ds_read_b64_tr_b16),
+// so no transposition pass is needed.
 //
-// Data movement.  The KV rows of a slice are translated to 64-bit row
-// offsets once per chunk of up to 16 tiles (the page-table walk), then every
-// tile is fetched by direct global->LDS loads (global_load_lds_dwordx4,
-// 16 B per lane, no VGPR staging) into a 3-deep ring of LDS buffers, so two
-// tiles are in flight while the third is computed.  Masked rows (slice tail,
-// invalid metadata) are fetched from a static zero row, so every thread issues
-// the same number of loads per tile and one vmcnt immediate tracks the ring.
-// LDS rows are XOR-swizzled in 16-byte chunks so that the K reads (one row per
-// lane) and the transpose reads (4 rows x 32 B per 16 lanes) are free of bank
-// conflicts.
+// Grid.  Jobs are numbered (query, KV head, slice, head block) with the head
+// block fastest and dealt to the 8 XCDs in contiguous ranges (workgroup w runs
+// job (w % 8) * ceil(jobs/8) + w / 8), so the head blocks that read the same
+// KV slice land on one XCD and share its L2.  This affects speed only, never
+// results.
 //
-// FP8 (OCP e4m3) compressed rows land in an LDS staging area and are widened
-// to bf16 exactly (every e4m3 value is a bf16 value) by the hardware
-// v_cvt_pk_f32_fp8; the per-token scales are applied in fp32 to the scores
-// (k) and to P (v), so the MFMAs see the exact codes.
+// Data movement.  The rows of up to 16 tiles are translated first (list
+// loads for the whole batch, then page-table loads), then every tile is
+// fetched by direct global->LDS loads (global_load_lds_dwordx4, 16 B per
+// lane, no VGPR staging) into a ring of NBUF LDS buffers, NBUF-1 tiles ahead
+// of the compute.  Masked rows (slice tail, invalid metadata) are fetched from
+// a static zero row and excluded through a per-tile 32-bit row mask, so every
+// thread issues the same number of loads per tile and one vmcnt immediate
+// tracks the ring.
+// LDS rows are XOR-swizzled in 16-byte chunks so that the K reads (one row
+// per lane) and the transpose reads (4 rows x 32 B per 16 lanes) are free of
+// bank conflicts.
+//
+// FP8 (OCP e4m3) compressed rows land in an LDS staging area, together with
+// their fp32 per-token scales (one 4-byte direct load per row), and are
+// widened to bf16 exactly (every e4m3 value is a bf16 value) by the hardware
+// v_cvt_pk_f32_fp8; the scales are applied in fp32 to the scores (k) and to
+// P (v), so the MFMAs see the exact codes.
 //
 // Softmax runs in the log2 domain (scores pre-multiplied by scale*log2 e,
-// sink by log2 e) with v_exp_f32; the running max starts at the sink and the
-// running sum at exp(0) = 1, i.e. the sink is folded into (m, l) from the
-// start.  With num_splits > 1 the workgroup writes a sink-free partial
-// (O_s f32, LSE_s) and the merge kernel adds the sink exactly once.
+// sink by log2 e) with v_exp_f32; with one slice the running max starts at
+// the sink and the running sum at exp(0) = 1, i.e. the sink is folded into
+// (m, l) from the start.  With num_splits > 1 each slice writes a sink-free
+// partial (O_s f32, LSE_s) to the workspace and the merge kernel
+// (spa_merge.hip) combines them, adding the sink exactly once.
 
 #include <hip/hip_runtime.h>
 
@@ -57,29 +65,47 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 constexpr int kTile = 32;        // KV rows per tile
-constexpr int kBufs = 3;         // LDS ring depth
 constexpr int kChunkTiles = 16;  // tiles translated per page-table pass
 constexpr float kLog2e = 1.4426950408889634f;
+// The running max used for the exponentials moves only when a tile's max
+// exceeds it by more than kTau (log2 units), so P and the sums stay below
+// 2^kTau and the O accumulators are rescaled only on such jumps.  Any
+// reference value gives the same softmax; only the rounding differs.
+constexpr float kTau = 8.f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Source of the 16-byte loads for masked rows.
+// Source of the 16-byte loads for masked rows (and of padding loads).
 __device__ __attribute__((aligned(16))) const uint8_t kZeroRow[256] = {};
 
-// One wave-wide direct global->LDS load: lane L's 16 bytes from `src` land at
-// lds_dst + 16 L (lds_dst is wave-uniform and goes through M0).  Written as
-// inline asm so that the compiler does not guard every later LDS read with a
-// wait for all outstanding loads; completion is tracked explicitly with
-// wait_vmcnt<> below.  The instruction has no destination registers.
+// LDS byte offset of a generic pointer into shared memory: the LDS aperture
+// is 4 GiB aligned in the flat address space, so the low 32 bits are the
+// offset (this avoids a checked generic->local address-space cast).
+__device__ __forceinline__ uint32_t lds_offset(const void *p) { return (uint32_t)(uintptr_t)p; }
+
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved; only these loads use it here
+// One wave-wide direct global->LDS load: lane L's 16 (or 4) bytes from `src`
+// land at lds_dst + 16 L (or 4 L); lds_dst is wave-uniform and goes through
+// M0.  Written as inline asm so that the compiler does not guard every later
+// LDS read with a wait for all outstanding loads; completion is tracked
+// explicitly with wait_vmcnt<>.  The instructions have no destination
+// registers.
 __device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds_dst);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_offset(lds_dst));
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *src, void *lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_offset(lds_dst));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :
                : "v"(src), "s"(lds)
                : "memory", "m0");
@@ -94,21 +120,34 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most `ahead` tiles of OPS loads each are still in flight.
+template <int OPS, int MAXA>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+  static_assert(MAXA <= 5 && MAXA * OPS < 64, "ring depth");
+  if (MAXA >= 5 && ahead >= 5) wait_vmcnt<(MAXA >= 5 ? 5 * OPS : 0)>();
+  else if (MAXA >= 4 && ahead >= 4) wait_vmcnt<(MAXA >= 4 ? 4 * OPS : 0)>();
+  else if (MAXA >= 3 && ahead >= 3) wait_vmcnt<(MAXA >= 3 ? 3 * OPS : 0)>();
+  else if (MAXA >= 2 && ahead >= 2) wait_vmcnt<(MAXA >= 2 ? 2 * OPS : 0)>();
+  else if (MAXA >= 1 && ahead >= 1) wait_vmcnt<OPS>();
+  else wait_vmcnt<0>();
+}
+
 // Workgroup barrier that waits only for this wave's LDS operations.  The
 // HIP __syncthreads() adds a workgroup release fence, which on gfx950 also
 // waits for every outstanding global load and would drain the LDS ring;
 // global->LDS loads are instead completed explicitly with wait_vmcnt<>.
 // The "memory" clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void block_sync() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
+__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ uint32_t pack_bf16_hi(float lo, float hi) {
   // exact narrowing for values that are bf16 already (widened e4m3 codes)
   return (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
 }
 
-template <int D, int NW, bool FP8>
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+
+template <int D, int NW, bool FP8, int NBUF>
 struct Cfg {
   static constexpr int kThreads = NW * 64;
   static constexpr int kRowB = 2 * D;                 // bf16 row bytes
@@ -118,19 +157,22 @@ struct Cfg {
   static constexpr int kOps = kKVInstr / NW;          // loads per thread per tile
   static constexpr int kF8TileB = kTile * D;          // one e4m3 K (or V) tile
   static constexpr int kF8Instr = 2 * kF8TileB / 1024;
+  static constexpr int kSlots = kChunkTiles * kTile;
+  static constexpr int kPer = kSlots / kThreads;      // translation slots per thread
   static_assert(kKVInstr % NW == 0 && kF8Instr % NW == 0, "load split");
-  static_assert((kF8Instr / NW) <= kOps, "fp8 loads are padded to the bf16 count");
+  static_assert(!FP8 || kF8Instr / NW < kOps, "fp8 tiles need one spare load slot per wave");
+  static_assert(kSlots % kThreads == 0, "slots");
 };
 
-template <int D, int NW, bool FP8>
+template <int D, int NW, bool FP8, int NBUF>
 struct Smem {
-  using C = Cfg<D, NW, FP8>;
-  alignas(16) uint8_t kv[kBufs][2][C::kTileB];
-  alignas(16) uint8_t stage[FP8 ? kBufs : 1][2][FP8 ? C::kF8TileB : 16];
+  using C = Cfg<D, NW, FP8, NBUF>;
+  alignas(16) uint8_t kv[NBUF][2][C::kTileB];
+  alignas(16) uint8_t stage[FP8 ? NBUF : 1][2][FP8 ? C::kF8TileB : 16];
+  alignas(16) float scl[FP8 ? NBUF : 1][64];          // k scales [0,32), v scales [32,64)
   alignas(16) uint8_t dummy[FP8 ? 1024 : 16];
-  alignas(16) int64_t erow[kChunkTiles * kTile];      // element row (row*Hkv+g), -1 = masked
-  alignas(16) float ks[kChunkTiles * kTile];
-  alignas(16) float vs[kChunkTiles * kTile];
+  alignas(16) int64_t erow[C::kSlots];                 // element row (row*Hkv+g), -1 = masked
+  uint32_t tmask[kChunkTiles];                         // bit r: row r of the tile is valid
 };
 
 // Tile j of a slice: compressed tiles cover [c_lo, c_hi), window tiles
@@ -150,22 +192,30 @@ struct SliceTiles {
   }
 };
 
-template <int D, int NW, bool FP8>
+template <int D, int NW, bool FP8, int NBUF>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
-  using C = Cfg<D, NW, FP8>;
-  __shared__ Smem<D, NW, FP8> sm;
+  using C = Cfg<D, NW, FP8, NBUF>;
+  __shared__ Smem<D, NW, FP8, NBUF> sm;
 
+  // ---- job of this workgroup (XCD-contiguous numbering)
+  const int job = (int)(blockIdx.x & 7) * p.jobs_per_xcd + (int)(blockIdx.x >> 3);
+  if (job >= p.total_jobs) return;
   const int S = p.num_splits;
-  const int qi = blockIdx.x / S;
-  const int split = blockIdx.x - qi * S;
-  const int g = blockIdx.y / p.head_groups;
-  const int hgrp = blockIdx.y - g * p.head_groups;
+  int t = job;
+  const int hgw = t % p.head_groups;
+  t /= p.head_groups;
+  const int split = t % S;
+  t /= S;
+  const int g = t % p.hkv;
+  const int qi = t / p.hkv;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hi = lane >> 5;             // which half of the wave
-  const int hl = hgrp * 128 + wave * 32 + (lane & 31);   // head within the KV group
+  const int hl = hgw * p.heads_per_block + wave * 32 + (lane & 31);   // head within the KV group
   const bool head_ok = hl < p.group;
+  const bool wave_ok = hgw * p.heads_per_block + wave * 32 < p.group;
   const int h = g * p.group + hl;
 
   // ---- Q^T as the B operand: lane holds head (lane%32), d = 16kk + 8*hi ..+7
@@ -177,9 +227,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
       uint4 v = head_ok ? *(const uint4 *)(qrow + 16 * kk + 8 * hi) : make_uint4(0, 0, 0, 0);
       qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
-    // Complete the Q loads here: a lazy wait at the first MFMA would also
-    // wait for every global->LDS load in flight at that point.
-    wait_vmcnt<0>();
   }
 
   // ---- KV set of the query and this workgroup's slice of it
@@ -207,49 +254,56 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
-  const float *ksc = p.k_cmp_scale;
-  const float *vsc = p.v_cmp_scale;
-
   for (int cbase = 0; cbase < st.total; cbase += kChunkTiles) {
     const int ct = min(kChunkTiles, st.total - cbase);
-    block_sync();   // previous chunk is done with the row table
-    // -- page-table walk for the chunk's tiles
-    for (int idx = tid; idx < ct * kTile; idx += C::kThreads) {
-      const int j = cbase + idx / kTile;
-      const int r = idx % kTile;
-      int start, len;
-      bool cmp;
-      st.tile(j, start, len, cmp);
-      int64_t er = -1;
-      float a = 1.f, b = 1.f;
-      if (r < len) {
-        const int64_t row = entry_row(p, kv, qi, start + r);
-        if (row >= 0) {
-          er = row * p.hkv + g;
-          if (FP8 && cmp) {
-            a = ksc[er];
-            b = vsc[er];
-          }
+    block_sync();   // the previous chunk is done with the row table
+    // -- translation: all list loads of the batch, then all page-table loads
+    {
+      int32_t x[C::kPer];
+      bool cmpk[C::kPer];
+#pragma unroll
+      for (int u = 0; u < C::kPer; ++u) {
+        const int idx = tid + u * C::kThreads;
+        const int j = cbase + idx / kTile;
+        const int r = idx % kTile;
+        x[u] = -1;
+        cmpk[u] = false;
+        if (idx < ct * kTile) {
+          int start, len;
+          bool cmp;
+          st.tile(j, start, len, cmp);
+          cmpk[u] = cmp;
+          if (r < len) x[u] = entry_logical(p, kv, qi, start + r);
         }
       }
-      sm.erow[idx] = er;
-      sm.ks[idx] = a;
-      sm.vs[idx] = b;
+#pragma unroll
+      for (int u = 0; u < C::kPer; ++u) {
+        const int idx = tid + u * C::kThreads;
+        const int64_t row = logical_row(p, kv, cmpk[u], x[u]);
+        sm.erow[idx] = row >= 0 ? row * p.hkv + g : -1;
+        // a tile's 32 slots are 32 consecutive lanes of one wave
+        const uint64_t valid = __ballot(row >= 0);
+        if ((lane & 31) == 0) sm.tmask[idx / kTile] = (uint32_t)(valid >> (lane & 32));
+      }
     }
+    // Q loads and the translation loads complete here, before the ring starts:
+    // a wait placed lazily later would also wait for the tile loads in flight.
+    wait_vmcnt<0>();
     block_sync();
 
-    // -- issue the loads of chunk tile jj into ring buffer jj % kBufs
+    // -- issue the loads of chunk tile jj into ring buffer jj % NBUF
     auto issue = [&](int jj) {
       int start, len;
       bool cmp;
       st.tile(cbase + jj, start, len, cmp);
-      const int buf = jj % kBufs;
+      const int buf = jj % NBUF;
       const int64_t *er = &sm.erow[jj * kTile];
       if (!FP8 || !cmp) {
         const uint8_t *kb = cmp ? p.k_cmp : p.k_raw;
         const uint8_t *vb = cmp ? p.v_cmp : p.v_raw;
+        const uint8_t *src[C::kOps];
 #pragma unroll
-        for (int n0 = 0; n0 < C::kOps; ++n0) {
+        for (int n0 = 0; n0 < C::kOps; ++n0) {   // all row lookups first, then the loads
           const int n = wave + n0 * NW;
           const int which = n / (C::kKVInstr / 2);
           const int nn = n - which * (C::kKVInstr / 2);
@@ -258,9 +312,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
           const int cp = (lin % C::kRowB) / 16;
           const int c = cp ^ (r & (C::kChunks - 1));
           const int64_t e = er[r];
-          const uint8_t *src = e >= 0 ? (which ? vb : kb) + e * C::kRowB + c * 16
-                                      : kZeroRow + (lane & 15) * 16;
-          dma16(src, &sm.kv[buf][which][nn * 1024]);
+          src[n0] = e >= 0 ? (which ? vb : kb) + e * C::kRowB + c * 16 : kZeroRow + (lane & 15) * 16;
+        }
+#pragma unroll
+        for (int n0 = 0; n0 < C::kOps; ++n0) {
+          const int n = wave + n0 * NW;
+          const int which = n / (C::kKVInstr / 2);
+          const int nn = n - which * (C::kKVInstr / 2);
+          dma16(src[n0], &sm.kv[buf][which][nn * 1024]);
         }
       } else {
 #pragma unroll
@@ -273,9 +332,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
             const int r = lin / D;
             const int c = (lin % D) / 16;
             const int64_t e = er[r];
-            const uint8_t *src = e >= 0 ? (which ? p.v_cmp : p.k_cmp) + e * D + c * 16
-                                        : kZeroRow + (lane & 15) * 16;
+            const uint8_t *src = e >= 0 ? (which ? p.v_cmp : p.k_cmp) + e * D + c * 16 : kZeroRow + (lane & 15) * 16;
             dma16(src, &sm.stage[FP8 ? buf : 0][which][nn * 1024]);
+          } else if (n == C::kF8Instr) {
+            // the per-token scales: lanes 0-31 k, lanes 32-63 v
+            const int64_t e = er[lane & 31];
+            const float *sc = hi ? p.v_cmp_scale : p.k_cmp_scale;
+            const void *src = e >= 0 ? (const void *)(sc + e) : (const void *)kZeroRow;
+            dma4(src, &sm.scl[FP8 ? buf : 0][0]);
           } else {
             dma16(kZeroRow + (lane & 15) * 16, &sm.dummy[0]);   // keeps the count uniform
           }
@@ -283,21 +347,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
       }
     };
 
-    const int pre = min(kBufs - 1, ct);
+    const int pre = min(NBUF - 1, ct);
     for (int jj = 0; jj < pre; ++jj) issue(jj);
 
     for (int jj = 0; jj < ct; ++jj) {
-      if (jj + kBufs - 1 < ct) issue(jj + kBufs - 1);
-      const int ahead = min(kBufs - 1, ct - 1 - jj);   // tiles issued after jj
-      if (ahead >= 2) wait_vmcnt<2 * C::kOps>();
-      else if (ahead == 1) wait_vmcnt<C::kOps>();
-      else wait_vmcnt<0>();
+      if (jj + NBUF - 1 < ct) issue(jj + NBUF - 1);
+      wait_tiles<C::kOps, NBUF - 1>(min(NBUF - 1, ct - 1 - jj));   // tiles issued after jj
       block_sync();
 
       int start, len;
       bool cmp;
       st.tile(cbase + jj, start, len, cmp);
-      const int buf = jj % kBufs;
+      const int buf = jj % NBUF;
 
       if (FP8 && cmp) {
         // widen the staged e4m3 rows to bf16 (exact) into the swizzled tile
@@ -322,7 +383,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
         block_sync();
       }
 
-      if (wave * 32 + hgrp * 128 < p.group) {
+      if (wave_ok) {
         const uint8_t *Kt = sm.kv[buf][0];
         const uint8_t *Vt = sm.kv[buf][1];
         // S^T = K . Q^T
@@ -336,37 +397,62 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
           }
         }
-        // scale, mask, online softmax
-        const float *tks = &sm.ks[jj * kTile];
-        const float *tvs = &sm.vs[jj * kTile];
-        float x[16];
-        float tmax = -INFINITY;
+        // online softmax.  Lane rows: 8*(i/4) + 4*hi + i%4.  The max is taken
+        // on the raw scores (the scale c = scale*log2 e is positive), and
+        // p = exp2(s*c - m) is one FMA and one exp per score.
+        float sc[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 8 * (i >> 2) + 4 * hi + (i & 3);
-          float v = s[i] * p.scale_log2;
-          if (FP8 && cmp) v *= tks[r];
-          x[i] = r < len ? v : -INFINITY;
-          tmax = fmaxf(tmax, x[i]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m, tmax);
-        const bool live = m_new != -INFINITY;
-        const float alpha = live ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-        float psum = 0.f;
-        float pr[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pr[i] = live ? __builtin_amdgcn_exp2f(x[i] - m_new) : 0.f;
-          psum += pr[i];
-        }
-        l = l * alpha + psum;
-        m = m_new;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+        for (int i = 0; i < 16; ++i) sc[i] = s[i];
         if (FP8 && cmp) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pr[i] *= tvs[8 * (i >> 2) + 4 * hi + (i & 3)];
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 kk4 = *(const float4 *)(&sm.scl[FP8 ? buf : 0][8 * q4 + 4 * hi]);
+            sc[4 * q4 + 0] *= kk4.x;
+            sc[4 * q4 + 1] *= kk4.y;
+            sc[4 * q4 + 2] *= kk4.z;
+            sc[4 * q4 + 3] *= kk4.w;
+          }
+        }
+        const uint32_t tm = sm.tmask[jj];
+        if (tm != 0xFFFFFFFFu) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = 8 * (i >> 2) + 4 * hi + (i & 3);
+            sc[i] = ((tm >> r) & 1u) ? sc[i] : -INFINITY;
+          }
+        }
+        float smax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        smax = fmaxf(smax, fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])),
+                                 fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]))));
+        smax = fmaxf(smax, __shfl_xor(smax, 32));
+        const float tmax = smax * p.scale_log2;               // -inf stays -inf
+        const bool need = tmax > m + kTau;                     // same on both lanes of a head
+        if (__any(need)) {
+          const float alpha = need ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;   // m = -inf -> 0
+          m = need ? tmax : m;
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+        }
+        const float negm = m == -INFINITY ? 0.f : -m;          // all scores are -inf then
+        float pr[16];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.scale_log2, negm));
+          psum += pr[i];
+        }
+        l += psum;
+        if (FP8 && cmp) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 vv = *(const float4 *)(&sm.scl[FP8 ? buf : 0][32 + 8 * q4 + 4 * hi]);
+            pr[4 * q4 + 0] *= vv.x;
+            pr[4 * q4 + 1] *= vv.y;
+            pr[4 * q4 + 2] *= vv.z;
+            pr[4 * q4 + 3] *= vv.w;
+          }
         }
         bf16x8 pb[2];
 #pragma unroll
@@ -389,7 +475,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
               const int off = row * C::kRowB + (((d >> 3) ^ (row & (C::kChunks - 1))) * 16) + (L & 1) * 8;
               part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(Vt + off));
             }
-            typedef short i16x8 __attribute__((ext_vector_type(8)));
             const i16x8 cat = {part[0][0], part[0][1], part[0][2], part[0][3],
                                part[1][0], part[1][1], part[1][2], part[1][3]};
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[k2],
@@ -397,17 +482,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
           }
         }
       }
-      block_sync();   // ring buffer jj % kBufs may be refilled next
+      block_sync();   // ring buffer jj % NBUF may be refilled next
     }
   }
 
   // ---- epilogue
   const float lt = l + __shfl_xor(l, 32);
-  if (!head_ok) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse2 = (m == -INFINITY || !(lt > 0.f)) ? -INFINITY : m + __builtin_amdgcn_logf(lt);
   const float lse = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
   if (S == 1) {
+    if (!head_ok) return;
     uint16_t *orow = p.o + ((int64_t)qi * p.hq + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -415,43 +500,42 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const Params p) {
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d0 = 32 * db + 8 * i4 + 4 * hi;
         uint2 w;
-        const __bf16 b0 = (__bf16)(acc[db][4 * i4 + 0] * inv);
-        const __bf16 b1 = (__bf16)(acc[db][4 * i4 + 1] * inv);
-        const __bf16 b2 = (__bf16)(acc[db][4 * i4 + 2] * inv);
-        const __bf16 b3 = (__bf16)(acc[db][4 * i4 + 3] * inv);
-        w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        w.x = bf16_bits(acc[db][4 * i4 + 0] * inv) | (bf16_bits(acc[db][4 * i4 + 1] * inv) << 16);
+        w.y = bf16_bits(acc[db][4 * i4 + 2] * inv) | (bf16_bits(acc[db][4 * i4 + 3] * inv) << 16);
         *(uint2 *)(orow + d0) = w;
       }
     }
     if (hi == 0 && p.lse) p.lse[(int64_t)qi * p.hq + h] = lse;
-  } else {
-    const int64_t prow = ((int64_t)split * p.num_queries + qi) * p.hq + h;
-    float *orow = p.part_o + prow * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = 32 * db + 8 * i4 + 4 * hi;
-        float4 w = make_float4(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv,
-                               acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv);
-        *(float4 *)(orow + d0) = w;
-      }
-    }
-    if (hi == 0) p.part_lse[prow] = lse;
+    return;
   }
+
+  // split: write the sink-free partial; the merge kernel adds the sink
+  if (!head_ok) return;
+  const int64_t prow = ((int64_t)split * p.num_queries + qi) * p.hq + h;
+  float *orow = p.part_o + prow * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = 32 * db + 8 * i4 + 4 * hi;
+      *(float4 *)(orow + d0) = make_float4(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv,
+                                           acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv);
+    }
+  }
+  if (hi == 0) p.part_lse[prow] = lse;
 }
 
 template <int D, int NW, bool FP8>
 hipError_t launch_t(const Params &p, hipStream_t stream) {
-  dim3 grid((unsigned)p.num_queries * (unsigned)p.num_splits, (unsigned)(p.hkv * p.head_groups));
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, FP8>), grid, dim3(NW * 64), 0, stream, p);
+  constexpr int NBUF = 4;
+  const unsigned grid = (unsigned)p.jobs_per_xcd * 8u;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, FP8, NBUF>), dim3(grid), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool FP8>
 hipError_t launch_d(const Params &p, hipStream_t stream) {
-  const int heads = p.group < 128 ? p.group : 128;
+  const int heads = p.group < p.heads_per_block ? p.group : p.heads_per_block;
   if (heads <= 32) return launch_t<D, 1, FP8>(p, stream);
   if (heads <= 64) return launch_t<D, 2, FP8>(p, stream);
   return launch_t<D, 4, FP8>(p, stream);

@@ -24,7 +24,6 @@ struct Params {
   uint16_t *o;
   float *lse;
   float *part_o, *part_lse;           // split partials (num_splits > 1)
-  int32_t *counters;                  // per (query, KV head, head block) arrival counts
   int32_t *err_flag;
   int32_t raw_pt_stride, cmp_pt_stride;
   int32_t num_seqs, num_queries, hq, hkv, head_dim, page_size, window, ratio, topk, num_splits;

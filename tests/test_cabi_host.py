@@ -98,6 +98,8 @@ FAULTS = [
     ("head_dim_96", lambda a: setattr(a, "head_dim", 96), -4),
     ("misaligned_q", lambda a: setattr(a, "q", a.q + 2), -5),
     ("misaligned_out", lambda a: setattr(a, "o", a.o + 8), -5),
+    ("scale_zero", lambda a: setattr(a, "scale", 0.0), -2),
+    ("heads_per_block_48", lambda a: setattr(a, "heads_per_block", 48), -4),
     ("splits_zero", lambda a: setattr(a, "num_splits", 0), -7),
     ("splits_too_many", lambda a: setattr(a, "num_splits", 65), -7),
     ("decode_with_positions", lambda a: setattr(a, "query_pos", 0x20000000), -9),

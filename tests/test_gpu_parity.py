@@ -77,6 +77,29 @@ def test_split_invariance_decode():
             assert accept(O, L, ref[0], ref[1]).ok
 
 
+@pytest.mark.parametrize("hpb", [32, 64, 128])
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_heads_per_block_variants(hpb, splits):
+    p = synth.make_workload("decode_csa", batch=3)
+    check_against_oracle(p, num_splits=splits, heads_per_block=hpb, label=f"hpb{hpb}/s{splits}")
+
+
+def test_workspace_reused_across_calls():
+    """One workspace (never cleared) serves consecutive calls with different
+    split counts and shapes."""
+    from sparse_paged_attention_amd import api
+    ws = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device="cuda")   # NaN-ish garbage
+    for name, batch, s in (("decode_csa", 5, 4), ("decode_csa", 5, 4), ("decode_hca", 2, 7),
+                           ("mixed_fp8", 3, 3), ("decode_csa", 2, 8)):
+        p = synth.make_workload(name, batch=batch)
+        dp = api.DeviceProblem.from_problem(p)
+        O, L = api.forward(dp, s, workspace=ws)
+        torch.cuda.synchronize()
+        Oref, Lref = oracle.attention(p)
+        rep = accept(O.float().cpu().numpy(), L.cpu().numpy(), Oref, Lref)
+        assert rep.ok, (name, s, rep)
+
+
 def _repage(p, seed):
     rng = np.random.default_rng(seed)
     for kk, vv, pt, sc in (("k_raw", "v_raw", "raw_pt", None), ("k_cmp", "v_cmp", "cmp_pt", "scale")):
