@@ -86,19 +86,22 @@ def parse_args(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="0 = the default for the workload")
     ap.add_argument("--heads-per-block", type=int, default=-1,
                     help="query heads per workgroup (32/64/128, 0 = library choice, -1 = workload default)")
+    ap.add_argument("--queries-per-block", type=int, default=-1,
+                    help="queries per workgroup (1/2/4, 0 = library choice, -1 = workload default)")
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="total size of the input replicas the timed steps rotate through")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")
     return ap.parse_args(argv)
 
 
-DEFAULTS = {   # (num_splits, heads_per_block) per workload
-    "decode_csa": (8, 128), "decode_hca": (4, 0), "mixed_fp8": (8, 128), "prefill_csa": (1, 0), "tiny": (1, 0),
+DEFAULTS = {   # (num_splits, heads_per_block, queries_per_block) per workload; 0 = library choice
+    "decode_csa": (4, 64, 1), "decode_hca": (4, 0, 1), "mixed_fp8": (8, 64, 1), "prefill_csa": (1, 0, 0),
+    "tiny": (1, 0, 0),
 }
 
 
-def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, rotate_mb=640.0, batch=0,
-        cpu_budget=0.0, problem=None):
+def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries_per_block=-1,
+        rotate_mb=640.0, batch=0, cpu_budget=0.0, problem=None):
     """Time `steps` calls of the hot path; returns the result dict."""
     import ctypes
 
@@ -109,9 +112,10 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, rotate_
     lib = _lib.load()
     dev = torch.device("cuda:0")
     p = problem if problem is not None else synth.make_workload(workload, batch=batch or None)
-    d_splits, d_hpb = DEFAULTS.get(workload, (1, 0))
+    d_splits, d_hpb, d_qpb = DEFAULTS.get(workload, (1, 0, 0))
     splits = splits or d_splits
     hpb = d_hpb if heads_per_block < 0 else heads_per_block
+    qpb = d_qpb if queries_per_block < 0 else queries_per_block
     base = api.DeviceProblem.from_problem(p, device=dev)
 
     # metadata from the library itself, for the byte/FLOP accounting
@@ -129,7 +133,7 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, rotate_
     for r in range(reps):
         dp = base if r == 0 else api.DeviceProblem(
             **{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in base.__dict__.items()})
-        a = dp.args(splits, hpb)
+        a = dp.args(splits, hpb, qpb)
         o = torch.empty((p.num_queries, p.num_q_heads, p.head_dim), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((p.num_queries, p.num_q_heads), dtype=torch.float32, device=dev)
         need = api.workspace_size(a)
@@ -222,6 +226,7 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, rotate_
                    "q_heads": p.num_q_heads, "kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
                    "page_size": p.page_size, "window": p.window, "ratio": p.ratio, "topk": p.topk,
                    "kv_entries": kv_entries, "num_splits": splits, "heads_per_block": hpb,
+                   "queries_per_block": qpb,
                    "replicas": reps},
         "roofline": roof,
         "cpu_baseline": cpu_baseline(p, cpu_budget) if cpu_budget > 0 else None,
@@ -247,7 +252,7 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     out = run(args.workload, steps=args.steps, warmup=args.warmup, splits=args.splits,
-              heads_per_block=args.heads_per_block, rotate_mb=args.rotate_mb, batch=args.batch,
+              heads_per_block=args.heads_per_block, queries_per_block=args.queries_per_block, rotate_mb=args.rotate_mb, batch=args.batch,
               cpu_budget=args.cpu_budget)
     print(json.dumps(out), flush=True)
 

@@ -44,6 +44,7 @@ class SpaFwdArgs(ctypes.Structure):
         ("cmp_dtype", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
         ("heads_per_block", ctypes.c_int32),
+        ("queries_per_block", ctypes.c_int32),
         ("q", ctypes.c_void_p),
         ("k_raw", ctypes.c_void_p),
         ("v_raw", ctypes.c_void_p),

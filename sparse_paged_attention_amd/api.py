@@ -90,7 +90,8 @@ class DeviceProblem:
             sink=dev(p.sink) if p.sink is not None else None,
         )
 
-    def args(self, num_splits: Optional[int] = None, heads_per_block: int = 0) -> _lib.SpaFwdArgs:
+    def args(self, num_splits: Optional[int] = None, heads_per_block: int = 0,
+             queries_per_block: int = 0) -> _lib.SpaFwdArgs:
         a = _lib.SpaFwdArgs()
         a.num_seqs = self.num_seqs
         a.num_queries = self.num_queries
@@ -106,6 +107,7 @@ class DeviceProblem:
         a.cmp_dtype = _lib.SPA_FP8_E4M3_OCP if self.cmp_fp8 else _lib.SPA_BF16
         a.num_splits = self.num_splits if num_splits is None else num_splits
         a.heads_per_block = heads_per_block
+        a.queries_per_block = queries_per_block
         a.q = _ptr(self.q)
         a.k_raw = _ptr(self.k_raw)
         a.v_raw = _ptr(self.v_raw)
@@ -149,9 +151,9 @@ def forward_args(dp: DeviceProblem, args: _lib.SpaFwdArgs, o: torch.Tensor, lse:
 def forward(dp: DeviceProblem, num_splits: Optional[int] = None, *, err_flag: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None,
-            heads_per_block: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+            heads_per_block: int = 0, queries_per_block: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Run attn_fwd_decode / attn_fwd_prefill; returns (O bf16 [Nq,Hq,D], LSE f32 [Nq,Hq])."""
-    args = dp.args(num_splits, heads_per_block)
+    args = dp.args(num_splits, heads_per_block, queries_per_block)
     dev = dp.q.device
     if out is None:
         out = torch.empty((dp.num_queries, dp.num_q_heads, dp.head_dim), dtype=torch.bfloat16, device=dev)

@@ -69,6 +69,19 @@ spa_status validate(const spa_fwd_args *a, bool decode, bool need_outputs) {
   if (a->heads_per_block != 0 && a->heads_per_block != 32 && a->heads_per_block != 64 &&
       a->heads_per_block != 128)
     return fail(SPA_ERR_UNSUPPORTED, "heads_per_block %d not supported (0, 32, 64 or 128)", a->heads_per_block);
+  if (a->queries_per_block != 0 && a->queries_per_block != 1 && a->queries_per_block != 2 &&
+      a->queries_per_block != 4)
+    return fail(SPA_ERR_UNSUPPORTED, "queries_per_block %d not supported (0, 1, 2 or 4)", a->queries_per_block);
+  if (a->queries_per_block > 1 && a->num_splits > 1)
+    return fail(SPA_ERR_UNSUPPORTED, "queries_per_block > 1 needs num_splits == 1");
+  if (a->queries_per_block > 1) {
+    const int64_t group = a->num_q_heads / a->num_kv_heads;
+    const int64_t hpb = a->heads_per_block > 0 ? a->heads_per_block : 32;
+    const int64_t heads = group < hpb ? group : hpb;
+    const int64_t nh = heads <= 32 ? 1 : (heads <= 64 ? 2 : 4);
+    if (nh * a->queries_per_block > 4)
+      return fail(SPA_ERR_UNSUPPORTED, "heads_per_block/32 * queries_per_block must be <= 4");
+  }
   {
     const int64_t group = a->num_q_heads / a->num_kv_heads;
     const int64_t jobs = (int64_t)a->num_queries * a->num_kv_heads * a->num_splits * ((group + 31) / 32);
@@ -126,21 +139,42 @@ WorkspaceLayout workspace_layout(const spa_fwd_args *a) {
 
 size_t workspace_bytes_for(const spa_fwd_args *a) { return workspace_layout(a).total; }
 
+int32_t waves_for(const spa_fwd_args *a, int32_t hpb) {
+  const int64_t group = a->num_q_heads / a->num_kv_heads;
+  const int64_t heads = group < hpb ? group : hpb;
+  return heads <= 32 ? 1 : (heads <= 64 ? 2 : 4);
+}
+
+// Queries per workgroup for a given head block: prefill shares KV rows
+// between consecutive tokens; decode queries are independent sequences.
+int32_t queries_for(const spa_fwd_args *a, bool decode, int32_t hpb) {
+  if (a->queries_per_block > 0) return a->queries_per_block;
+  if (decode || a->num_splits > 1) return 1;
+  (void)hpb;
+  return 1;   // sharing a union stream costs more than it saves at the measured shapes
+}
+
+int64_t jobs_for(const spa_fwd_args *a, int32_t hpb, int32_t nq) {
+  const int64_t group = a->num_q_heads / a->num_kv_heads;
+  const int64_t groups = (a->num_queries + nq - 1) / nq;
+  return groups * a->num_kv_heads * a->num_splits * ((group + hpb - 1) / hpb);
+}
+
 // Query heads per workgroup: the requested value, or the largest of
 // 128/64/32 that still yields >= 256 workgroups (one per compute unit).
-int32_t pick_heads_per_block(const spa_fwd_args *a) {
+
+int32_t pick_heads_per_block(const spa_fwd_args *a, bool decode) {
   if (a->heads_per_block > 0) return a->heads_per_block;
-  const int64_t group = a->num_q_heads / a->num_kv_heads;
   int32_t hpb = 128;
   while (hpb > 32) {
-    const int64_t jobs = (int64_t)a->num_queries * a->num_kv_heads * a->num_splits * ((group + hpb - 1) / hpb);
-    if (jobs >= 256) break;
+    const int32_t nq = queries_for(a, decode, hpb);
+    if (waves_for(a, hpb) * nq <= 4 && jobs_for(a, hpb, nq) >= 256) break;
     hpb /= 2;
   }
   return hpb;
 }
 
-spa::Params make_params(const spa_fwd_args *a) {
+spa::Params make_params(const spa_fwd_args *a, bool decode) {
   spa::Params p{};
   p.q = static_cast<const uint16_t *>(a->q);
   p.k_raw = static_cast<const uint8_t *>(a->k_raw);
@@ -175,10 +209,11 @@ spa::Params make_params(const spa_fwd_args *a) {
   p.topk = a->ratio > 0 ? a->topk : 0;
   p.num_splits = a->num_splits;
   p.group = a->num_q_heads / a->num_kv_heads;
-  p.heads_per_block = pick_heads_per_block(a);
+  p.heads_per_block = pick_heads_per_block(a, decode);
+  p.queries_per_group = queries_for(a, decode, p.heads_per_block);
   p.head_groups = (p.group + p.heads_per_block - 1) / p.heads_per_block;
   {
-    const int64_t jobs = (int64_t)a->num_queries * a->num_kv_heads * a->num_splits * p.head_groups;
+    const int64_t jobs = jobs_for(a, p.heads_per_block, p.queries_per_group);
     p.total_jobs = (int32_t)jobs;
     p.jobs_per_xcd = (int32_t)((jobs + 7) / 8);
   }
@@ -191,7 +226,7 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
   spa_status st = validate(a, decode, true);
   if (st != SPA_OK) return st;
   if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return fail(SPA_ERR_SHAPE, "scale must be finite and > 0");
-  spa::Params p = make_params(a);
+  spa::Params p = make_params(a, decode);
   const size_t need = workspace_bytes_for(a);
   if (need > 0) {
     if (a->workspace == nullptr) return fail(SPA_ERR_WORKSPACE, "num_splits > 1 needs a workspace");
@@ -256,7 +291,7 @@ spa_status attn_build_gather(const spa_fwd_args *args, int32_t decode, int32_t c
   if (cap < 0) return fail(SPA_ERR_SHAPE, "cap must be >= 0");
   if ((int64_t)(cap > 0 ? (cap + 255) / 256 : 1) * args->num_queries > 0x7FFFFFFFLL)
     return fail(SPA_ERR_SHAPE, "cap * num_queries exceeds the launch grid");
-  spa::Params p = make_params(args);
+  spa::Params p = make_params(args, decode != 0);
   hipError_t e = spa::launch_gather(p, cap, rows_out, counts_out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "gather launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -63,18 +63,20 @@ __device__ __forceinline__ QueryKV query_kv(const Params &p, int32_t i) {
   return kv;
 }
 
+// A listed compressed id is usable only if it names a complete group.
+__device__ __forceinline__ int32_t check_cmp_id(const Params &p, const QueryKV &kv, int32_t c) {
+  if (c < 0 || c >= kv.n_c) {
+    flag_error(p, kErrCmpId);
+    return -1;
+  }
+  return c;
+}
+
 // Step 1: logical id of canonical entry e (a compressed id when e < n_sel,
 // else a raw position); -1 when the listed id is not a complete group.
 __device__ __forceinline__ int32_t entry_logical(const Params &p, const QueryKV &kv, int32_t i,
                                                  int32_t e) {
-  if (e < kv.n_sel) {
-    const int32_t c = p.topk > 0 ? p.cmp_idx[(int64_t)i * p.topk + e] : e;
-    if (c < 0 || c >= kv.n_c) {
-      flag_error(p, kErrCmpId);
-      return -1;
-    }
-    return c;
-  }
+  if (e < kv.n_sel) return check_cmp_id(p, kv, p.topk > 0 ? p.cmp_idx[(int64_t)i * p.topk + e] : e);
   return kv.win_lo + (e - kv.n_sel);
 }
 

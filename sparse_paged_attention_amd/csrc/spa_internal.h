@@ -29,8 +29,9 @@ struct Params {
   int32_t num_seqs, num_queries, hq, hkv, head_dim, page_size, window, ratio, topk, num_splits;
   int32_t group;                      // Hq / Hkv
   int32_t heads_per_block;            // query heads per workgroup: 32, 64 or 128
+  int32_t queries_per_group;          // queries a workgroup serves together: 1, 2 or 4
   int32_t head_groups;                // ceil(group / heads_per_block)
-  int32_t total_jobs;                 // Nq * Hkv * num_splits * head_groups
+  int32_t total_jobs;                 // ceil(Nq / queries_per_group) * Hkv * num_splits * head_groups
   int32_t jobs_per_xcd;               // ceil(total_jobs / 8)
   int32_t cmp_fp8;
   float scale_log2;                   // scale * log2(e)

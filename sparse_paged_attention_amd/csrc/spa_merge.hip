@@ -31,25 +31,43 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ o_
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const float sk = sink ? sink[row % hq] : -INFINITY;
+  // loads are issued 8 parts at a time so that they are in flight together
   float M = sk;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lse_parts[(int64_t)s * rows + row]);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float ls[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ls[k] = s0 + k < S ? lse_parts[(int64_t)(s0 + k) * rows + row] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) M = fmaxf(M, ls[k]);
+  }
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   float lse = -INFINITY;
   if (M != -INFINITY) {
     float Z = sk == -INFINITY ? 0.f : __expf(sk - M);
-    for (int s = 0; s < S; ++s) {
-      const float ls = lse_parts[(int64_t)s * rows + row];
-      const float w = ls == -INFINITY ? 0.f : __expf(ls - M);
-      Z += w;
-      const float *src = o_parts + ((int64_t)s * rows + row) * D + lane * E;
-      if constexpr (E == 2) {
-        const float2 v = *(const float2 *)src;
-        o[0] += w * v.x;
-        o[1] += w * v.y;
-      } else {
-        o[0] += w * src[0];
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float ls[8];
+      float v[8][E];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool in = s0 + k < S;
+        ls[k] = in ? lse_parts[(int64_t)(s0 + k) * rows + row] : -INFINITY;
+        const float *src = o_parts + ((int64_t)(s0 + k) * rows + row) * D + lane * E;
+        if constexpr (E == 2) {
+          const float2 t = in ? *(const float2 *)src : make_float2(0.f, 0.f);
+          v[k][0] = t.x;
+          v[k][E - 1] = t.y;
+        } else {
+          v[k][0] = in ? src[0] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float w = ls[k] == -INFINITY ? 0.f : __expf(ls[k] - M);
+        Z += w;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] += w * v[k][e];
       }
     }
     const float inv = 1.f / Z;

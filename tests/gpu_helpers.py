@@ -26,18 +26,20 @@ def to_numpy_bf16(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def run_hip(p, num_splits=None, err_flag=None, heads_per_block=0):
+def run_hip(p, num_splits=None, err_flag=None, heads_per_block=0, queries_per_block=0):
     from sparse_paged_attention_amd import api
     dp = api.DeviceProblem.from_problem(p)
-    O, L = api.forward(dp, num_splits, err_flag=err_flag, heads_per_block=heads_per_block)
+    O, L = api.forward(dp, num_splits, err_flag=err_flag, heads_per_block=heads_per_block,
+                       queries_per_block=queries_per_block)
     torch.cuda.synchronize()
     return to_numpy_bf16(O), L.cpu().numpy().astype(np.float64), dp
 
 
-def check_against_oracle(p, num_splits=None, queries=None, label="", heads_per_block=0):
+def check_against_oracle(p, num_splits=None, queries=None, label="", heads_per_block=0,
+                         queries_per_block=0):
     announce(f"{label or p.name}: Nq={p.num_queries} Hq={p.num_q_heads} D={p.head_dim} "
-             f"splits={num_splits or p.num_splits} hpb={heads_per_block}")
-    O, L, _ = run_hip(p, num_splits, heads_per_block=heads_per_block)
+             f"splits={num_splits or p.num_splits} hpb={heads_per_block} qpb={queries_per_block}")
+    O, L, _ = run_hip(p, num_splits, heads_per_block=heads_per_block, queries_per_block=queries_per_block)
     Oref, Lref = oracle.attention(p, queries)
     if queries is not None:
         O, L = O[queries], L[queries]
