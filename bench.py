@@ -27,6 +27,58 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# the sources whose change invalidates counter-measured traffic
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
+                  for f in ("spa_attention.hip", "spa_device.h", "spa_internal.h", "spa_api.cpp")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, cfg):
+    """HBM bytes per attention launch from the committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or
+    None when none matches this workload, launch configuration and kernel
+    source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = data.get(workload)
+    if not e or e.get("kernel_source") != kernel_source_hash():
+        return None
+    if any(e.get("config", {}).get(k) != cfg.get(k) for k in ("batch", "num_splits", "heads_per_block",
+                                                                "queries_per_block")):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def copy_calibration(mib, steps):
+    """A plain device-to-device copy of `mib` MiB, `steps` times: the known
+    reference (mib MiB read and written per launch) for the FETCH_SIZE and
+    WRITE_SIZE counters."""
+    import torch
+    n = int(mib * (1 << 20))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"copy_mib": mib, "launches": steps, "ms_per_copy": ms, "gbs_read_plus_write": 2 * n / (ms / 1e3) / 1e9}
 
 
 def algorithmic_work(p, counts):
@@ -91,6 +143,11 @@ def parse_args(argv=None):
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="total size of the input replicas the timed steps rotate through")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="time host-launched calls only (no graph capture), e.g. under counter collection")
+    ap.add_argument("--copy-mib", type=float, default=0.0,
+                    help="instead of the attention: time a plain device copy of this many MiB "
+                         "(the reference for the traffic counters)")
     return ap.parse_args(argv)
 
 
@@ -101,7 +158,7 @@ DEFAULTS = {   # (num_splits, heads_per_block, queries_per_block) per workload; 
 
 
 def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries_per_block=-1,
-        rotate_mb=640.0, batch=0, cpu_budget=0.0, problem=None):
+        rotate_mb=640.0, batch=0, cpu_budget=0.0, problem=None, eager_only=False):
     """Time `steps` calls of the hot path; returns the result dict."""
     import ctypes
 
@@ -167,32 +224,62 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
     wall = time.perf_counter() - t_wall0
     eager_ms = e0.elapsed_time(e1) / steps
 
-    # graph: the same `steps` launches captured once and replayed, so the GPU
-    # runs them back to back with no host in the loop
-    cap_stream = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(cap_stream):
-        stream = cap_stream.cuda_stream
-        for k in range(3):
-            step(k)
-        cap_stream.synchronize()
-        with torch.cuda.graph(graph, stream=cap_stream):
-            stream = torch.cuda.current_stream().cuda_stream
-            for k in range(steps):
-                step(k)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    reps_g = 5
-    ge = [torch.cuda.Event(enable_timing=True) for _ in range(reps_g + 1)]
-    ge[0].record()
-    for r in range(reps_g):
-        graph.replay()
-        ge[r + 1].record()
-    torch.cuda.synchronize()
-    per = np.array([ge[r].elapsed_time(ge[r + 1]) / steps for r in range(reps_g)])   # ms per launch
-    ms_per_step = float(ge[0].elapsed_time(ge[reps_g]) / (steps * reps_g))
-    kernel_ms = ms_per_step
+    def replay_ms(launch, n):
+        """Per-launch time of `n` calls of `launch(stream, k)` captured in one
+        HIP graph and replayed 5 times back to back (HIP events on the
+        capture stream)."""
+        cap_stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap_stream):
+            for k in range(3):
+                launch(cap_stream.cuda_stream, k)
+            cap_stream.synchronize()
+            with torch.cuda.graph(graph, stream=cap_stream):
+                cs = torch.cuda.current_stream()
+                for k in range(n):
+                    launch(cs.cuda_stream, k)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            reps_g = 5
+            ge = [torch.cuda.Event(enable_timing=True) for _ in range(reps_g + 1)]
+            ge[0].record(cap_stream)
+            for r in range(reps_g):
+                graph.replay()
+                ge[r + 1].record(cap_stream)
+            torch.cuda.synchronize()
+        per = np.array([ge[r].elapsed_time(ge[r + 1]) / n for r in range(reps_g)])
+        return float(ge[0].elapsed_time(ge[reps_g]) / (n * reps_g)), per
+
+    def fwd_launch(s, k):
+        st = fn(prepared[k % reps], s)
+        if st != 0:
+            _lib.check(st)
+
+    if eager_only:
+        ms_per_step, per = eager_ms, np.array([eager_ms])
+        merge_ms = 0.0
+    else:
+        # the whole step: attention (+ the LSE merge when split)
+        ms_per_step, per = replay_ms(fwd_launch, steps)
+        # the merge alone (same launch through its own entry point, on the
+        # partials the step left in each replica's workspace), so that the
+        # attention kernel's own duration is the difference
+        merge_ms = 0.0
+        if splits > 1:
+            rows = p.num_queries * p.num_q_heads
+            lse_off = ((rows * p.head_dim * 4 * splits) + 255) // 256 * 256
+            sink_ptr = base.sink.data_ptr() if base.sink is not None else None
+
+            def merge_launch(s, k):
+                _, a, o, lse, ws = replicas[k % reps]
+                st = lib.attn_merge_lse(ws.data_ptr(), ws.data_ptr() + lse_off, splits, rows, p.head_dim,
+                                        p.num_q_heads, sink_ptr, o.data_ptr(), lse.data_ptr(), s)
+                if st != 0:
+                    _lib.check(st)
+
+            merge_ms, _ = replay_ms(merge_launch, steps)
+    kernel_ms = ms_per_step - merge_ms
 
     nq = p.num_queries
     decode = p.mode == "decode"
@@ -203,9 +290,11 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
         roof = {"bound": "mfma", "achieved": alg_flops / (kernel_ms / 1e3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = None   # filled in below from the committed counter runs, if they match
     roof["kernel"] = "attn_fwd_kernel"
     roof["kernel_ms"] = kernel_ms
+    roof["kernel_ms_how"] = ("graph replay of the step minus graph replay of the merge alone" if merge_ms > 0
+                             else "graph replay of the step (one kernel)")
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["algorithmic_flops_per_launch"] = alg_flops
 
@@ -233,10 +322,12 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
         "timing": {"graph_replay_ms_per_step_min": float(per.min()),
                    "graph_replay_ms_per_step_max": float(per.max()),
                    "eager_ms_per_step": eager_ms,
+                   "merge_ms": merge_ms,
                    "host_wall_ms_per_step": wall / steps * 1e3,
                    "tflops": alg_flops / (ms_per_step / 1e3) / 1e12,
                    "gbs_step": alg_bytes / (ms_per_step / 1e3) / 1e9},
     }
+    out["roofline"]["traffic"] = measured_traffic(workload, out["config"])
     return out
 
 
@@ -251,9 +342,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_mib > 0:
+        print(json.dumps(copy_calibration(args.copy_mib, args.steps)), flush=True)
+        return
     out = run(args.workload, steps=args.steps, warmup=args.warmup, splits=args.splits,
               heads_per_block=args.heads_per_block, queries_per_block=args.queries_per_block, rotate_mb=args.rotate_mb, batch=args.batch,
-              cpu_budget=args.cpu_budget)
+              cpu_budget=args.cpu_budget, eager_only=args.eager_only)
     print(json.dumps(out), flush=True)
 
 
