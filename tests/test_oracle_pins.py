@@ -317,6 +317,32 @@ def test_merge_contiguous_splits_and_empty():
     assert np.all(empty[1] == -np.inf) and np.all(empty[0] == 0)
 
 
+def test_lse_merge_arrays_flat_rows():
+    """The flat-array merge (rows = query * Hq + head, sink of row r is
+    sink[r % Hq]) over 3 contiguous partials of every query's KV set equals the
+    sink-folded single pass, query by query and head by head."""
+    p = synth.make_workload("tiny")
+    scale = float(p.scale)
+    Hq, D, S = p.num_q_heads, p.head_dim, 3
+    o_parts = np.zeros((S, p.num_queries * Hq, D))
+    lse_parts = np.zeros((S, p.num_queries * Hq))
+    for i in range(p.num_queries):
+        s = A.kv_set(p, i)
+        K, V = A.gather_rows(p, s)
+        q = A.query_f64(p, i)
+        for j, (a, b) in enumerate(A.partial_split(len(K), S)):
+            o, l = A.attend_partial(q, K[a:b], V[a:b], scale)
+            o_parts[j, i * Hq:(i + 1) * Hq] = o
+            lse_parts[j, i * Hq:(i + 1) * Hq] = l
+    O, L = A.lse_merge_arrays(o_parts, lse_parts, p.sink, Hq)
+    Oref, Lref = oracle.attention(p)
+    np.testing.assert_allclose(O.reshape(Oref.shape), Oref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L.reshape(Lref.shape), Lref, rtol=0, atol=1e-12)
+    # a sink row mapping shifted by one head must not pass
+    O2, _ = A.lse_merge_arrays(o_parts, lse_parts, np.roll(p.sink, 1), Hq)
+    assert np.abs(O2.reshape(Oref.shape) - Oref).max() > 1e-6
+
+
 def test_partial_split_covers():
     for n in range(0, 50):
         for S in range(1, 9):
