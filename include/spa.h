@@ -93,15 +93,12 @@ typedef struct spa_fwd_args {
   int32_t raw_dtype;      /* spa_dtype: must be SPA_BF16                         */
   int32_t cmp_dtype;      /* spa_dtype: SPA_BF16 or SPA_FP8_E4M3_OCP             */
   int32_t num_splits;     /* 1 = one pass; >1 = split-KV partials + LSE merge    */
-  int32_t heads_per_block; /* query heads one workgroup computes: 32, 64 or 128,
-                              or 0 = chosen by the library (a tuning knob; the
-                              result does not depend on it)                       */
-  int32_t queries_per_block; /* queries one workgroup serves together, sharing
-                              the KV rows they have in common: 1, 2 or 4 (with
-                              heads_per_block/32 * queries_per_block <= 4 and
-                              num_splits == 1 when above 1), or 0 = chosen by
-                              the library (currently 1); a
-                              tuning knob, the result does not depend on it  */
+  int32_t heads_per_block; /* query heads one job computes, sharing each KV
+                              tile: 32 or 64, or 0 = chosen by the library (64
+                              when the KV group has more than 32 heads); a
+                              tuning knob, the result does not depend on it    */
+  int32_t queries_per_block; /* queries one job serves: 0 or 1 (one query per
+                              job; other values are rejected)                   */
 
   const void *q;          /* bf16 [Nq, Hq, D]                                    */
   const void *k_raw;      /* bf16 [raw_pages, P, Hkv, D]                         */

@@ -66,22 +66,10 @@ spa_status validate(const spa_fwd_args *a, bool decode, bool need_outputs) {
     return fail(SPA_ERR_DTYPE, "cmp_dtype %d unknown", a->cmp_dtype);
   if (a->num_splits < 1 || a->num_splits > SPA_MAX_SPLITS)
     return fail(SPA_ERR_SPLITS, "num_splits %d outside [1, %d]", a->num_splits, SPA_MAX_SPLITS);
-  if (a->heads_per_block != 0 && a->heads_per_block != 32 && a->heads_per_block != 64 &&
-      a->heads_per_block != 128)
-    return fail(SPA_ERR_UNSUPPORTED, "heads_per_block %d not supported (0, 32, 64 or 128)", a->heads_per_block);
-  if (a->queries_per_block != 0 && a->queries_per_block != 1 && a->queries_per_block != 2 &&
-      a->queries_per_block != 4)
-    return fail(SPA_ERR_UNSUPPORTED, "queries_per_block %d not supported (0, 1, 2 or 4)", a->queries_per_block);
-  if (a->queries_per_block > 1 && a->num_splits > 1)
-    return fail(SPA_ERR_UNSUPPORTED, "queries_per_block > 1 needs num_splits == 1");
-  if (a->queries_per_block > 1) {
-    const int64_t group = a->num_q_heads / a->num_kv_heads;
-    const int64_t hpb = a->heads_per_block > 0 ? a->heads_per_block : 32;
-    const int64_t heads = group < hpb ? group : hpb;
-    const int64_t nh = heads <= 32 ? 1 : (heads <= 64 ? 2 : 4);
-    if (nh * a->queries_per_block > 4)
-      return fail(SPA_ERR_UNSUPPORTED, "heads_per_block/32 * queries_per_block must be <= 4");
-  }
+  if (a->heads_per_block != 0 && a->heads_per_block != 32 && a->heads_per_block != 64)
+    return fail(SPA_ERR_UNSUPPORTED, "heads_per_block %d not supported (0, 32 or 64)", a->heads_per_block);
+  if (a->queries_per_block != 0 && a->queries_per_block != 1)
+    return fail(SPA_ERR_UNSUPPORTED, "queries_per_block %d not supported (0 or 1)", a->queries_per_block);
   {
     const int64_t group = a->num_q_heads / a->num_kv_heads;
     const int64_t jobs = (int64_t)a->num_queries * a->num_kv_heads * a->num_splits * ((group + 31) / 32);
@@ -139,39 +127,12 @@ WorkspaceLayout workspace_layout(const spa_fwd_args *a) {
 
 size_t workspace_bytes_for(const spa_fwd_args *a) { return workspace_layout(a).total; }
 
-int32_t waves_for(const spa_fwd_args *a, int32_t hpb) {
-  const int64_t group = a->num_q_heads / a->num_kv_heads;
-  const int64_t heads = group < hpb ? group : hpb;
-  return heads <= 32 ? 1 : (heads <= 64 ? 2 : 4);
-}
-
-// Queries per workgroup for a given head block: prefill shares KV rows
-// between consecutive tokens; decode queries are independent sequences.
-int32_t queries_for(const spa_fwd_args *a, bool decode, int32_t hpb) {
-  if (a->queries_per_block > 0) return a->queries_per_block;
-  if (decode || a->num_splits > 1) return 1;
-  (void)hpb;
-  return 1;   // sharing a union stream costs more than it saves at the measured shapes
-}
-
-int64_t jobs_for(const spa_fwd_args *a, int32_t hpb, int32_t nq) {
-  const int64_t group = a->num_q_heads / a->num_kv_heads;
-  const int64_t groups = (a->num_queries + nq - 1) / nq;
-  return groups * a->num_kv_heads * a->num_splits * ((group + hpb - 1) / hpb);
-}
-
-// Query heads per workgroup: the requested value, or the largest of
-// 128/64/32 that still yields >= 256 workgroups (one per compute unit).
-
-int32_t pick_heads_per_block(const spa_fwd_args *a, bool decode) {
+// Query heads per job: 64 (two compute waves sharing each KV tile) unless
+// the KV group has at most 32 heads, or the caller's choice.
+int32_t pick_heads_per_block(const spa_fwd_args *a) {
   if (a->heads_per_block > 0) return a->heads_per_block;
-  int32_t hpb = 128;
-  while (hpb > 32) {
-    const int32_t nq = queries_for(a, decode, hpb);
-    if (waves_for(a, hpb) * nq <= 4 && jobs_for(a, hpb, nq) >= 256) break;
-    hpb /= 2;
-  }
-  return hpb;
+  const int64_t group = a->num_q_heads / a->num_kv_heads;
+  return group > 32 ? 64 : 32;
 }
 
 spa::Params make_params(const spa_fwd_args *a, bool decode) {
@@ -209,14 +170,14 @@ spa::Params make_params(const spa_fwd_args *a, bool decode) {
   p.topk = a->ratio > 0 ? a->topk : 0;
   p.num_splits = a->num_splits;
   p.group = a->num_q_heads / a->num_kv_heads;
-  p.heads_per_block = pick_heads_per_block(a, decode);
-  p.queries_per_group = queries_for(a, decode, p.heads_per_block);
+  p.heads_per_block = pick_heads_per_block(a);
   p.head_groups = (p.group + p.heads_per_block - 1) / p.heads_per_block;
-  {
-    const int64_t jobs = jobs_for(a, p.heads_per_block, p.queries_per_group);
-    p.total_jobs = (int32_t)jobs;
-    p.jobs_per_xcd = (int32_t)((jobs + 7) / 8);
-  }
+  p.jobs_per_unit = p.num_splits * p.head_groups;
+  p.unit_begin = 0;
+  p.unit_end = 0;   // set per launch
+  p.page_shift = -1;
+  for (int32_t sh = 0; sh < 31; ++sh)
+    if ((int32_t(1) << sh) == a->page_size) p.page_shift = sh;
   p.cmp_fp8 = (a->ratio > 0 && a->cmp_dtype == SPA_FP8_E4M3_OCP) ? 1 : 0;
   p.scale_log2 = a->scale * 1.4426950408889634f;
   return p;

@@ -4,71 +4,76 @@
 // with sink", section "Reuse and arithmetic" — the selected compressed KV, the
 // full recent raw window and a per-head sink logit share one softmax
 // denominator; the sink has no value row; P and O are bf16, LSE is fp32
-// natural log.  The KV set and page translation live in spa_device.h.
+// natural log.  The KV set and page translation rules live in spa_device.h.
 //
-// Work decomposition.  A job is (query group, KV head, KV slice, block of
-// query heads).  A query group is NQ queries (1 for decode; consecutive
-// prefill tokens otherwise).  All query heads of a KV head read the same KV
-// rows, and consecutive tokens of one sequence read mostly the same rows
-// (overlapping windows, mostly shared compressed groups), so a workgroup
-// streams one KV stream for the whole group through LDS and every compute
-// wave feeds each tile to bf16 MFMAs for its (token, 32 query heads):
+// Work decomposition.  A job is (query, KV head, KV slice, block of 32*NH
+// query heads); all query heads of a KV head read the same KV rows, so one
+// job streams its KV rows once through LDS and each compute wave feeds every
+// tile to bf16 MFMAs for its 32 heads:
 //
 //   S^T[kv, head]  = K[kv, :] . Q^T[:, head]        v_mfma_f32_32x32x16_bf16
 //   O^T[d, head]  += V^T[d, kv] . P^T[kv, head]      v_mfma_f32_32x32x16_bf16
 //
 // With S^T and O^T in the MFMA accumulator layout every lane owns one query
-// head (lane % 32), so the online-softmax state (m, l) is per lane; the row
-// max needs one exchange with lane ^ 32, and P^T goes from the S^T
-// accumulators straight into the B operand of the PV MFMA (the KV order inside
-// a 16-row step is permuted identically on both operands).  V^T comes from the
-// row-major V tile through the gfx950 LDS transpose read (ds_read_b64_tr_b16),
-// so no transposition pass is needed.
+// head (lane % 32): the online-softmax state (m, l) is per lane, the row max
+// needs one exchange with lane ^ 32, and P^T goes from the S^T accumulators
+// straight into the B operand of the PV MFMA (the KV order inside a 16-row
+// step is permuted identically on both operands).  V^T comes from the
+// row-major V tile through the gfx950 LDS transpose read (ds_read_b64_tr_b16).
 //
-// The group's stream.  When the group's queries belong to one sequence, sit
-// within one window span of each other and (for a listed layer) their group
-// ids fit an LDS bitmap, the stream is the union of their KV sets: the union
-// of the compressed lists (built in LDS: one bit per (id, token), then
-// compacted in ascending id order), then the union of the windows; each row
-// carries a token mask and every compute wave masks the rows its token does
-// not see.  Otherwise the workgroup makes one pass per query over that
-// query's own set.  Masked work is never counted as useful.
+// Persistent workgroups.  The grid holds as many workgroups as are resident
+// at once; each runs a static list of jobs.  Jobs are grouped in units (one
+// query and KV head: its slices and head blocks read the same rows); units
+// are dealt to the 8 XCDs round-robin (unit u to XCD u % 8, so every XCD gets
+// a mix of short and long KV sets) and, within an XCD, consecutive jobs go to
+// consecutive workgroups, so the jobs of one unit share that XCD's L2.  This
+// affects speed only, never results.
 //
-// Grid.  Jobs are numbered (group, KV head, slice, head block) with the head
-// block fastest and dealt to the 8 XCDs in contiguous ranges (workgroup w runs
-// job (w % 8) * ceil(jobs/8) + w / 8), so the head blocks that read the same
-// KV rows land on one XCD and share its L2.  This affects speed only, never
-// results.
+// One tile stream per workgroup.  The workgroup's jobs form one stream of
+// 32-row tiles: per job a Q tile (its query's rows for the head block) and
+// then its KV tiles (selected compressed rows, then the window; an empty set
+// gets one fully masked tile).  A producer wave (the last wave) runs the
+// stream through two rings of 4 LDS slots, one for K and one for V (a Q tile
+// puts heads 0-31 in its K slot and 32-63 in its V slot), with direct
+// global->LDS loads (global_load_lds_dwordx4 / _dword: no VGPR staging), and
+// translates rows ahead of those loads in two stages that are direct loads
+// into small LDS rings as well.  Step t of the stream issues K of tile t+4,
+// V of tile t+3, the page-table entries of tile t+7 and the list entries of
+// tile t+10.  Every step issues the same number of loads (padding loads read
+// a static zero row into a scratch area), so one vmcnt immediate tracks
+// everything: the data of a step's loads is complete three steps later,
+// which is when the next stage (or the compute waves) reads it.  The per-job
+// metadata is computed once, up front, one job per producer lane.
 //
-// Data movement.  The rows of up to 16 tiles are translated first (list
-// loads for the whole batch, then page-table loads), then every tile is
-// fetched by direct global->LDS loads (global_load_lds_dwordx4, 16 B per
-// lane, no VGPR staging) into a ring of NBUF LDS buffers.  One extra wave per
-// workgroup is the producer: it issues all tile loads and waits for them, so
-// the compute waves never stall on a full memory queue; one barrier per tile
-// hands a filled buffer to the compute waves and returns the previous one.
-// Masked rows are fetched from a static zero row and excluded through the
-// per-tile row masks, so the producer issues the same number of loads per
-// tile and one vmcnt immediate tracks the ring.  LDS rows are XOR-swizzled in
-// 16-byte chunks so that the K reads (one row per lane) and the transpose
-// reads (4 rows x 32 B per 16 lanes) are free of bank conflicts.
-//
-// FP8 (OCP e4m3) compressed rows land in an LDS staging area, together with
-// their fp32 per-token scales (one 4-byte direct load per row), and are
-// widened to bf16 exactly (every e4m3 value is a bf16 value) by the hardware
-// v_cvt_pk_f32_fp8; the scales are applied in fp32 to the scores (k) and to
-// P (v), so the MFMAs see the exact codes.
+// Compute waves.  Barrier t hands K of tile t+1 and V of tile t over (the
+// producer waits for them first); in step t the compute waves take the
+// scores of tile t+1 and the softmax and PV product of tile t, and the
+// producer refills the K slot of tile t and the V slot of tile t-1.  A Q
+// tile is copied into the Q fragments before the scores of its job's first
+// KV tile; after a job's last KV tile the epilogue writes its output and the
+// state is reset for the next job.
 //
 // Softmax runs in the log2 domain (scores pre-multiplied by scale*log2 e,
 // sink by log2 e) with v_exp_f32; with one slice the running max starts at
 // the sink and the running sum at exp(0) = 1, i.e. the sink is folded into
-// (m, l) from the start.  With num_splits > 1 (decode) each slice writes a
-// sink-free partial (O_s f32, LSE_s) to the workspace and the merge kernel
+// (m, l) from the start.  With num_splits > 1 each slice writes a sink-free
+// partial (O_s f32, LSE_s) to the workspace and the merge kernel
 // (spa_merge.hip) combines them, adding the sink exactly once.
+//
+// FP8 (OCP e4m3) compressed rows land in an LDS staging area, together with
+// their fp32 per-token scales, and are widened to bf16 exactly (every e4m3
+// value is a bf16 value) by v_cvt_pk_f32_fp8; the scales are applied in fp32
+// to the scores (k) and to P (v), so the MFMAs see the exact codes.
+//
+// Invalid metadata (a listed id that is not a complete group, a page id
+// outside its pool, a page-table column past the table, a bad count or
+// position) masks the entry, sets a bit in err_flag and is never loaded.
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "spa_device.h"
 
@@ -82,9 +87,10 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-constexpr int kTile = 32;        // KV rows per tile
-constexpr int kChunkTiles = 16;  // tiles translated per page-table pass
-constexpr int kUnionCap = 4096;  // compressed ids a group union may span
+constexpr int kTile = 32;      // KV rows per tile
+constexpr int kRing = 4;       // LDS tile slots
+constexpr int kXRing = 8;      // translation ring slots (list, page-table and id entries)
+constexpr int kStages = 2;     // translation loads per step (page table, list)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // The running max used for the exponentials moves only when a tile's max
@@ -93,7 +99,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 // reference value gives the same softmax; only the rounding differs.
 constexpr float kTau = 8.f;
 
-// Source of the 16-byte loads for masked rows (and of padding loads).
+// Tile descriptor flags.
+enum : uint32_t { kTileQ = 1, kTileKV = 2, kTileCmp = 4, kTileLast = 8, kTileWiden = 16 };
+
+// Source of the padding loads and of the loads for masked rows.
 __device__ __attribute__((aligned(16))) const uint8_t kZeroRow[256] = {};
 
 // LDS byte offset of a generic pointer into shared memory: the LDS aperture
@@ -133,24 +142,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until at most `ahead` tiles of OPS loads each are still in flight.
-template <int OPS, int MAXA>
-__device__ __forceinline__ void wait_tiles(int ahead) {
-  static_assert(MAXA <= 5 && MAXA * OPS < 64, "ring depth");
-  if (MAXA >= 5 && ahead >= 5) wait_vmcnt<(MAXA >= 5 ? 5 * OPS : 0)>();
-  else if (MAXA >= 4 && ahead >= 4) wait_vmcnt<(MAXA >= 4 ? 4 * OPS : 0)>();
-  else if (MAXA >= 3 && ahead >= 3) wait_vmcnt<(MAXA >= 3 ? 3 * OPS : 0)>();
-  else if (MAXA >= 2 && ahead >= 2) wait_vmcnt<(MAXA >= 2 ? 2 * OPS : 0)>();
-  else if (MAXA >= 1 && ahead >= 1) wait_vmcnt<OPS>();
-  else wait_vmcnt<0>();
-}
-
 // Workgroup barrier that waits only for this wave's LDS operations.  The
 // HIP __syncthreads() adds a workgroup release fence, which on gfx950 also
 // waits for every outstanding global load and would drain the LDS ring;
 // global->LDS loads are instead completed explicitly with wait_vmcnt<>.
 // The "memory" clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// max(v, v of lane ^ 32): v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second, so with both holding v
+// each lane ends up with its own value in one register and its partner's in
+// the other.  (Written as asm: the builtin is folded wrongly when both
+// operands are the same value.)
+__device__ __forceinline__ float max_lane_pair(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
 
 __device__ __forceinline__ uint32_t pack_bf16_hi(float lo, float hi) {
   // exact narrowing for values that are bf16 already (widened e4m3 codes)
@@ -161,597 +169,719 @@ __device__ __forceinline__ int round_up(int x, int m) { return (x + m - 1) / m *
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
-template <int D, int NH, int NQ, bool FP8, int NBUF>
+// LDS layout of a tile: row r (2D bytes) holds logical 16-byte chunk c at
+// physical chunk c ^ swz(r).  For D 128 (16 chunks) the permutation makes
+// both access patterns conflict-free: the K (and Q) reads, where 16 lanes
+// read one chunk of 16 consecutive rows, and the V transpose reads, where 16
+// lanes read 2 adjacent chunks of 4 consecutive rows.  For D 64 (8 chunks,
+// two rows per bank sweep) the K reads are conflict-free.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (r >> 1) & 7;
+}
+
+// ---------------------------------------------------------------- job lists
+// Job k of workgroup (XCD x, index y of Gx on that XCD): local index
+// l = y + k Gx, unit unit_begin + x + 8 floor(l / R), job r = l % R of the
+// unit (R = jobs_per_unit; r = split * head_groups + head block).
+struct JobId {
+  int32_t qi, g, split, hb;
+  bool valid;
+};
+
+__device__ __forceinline__ JobId job_id(const Params &p, int32_t x, int32_t y, int32_t Gx, int32_t k) {
+  const int32_t R = p.jobs_per_unit;
+  const int32_t l = y + k * Gx;
+  const int32_t m = l / R;
+  const int32_t r = l - m * R;
+  const int32_t u = p.unit_begin + x + 8 * m;
+  JobId j;
+  j.valid = u < p.unit_end;
+  j.qi = u / p.hkv;
+  j.g = u - j.qi * p.hkv;
+  j.split = r / p.head_groups;
+  j.hb = r - j.split * p.head_groups;
+  return j;
+}
+
+template <int D, int NH, bool FP8>
 struct Cfg {
-  static constexpr int NC = NH * NQ;                  // compute waves
-  static constexpr int kThreads = NC * 64;            // compute threads
-  static constexpr int kBlock = (NC + 1) * 64;        // + one producer wave
-  static constexpr int kRowB = 2 * D;                 // bf16 row bytes
-  static constexpr int kChunks = kRowB / 16;          // 16-byte chunks per row
-  static constexpr int kTileB = kTile * kRowB;        // one K (or V) tile, bytes
-  static constexpr int kKVInstr = 2 * kTileB / 1024;  // wave-wide 1 KiB loads per tile
-  static constexpr int kOps = kKVInstr;               // producer loads per tile
-  static constexpr int kF8TileB = kTile * D;          // one e4m3 K (or V) tile
-  static constexpr int kF8Instr = 2 * kF8TileB / 1024;
-  static constexpr int kSlots = kChunkTiles * kTile;
-  static constexpr int kPer = kSlots / kThreads;      // translation slots per thread
-  static_assert(NC <= 4, "compute waves (5 waves per workgroup keep 256 VGPRs per lane)");
-  static_assert(!FP8 || kF8Instr + 1 <= kOps, "fp8 tiles: data + scale loads fit the per-tile count");
-  static_assert((NBUF - 2) * kOps < 64, "vmcnt range");
-  static_assert(kSlots % kThreads == 0, "slots");
+  static constexpr int NC = NH;                        // compute waves
+  static constexpr int kThreads = NC * 64;             // compute threads
+  static constexpr int kBlock = kThreads + 128;        // + the load wave and the translation wave
+  static constexpr int kRowB = 2 * D;                  // bf16 row bytes
+  static constexpr int kChunks = kRowB / 16;           // 16-byte chunks per row
+  static constexpr int kTileB = kTile * kRowB;         // one K (or V) tile, bytes
+  static constexpr int kHalfOps = kTileB / 1024;       // wave-wide 1 KiB loads per K (or V) tile
+  static constexpr int kF8RowB = D;                    // e4m3 row bytes
+  static constexpr int kF8TileB = kTile * D;           // one e4m3 K (or V) tile
+  static constexpr int kF8HalfOps = kF8TileB / 1024;
+  static constexpr int kLoadOps = 2 * kHalfOps;        // load wave: loads per stream step (K + V)
+  static constexpr int kMaxJobs = 64;                  // jobs per workgroup per launch
+  static_assert(!FP8 || 2 * kF8HalfOps + 1 <= kLoadOps, "fp8 tile: data + scale loads fit the per-tile count");
+  static_assert(2 * kLoadOps < 64, "vmcnt range");
 };
 
-template <int D, int NH, int NQ, bool FP8, int NBUF>
+template <int D, int NH, bool FP8>
 struct Smem {
-  using C = Cfg<D, NH, NQ, FP8, NBUF>;
-  static constexpr int kU = NQ > 1 ? kUnionCap : 4;
-  alignas(16) uint8_t kv[NBUF][2][C::kTileB];
-  alignas(16) uint8_t stage[FP8 ? NBUF : 1][2][FP8 ? C::kF8TileB : 16];
-  alignas(16) float scl[FP8 ? NBUF : 1][64];          // k scales [0,32), v scales [32,64)
-  alignas(16) uint8_t dummy[FP8 ? 1024 : 16];
-  alignas(16) int64_t erow[C::kSlots];                 // element row (row*Hkv+g), -1 = masked
-  uint32_t tmask[kChunkTiles][NQ];                     // bit r: row r of the tile is seen by token q
-  // group union (NQ > 1): per-id token bits, then the compacted list
-  alignas(16) uint32_t ubits[kU / 4];                  // byte c: tokens whose list holds id c
-  alignas(16) int32_t uid[kU];                         // union ids, ascending
-  uint8_t umask[kU];                                   // token bits of uid[k]
-  int32_t scan[C::kThreads];
-  QueryKV qkv[NQ];                                     // the group's queries
-  int32_t gshared, gnq, gwlo, gnwr, gncmax, gnu;
+  using C = Cfg<D, NH, FP8>;
+  alignas(16) uint8_t kr[kRing][C::kTileB];                       // K tiles (a Q tile: heads 0-31)
+  alignas(16) uint8_t vr[kRing][C::kTileB];                       // V tiles (a Q tile: heads 32-63)
+  alignas(16) uint8_t stk[FP8 ? kRing : 1][FP8 ? C::kF8TileB : 16];   // e4m3 K staging
+  alignas(16) uint8_t stv[FP8 ? kRing : 1][FP8 ? C::kF8TileB : 16];   // e4m3 V staging
+  alignas(16) float scl[FP8 ? kRing : 1][64];                     // k scales [0,32), v scales [32,64)
+  alignas(16) int32_t lst[kXRing][64];                            // list entries (lanes 0-31)
+  alignas(16) int32_t pg[kXRing][64];                             // page-table entries (lanes 0-31)
+  alignas(16) int32_t xid[kXRing][32];                            // logical id per row, -1 = masked
+  // source address of each row of the tile being issued (K rows, V rows;
+  // masked rows point into the zero row) and of its fp8 scales (lanes 0-31
+  // k, 32-63 v)
+  alignas(16) uint64_t kptr[1][32];
+  alignas(16) uint64_t vptr[1][32];
+  alignas(16) uint64_t sptr[1][64];
+  alignas(16) uint8_t dummy[1024];                                // destination of padding loads
+  alignas(16) uint4 desc[kRing];                                  // tile descriptors
+  int32_t ntiles;
 };
 
-// The KV stream of one pass: compressed rows [0, ncr) then window rows
-// [0, nwr); compressed tiles first, window tiles start on a tile boundary.
-struct Stream {
-  int ncr, nwr, nct, total;
-  __device__ __forceinline__ void tile(int j, int &k0, int &len, bool &cmp) const {
-    if (j < nct) {
-      k0 = j * kTile;
-      len = min(kTile, ncr - k0);
-      cmp = true;
-    } else {
-      k0 = (j - nct) * kTile;
-      len = min(kTile, nwr - k0);
-      cmp = false;
-    }
-  }
-};
+template <int D, int NH, bool FP8>
+__global__ __launch_bounds__((NH + 2) * 64) __attribute__((amdgpu_waves_per_eu(2)))  // <= 256 VGPRs
+void attn_fwd_kernel(const Params p) {
+  using C = Cfg<D, NH, FP8>;
+  __shared__ Smem<D, NH, FP8> sm;
 
-template <int D, int NH, int NQ, bool FP8, int NBUF>
-__global__ __launch_bounds__((NH * NQ + 1) * 64) void attn_fwd_kernel(const Params p) {
-  using C = Cfg<D, NH, NQ, FP8, NBUF>;
-  __shared__ Smem<D, NH, NQ, FP8, NBUF> sm;
-
-  // ---- job of this workgroup (XCD-contiguous numbering)
-  const int job = (int)(blockIdx.x & 7) * p.jobs_per_xcd + (int)(blockIdx.x >> 3);
-  if (job >= p.total_jobs) return;
-  const int S = p.num_splits;
-  int t = job;
-  const int hgw = t % p.head_groups;
-  t /= p.head_groups;
-  const int split = t % S;
-  t /= S;
-  const int g = t % p.hkv;
-  const int grp = t / p.hkv;
+  const int32_t x = (int32_t)(blockIdx.x & 7);
+  const int32_t y = (int32_t)(blockIdx.x >> 3);
+  const int32_t Gx = (int32_t)(gridDim.x >> 3);
+  if (!job_id(p, x, y, Gx, 0).valid) return;   // no work for this workgroup
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int hi = lane >> 5;                  // which half of the wave
-  const bool producer = wave == C::NC;       // the last wave only moves data
-  const int qt = producer ? 0 : wave / NH;   // this wave's token within the group
-  const int hw = producer ? 0 : wave % NH;   // this wave's 32-head block within the workgroup's heads
-  const int qi = grp * NQ + qt;              // this wave's query
-  const bool q_ok = !producer && qi < p.num_queries;
-  const int hl = hgw * p.heads_per_block + hw * 32 + (lane & 31);   // head within the KV group
-  const bool head_ok = q_ok && hl < p.group;
-  const bool wave_ok = q_ok && hgw * p.heads_per_block + hw * 32 < p.group;
-  const int h = g * p.group + hl;
+  const int hi = lane >> 5;                    // which half of the wave
+  const int S = p.num_splits;
 
-  // ---- Q^T as the B operand: lane holds head (lane%32), d = 16kk + 8*hi ..+7
-  bf16x8 qf[D / 16];
-  {
-    const uint16_t *qrow = p.q + ((int64_t)(q_ok ? qi : 0) * p.hq + (head_ok ? h : 0)) * D;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      uint4 v = head_ok ? *(const uint4 *)(qrow + 16 * kk + 8 * hi) : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  // ---- decode (one query per group): the slice's list entries of the first
-  // chunk are loaded right away, together with Q and the query's counts.
-  // Slices are cut by capacity: list slots [cs, ce) of the compressed part
-  // (the top-k list, or the n_c groups of an all-groups layer) and window
-  // slots [ws, we).
-  int32_t xl[C::kPer];
-  const int lper = (NQ == 1 && p.topk > 0) ? round_up((p.topk + S - 1) / S, kTile) : 0;
-  const int ls = min(p.topk, split * lper);
-  const int le = NQ == 1 ? min(p.topk, ls + lper) : 0;
-#pragma unroll
-  for (int u = 0; u < C::kPer; ++u) {
-    const int e = ls + tid + u * C::kThreads;   // slot idx -> tile idx/32, row idx%32
-    xl[u] = (!producer && e < le) ? p.cmp_idx[(int64_t)grp * p.topk + e] : -1;
-  }
-
-  // ---- the group's queries, in LDS (computed once, read uniformly)
-  if (tid < NQ) {
-    const int i = grp * NQ + tid;
-    sm.qkv[tid] = i < p.num_queries ? query_kv(p, i) : QueryKV{0, 0, 0, 0, 0, 0};
-  }
-  block_sync();
-  if (tid == 0) {
-    int nqv = 0;
-    bool same = true;
-    int tmax = -1, wlo = 0x7FFFFFFF, ncm = 0;
-    for (int q = 0; q < NQ; ++q) {
-      if (grp * NQ + q >= p.num_queries) break;
-      const QueryKV k = sm.qkv[q];
-      ++nqv;
-      // a query whose metadata failed validation has an empty set
-      same = same && k.b == sm.qkv[0].b && k.win_len + k.n_sel > 0;
-      tmax = max(tmax, k.t);
-      wlo = min(wlo, k.win_lo);
-      ncm = max(ncm, k.n_c);
-    }
-    const int nwr = max(0, tmax - wlo + 1);
-    sm.gnq = nqv;
-    sm.gwlo = wlo;
-    sm.gnwr = nwr;
-    sm.gncmax = ncm;
-    sm.gshared = NQ > 1 && nqv > 1 && same && S == 1 && nwr <= 2 * p.window + 2 * NQ &&
-                 (p.topk == 0 || ncm <= kUnionCap);
-  }
-  block_sync();
-  const bool shared = sm.gshared != 0;
-  const int nq_valid = sm.gnq;
-
-  // ---- online softmax state (log2 domain); the sink is folded in up front
-  float m = -INFINITY, l = 0.f;
-  if (S == 1 && p.sink != nullptr && head_ok) {
-    m = p.sink[h] * kLog2e;
-    l = hi == 0 ? 1.f : 0.f;   // exp2(sink - m) = 1, counted once per head
-  }
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-
-  const int npass = shared ? 1 : (NQ == 1 ? 1 : nq_valid);
-  for (int pass = 0; pass < npass; ++pass) {
-    // ---- this pass's stream
-    const int pq = shared ? 0 : pass;          // the query of a single-query pass
-    const QueryKV pkv = sm.qkv[pq];
-    const int pqi = grp * NQ + pq;
-    Stream st;
-    int c_base = 0, w_base = 0;                // first list entry / first window position
-    int nu = 0;                                // union size (listed layers)
-    if (shared) {
-      if (p.topk > 0) {
-        // union of the lists: token bits per id, then compaction in id order
-        for (int w = producer ? kUnionCap : tid; w < kUnionCap / 4; w += C::kThreads) sm.ubits[w] = 0u;
-        block_sync();
-        if (!producer) {
-#pragma unroll
-          for (int q = 0; q < NQ; ++q) {
-            if (q < nq_valid) {
-              const int i = grp * NQ + q;
-              const QueryKV kq = sm.qkv[q];
-              for (int e = tid; e < kq.n_sel; e += C::kThreads) {
-                const int c = check_cmp_id(p, kq, p.cmp_idx[(int64_t)i * p.topk + e]);
-                if (c >= 0) atomicOr(&sm.ubits[c >> 2], 1u << (8 * (c & 3) + q));
-              }
-            }
-          }
-        }
-        block_sync();
-        // compaction: thread t owns ids [t*per, (t+1)*per)
-        const int ncmax = sm.gncmax;
-        const int per = (ncmax + C::kThreads - 1) / C::kThreads;
-        int cnt = 0;
-        if (!producer) {
-          for (int c = tid * per; c < min(ncmax, (tid + 1) * per); ++c)
-            cnt += ((sm.ubits[c >> 2] >> (8 * (c & 3))) & 0xFFu) != 0u;
-          sm.scan[tid] = cnt;
-        }
-        block_sync();
-        if (wave == 0) {   // exclusive scan of the per-thread counts
-          constexpr int kPerLane = (C::kThreads + 63) / 64;
-          int v[kPerLane];
-          int sum = 0;
-#pragma unroll
-          for (int k = 0; k < kPerLane; ++k) {
-            const int idx = lane * kPerLane + k;
-            v[k] = idx < C::kThreads ? sm.scan[idx] : 0;
-            sum += v[k];
-          }
-          int inc = sum;
-#pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            const int o = __shfl_up(inc, d);
-            if (lane >= d) inc += o;
-          }
-          int run = inc - sum;
-#pragma unroll
-          for (int k = 0; k < kPerLane; ++k) {
-            const int idx = lane * kPerLane + k;
-            if (idx < C::kThreads) sm.scan[idx] = run;
-            run += v[k];
-          }
-        }
-        block_sync();
-        if (!producer) {
-          int pos = sm.scan[tid];
-          for (int c = tid * per; c < min(ncmax, (tid + 1) * per); ++c) {
-            const uint32_t bits = (sm.ubits[c >> 2] >> (8 * (c & 3))) & 0xFFu;
-            if (bits) {
-              sm.uid[pos] = c;
-              sm.umask[pos] = (uint8_t)bits;
-              ++pos;
-            }
-          }
-        }
-        {
-          // total = last thread's offset + its count
-          block_sync();
-          nu = sm.scan[C::kThreads - 1];
-          int lastcnt = 0;
-          const int tl = C::kThreads - 1;
-          for (int c = tl * per; c < min(ncmax, (tl + 1) * per); ++c)
-            lastcnt += ((sm.ubits[c >> 2] >> (8 * (c & 3))) & 0xFFu) != 0u;
-          nu += lastcnt;
-        }
-        st.ncr = nu;
-      } else {
-        st.ncr = sm.gncmax;   // all-groups layer: ids [0, ncmax), token q sees ids < n_c(q)
+  // =================================================================
+  // Load wave (K, V and Q tiles) and translation wave (page-table and
+  // list entries)
+  // =================================================================
+  if (wave >= C::NC) {
+    const bool loader = wave == C::NC;
+    // ---- per-job metadata, one job per lane (ordinary loads: nothing is in
+    // flight yet); both waves compute the same records
+    const JobId jl = job_id(p, x, y, Gx, lane);
+    const bool jvalid = lane < C::kMaxJobs && jl.valid;
+    int32_t jnc = 0, jcs = 0, jncr = 0, jwb = 0, jnwr = 0, jnct = 0, jnkv = 1;
+    int64_t jrpt = 0, jcpt = 0, jlst = 0;   // row bases: page tables, list
+    const int64_t jq = ((int64_t)jl.qi * p.hq + jl.g * p.group + jl.hb * p.heads_per_block) * D;   // Q
+    const int32_t jnh = jvalid ? min(32 * NH, p.group - jl.hb * p.heads_per_block) : 0;   // real heads
+    const uint8_t *zero16 = kZeroRow + (lane & 15) * 16;
+    const void *zero4 = kZeroRow + lane * 4;
+    // Job 0's Q tile and (top-k layers) the list entries of its first
+    // compressed tiles need no metadata: they are issued before it is read,
+    // so that their loads overlap the metadata loads.  The list entries are
+    // taken up to the slice's capacity; the page stage uses only the valid
+    // ones.
+    constexpr int kSpec = 5;                 // tiles 1..kSpec of the stream at most
+    int32_t nspec = 0;
+    if (wave == C::NC + 1 && p.topk > 0) {
+      const JobId j0 = job_id(p, x, y, Gx, 0);
+      const int cper = round_up((p.topk + S - 1) / S, kTile);
+      const int cs0 = min(p.topk, j0.split * cper);
+      const int cap0 = min(p.topk, cs0 + cper) - cs0;
+      nspec = min(kSpec, (cap0 + kTile - 1) / kTile);
+      for (int u = 1; u <= nspec; ++u) {
+        const int32_t idx = (u - 1) * kTile + lane;
+        dma4(lane < kTile && idx < cap0 ? (const void *)(p.cmp_idx + (int64_t)j0.qi * p.topk + cs0 + idx) : zero4,
+             &sm.lst[u % kXRing][0]);
       }
-      st.nwr = sm.gnwr;
-      w_base = sm.gwlo;
-    } else {
-      // one query: its own set, or its slice of it (decode splits)
-      const int ccap = p.topk > 0 ? p.topk : pkv.n_sel;
+    }
+    // the 16-byte chunk each lane moves within its row in load n of a tile:
+    // row 4n + lane/16 (D 128) or 8n + lane/8 (D 64), logical chunk
+    // (lane % chunks) ^ swz(row), which depends on n mod (16 / rows per load)
+    // only
+    constexpr int kRowsPerOp = 1024 / C::kRowB;
+    constexpr int kPeriod = 16 / kRowsPerOp;   // 4 (D 128) or 2 (D 64)
+    int32_t cs16[kPeriod];
+#pragma unroll
+    for (int n = 0; n < kPeriod; ++n) {
+      const int r = n * kRowsPerOp + lane / C::kChunks;
+      cs16[n] = ((lane % C::kChunks) ^ swz<C::kChunks>(r)) * 16;
+    }
+
+    if (wave == C::NC) {
+      // job 0's Q tile: heads 0-31 into K slot 0, 32-63 into V slot 0
+      const int64_t q0 = (int64_t)(((uint64_t)__builtin_amdgcn_readlane((uint32_t)(jq >> 32), 0) << 32) |
+                                   __builtin_amdgcn_readlane((uint32_t)jq, 0));
+      const int32_t nh0 = __builtin_amdgcn_readlane(jnh, 0);
+      const uint8_t *qb = (const uint8_t *)(p.q + q0) + (lane / C::kChunks) * C::kRowB;
+#pragma unroll
+      for (int n = 0; n < C::kHalfOps; ++n) {
+        const int r = n * kRowsPerOp + lane / C::kChunks;
+        dma16(r < nh0 ? qb + n * 1024 + cs16[n % kPeriod] : zero16, &sm.kr[0][n * 1024]);
+      }
+#pragma unroll
+      for (int n = 0; n < C::kHalfOps; ++n) {
+        const int r = 32 + n * kRowsPerOp + lane / C::kChunks;
+        dma16(r < nh0 ? qb + 32 * C::kRowB + n * 1024 + cs16[n % kPeriod] : zero16, &sm.vr[0][n * 1024]);
+      }
+      if (lane == 0) sm.desc[0] = make_uint4(0u, kTileQ, 0u, 0u);
+    }
+    if (jvalid) {
+      const QueryKV kv = query_kv(p, jl.qi);
+      // slices cut by capacity: list slots [cs, ce) of the compressed part
+      // (the top-k list, or the n_c groups of an all-groups layer) and
+      // window slots [ws, we)
+      const int ccap = p.topk > 0 ? p.topk : kv.n_sel;
       const int cper = round_up((ccap + S - 1) / S, kTile);
-      const int cs = min(ccap, split * cper);
+      const int cs = min(ccap, jl.split * cper);
       const int ce = min(ccap, cs + cper);
       const int wper = round_up((p.window + S - 1) / S, kTile);
-      const int ws = min(pkv.win_len, split * wper);
-      const int we = min(pkv.win_len, ws + wper);
-      c_base = cs;
-      st.ncr = max(0, min(ce, pkv.n_sel) - cs);
-      st.nwr = we - ws;
-      w_base = pkv.win_lo + ws;
+      const int ws = min(kv.win_len, jl.split * wper);
+      const int we = min(kv.win_len, ws + wper);
+      jnc = kv.n_c;
+      jcs = cs;
+      jncr = max(0, min(ce, kv.n_sel) - cs);
+      jwb = kv.win_lo + ws;
+      jnwr = we - ws;
+      jnct = (jncr + kTile - 1) / kTile;
+      jnkv = max(1, jnct + (jnwr + kTile - 1) / kTile);   // an empty set still gets one (masked) tile
+      jrpt = (int64_t)kv.b * p.raw_pt_stride;
+      jcpt = (int64_t)kv.b * p.cmp_pt_stride;
+      jlst = (int64_t)jl.qi * p.topk + cs;
     }
-    st.nct = (st.ncr + kTile - 1) / kTile;
-    st.total = st.nct + (st.nwr + kTile - 1) / kTile;
-    const bool use_xl = NQ == 1 && p.topk > 0;
+    const int32_t jg = jl.g;
+    const int32_t njobs = __popcll(__ballot(jvalid));
+    // total stream length (a Q tile + the KV tiles per job)
+    int32_t T = jvalid ? 1 + jnkv : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) T += __shfl_xor(T, d);
+    if (loader && lane == 0) sm.ntiles = T;
 
-    for (int cbase = 0; cbase < st.total; cbase += kChunkTiles) {
-      const int ct = min(kChunkTiles, st.total - cbase);
-      block_sync();   // the previous chunk (or pass) is done with the row table
-      // -- translation (compute waves): all list loads of the batch, then all
-      // page-table loads
-      if (!producer) {
-        int32_t x[C::kPer];
-        bool cmpk[C::kPer];
-        uint32_t tok[C::kPer];   // token bits of the row
-#pragma unroll
-        for (int u = 0; u < C::kPer; ++u) {
-          const int idx = tid + u * C::kThreads;
-          const int j = cbase + idx / kTile;
-          const int r = idx % kTile;
-          x[u] = -1;
-          cmpk[u] = false;
-          tok[u] = 0u;
-          if (idx < ct * kTile) {
-            int k0, len;
-            bool cmp;
-            st.tile(j, k0, len, cmp);
-            cmpk[u] = cmp;
-            const int k = k0 + r;
-            if (r < len) {
-              if (cmp) {
-                if (shared) {
-                  if (p.topk > 0) {
-                    x[u] = sm.uid[k];
-                    tok[u] = sm.umask[k];
-                  } else {
-                    x[u] = k;
-#pragma unroll
-                    for (int q = 0; q < NQ; ++q)
-                      if (q < nq_valid && k < sm.qkv[q].n_c) tok[u] |= 1u << q;
-                  }
-                } else {
-                  // chunk 0 of a decode list: the list entry was loaded up front
-                  x[u] = (use_xl && cbase == 0) ? check_cmp_id(p, pkv, xl[u])
-                                                : entry_logical(p, pkv, pqi, c_base + k);
-                  tok[u] = 1u << pq;
-                }
+    int32_t errbits = 0;   // reported once at the end (an atomic now would add to the load count)
+
+    // wave-uniform copy of job k's record, refreshed when a cursor moves on
+    auto rd = [&](int32_t v, int32_t k) { return __builtin_amdgcn_readlane(v, k); };
+    auto rd64 = [&](int64_t v, int32_t k) {
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, k);
+      const uint32_t hi32 = __builtin_amdgcn_readlane((uint32_t)(v >> 32), k);
+      return (int64_t)(((uint64_t)hi32 << 32) | lo);
+    };
+    struct Job {
+      int32_t nkv, nct, ncr, cs, wb, nwr, nc, nh, g;
+      int64_t rpt, cpt, lst, q;
+    };
+    auto job = [&](int32_t k) {
+      Job j{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      if (k < njobs) {
+        j.nkv = rd(jnkv, k);
+        j.nct = rd(jnct, k);
+        j.ncr = rd(jncr, k);
+        j.cs = rd(jcs, k);
+        j.wb = rd(jwb, k);
+        j.nwr = rd(jnwr, k);
+        j.nc = rd(jnc, k);
+        j.nh = rd(jnh, k);
+        j.g = rd(jg, k);
+        j.rpt = rd64(jrpt, k);
+        j.cpt = rd64(jcpt, k);
+        j.lst = rd64(jlst, k);
+        j.q = rd64(jq, k);
+      }
+      return j;
+    };
+    // stream cursor: job k, position v (0 = Q tile, 1..nkv = KV tiles),
+    // stream index u
+    struct Cur {
+      int32_t k, v, u;
+      Job j;
+    };
+    auto advance = [&](Cur &c) {
+      ++c.u;
+      if (c.k < njobs && ++c.v > c.j.nkv) {
+        ++c.k;
+        c.v = 0;
+        c.j = job(c.k);
+      }
+    };
+    const bool pow2 = p.page_shift >= 0;
+    const int32_t P = p.page_size;
+    // ---------------- translation wave stages
+    // -- list stage: list entries of a compressed KV tile of a top-k layer
+    auto stage_list = [&](const Cur &c) {
+      const void *src = zero4;
+      void *dst = sm.dummy;
+      if (c.k < njobs && c.v > 0 && p.topk > 0 && c.v - 1 < c.j.nct) {
+        const int32_t idx = (c.v - 1) * kTile + lane;
+        if (lane < kTile && idx < c.j.ncr) src = p.cmp_idx + c.j.lst + idx;
+        dst = &sm.lst[c.u % kXRing][0];
+      }
+      dma4(src, dst);
+    };
+    // -- page stage: logical id of every row of a KV tile, then its
+    // page-table entry
+    auto stage_page = [&](const Cur &c) {
+      const void *src = zero4;
+      void *dst = sm.dummy;
+      if (c.k < njobs && c.v > 0) {
+        const int32_t e0 = c.v - 1;
+        const bool cmp = e0 < c.j.nct;
+        if (lane < kTile) {
+          int32_t xv = -1;
+          if (cmp) {
+            const int32_t idx = e0 * kTile + lane;
+            if (idx < c.j.ncr) {
+              if (p.topk > 0) {
+                const int32_t c_id = sm.lst[c.u % kXRing][lane];
+                if (c_id >= 0 && c_id < c.j.nc) xv = c_id;
+                else errbits |= kErrCmpId;
               } else {
-                const int pos = w_base + k;
-                x[u] = pos;
-                if (shared) {
-#pragma unroll
-                  for (int q = 0; q < NQ; ++q)
-                    if (q < nq_valid && pos >= sm.qkv[q].win_lo && pos <= sm.qkv[q].t) tok[u] |= 1u << q;
-                } else {
-                  tok[u] = 1u << pq;
-                }
+                xv = c.j.cs + idx;   // all-groups layer: ids in order
               }
             }
+          } else {
+            const int32_t idx = (e0 - c.j.nct) * kTile + lane;
+            if (idx < c.j.nwr) xv = c.j.wb + idx;
           }
-        }
-#pragma unroll
-        for (int u = 0; u < C::kPer; ++u) {
-          const int idx = tid + u * C::kThreads;
-          const int64_t row = logical_row(p, pkv, cmpk[u], x[u]);
-          sm.erow[idx] = row >= 0 ? row * p.hkv + g : -1;
-          // a tile's 32 slots are 32 consecutive lanes of one wave
-#pragma unroll
-          for (int q = 0; q < NQ; ++q) {
-            const uint64_t seen = __ballot(row >= 0 && ((tok[u] >> q) & 1u));
-            if ((lane & 31) == 0 && idx / kTile < kChunkTiles) sm.tmask[idx / kTile][q] = (uint32_t)(seen >> (lane & 32));
+          if (xv >= 0) {
+            const int32_t col = pow2 ? (xv >> p.page_shift) : xv / P;
+            if (col < (cmp ? p.cmp_pt_stride : p.raw_pt_stride)) {
+              src = cmp ? (const void *)(p.cmp_pt + c.j.cpt + col) : (const void *)(p.raw_pt + c.j.rpt + col);
+            } else {
+              errbits |= kErrPage;
+              xv = -1;
+            }
           }
+          sm.xid[c.u % kXRing][lane] = xv;
         }
+        dst = &sm.pg[c.u % kXRing][0];
       }
-      // Q loads and the translation loads complete here, before the ring starts:
-      // a wait placed lazily later would also wait for the tile loads in flight.
-      wait_vmcnt<0>();
-      block_sync();
+      dma4(src, dst);
+    };
 
-      // -- producer: issue the loads of chunk tile jj into ring buffer jj % NBUF
-      auto issue = [&](int jj) {
-        int k0, len;
-        bool cmp;
-        st.tile(cbase + jj, k0, len, cmp);
-        const int buf = jj % NBUF;
-        const int64_t *er = &sm.erow[jj * kTile];
-        if (!FP8 || !cmp) {
+    // ---------------- load wave stage
+    // -- the tile's loads: K and V (or the two head halves of a Q tile) and
+    // its descriptor
+    auto stage_kv = [&](const Cur &c) {
+      const int slot = c.u % kRing;
+      uint4 d = make_uint4(0u, 0u, 0u, 0u);
+      if (c.k >= njobs) {
+#pragma unroll
+        for (int n = 0; n < 2 * C::kHalfOps; ++n) dma16(zero16, sm.dummy);
+      } else if (c.v == 0) {
+        // Q rows of the block's heads, swizzled like a K tile: heads 0-31 in
+        // the K slot, 32-63 in the V slot; heads past the KV group read zeros
+        const uint8_t *qb = (const uint8_t *)(p.q + c.j.q) + (lane / C::kChunks) * C::kRowB;
+#pragma unroll
+        for (int n = 0; n < C::kHalfOps; ++n) {
+          const int r = n * kRowsPerOp + lane / C::kChunks;
+          dma16(r < c.j.nh ? qb + n * 1024 + cs16[n % kPeriod] : zero16, &sm.kr[slot][n * 1024]);
+        }
+#pragma unroll
+        for (int n = 0; n < C::kHalfOps; ++n) {
+          const int r = 32 + n * kRowsPerOp + lane / C::kChunks;
+          dma16(r < c.j.nh ? qb + 32 * C::kRowB + n * 1024 + cs16[n % kPeriod] : zero16, &sm.vr[slot][n * 1024]);
+        }
+        d = make_uint4(0u, kTileQ, (uint32_t)c.k, 0u);
+      } else {
+        const int xs = c.u % kXRing;
+        const bool cmp = c.v - 1 < c.j.nct;
+        const bool f8 = FP8 && cmp;
+        // row addresses (lanes 0-31 = rows), page ids checked
+        bool ok = false;
+        if (lane < kTile) {
+          const int32_t xv = sm.xid[xs][lane];
+          int64_t er = -1;
+          if (xv >= 0) {
+            const int32_t page = sm.pg[xs][lane];
+            if (page >= 0 && (int64_t)page < (cmp ? p.cmp_pages : p.raw_pages)) {
+              const int32_t off = pow2 ? (xv & (P - 1)) : xv - (xv / P) * P;
+              er = ((int64_t)page * P + off) * p.hkv + c.j.g;
+            } else {
+              errbits |= kErrPage;
+            }
+          }
+          ok = er >= 0;
+          const int64_t rb = f8 ? C::kF8RowB : C::kRowB;
           const uint8_t *kb = cmp ? p.k_cmp : p.k_raw;
           const uint8_t *vb = cmp ? p.v_cmp : p.v_raw;
-          int64_t off[C::kKVInstr / 2];
+          sm.kptr[0][lane] = (uint64_t)(ok ? kb + er * rb : kZeroRow);
+          sm.vptr[0][lane] = (uint64_t)(ok ? vb + er * rb : kZeroRow);
+          if (FP8 && f8) {
+            sm.sptr[0][lane] = (uint64_t)(ok ? (const void *)(p.k_cmp_scale + er) : zero4);
+            sm.sptr[0][32 + lane] = (uint64_t)(ok ? (const void *)(p.v_cmp_scale + er) : zero4);
+          }
+        }
+        const uint32_t mask = (uint32_t)__ballot(ok);
+        // all row lookups before the first load: a load's asm orders every
+        // later LDS access behind it
+        if (!f8) {
+          const uint8_t *ks[C::kHalfOps], *vs[C::kHalfOps];
 #pragma unroll
-          for (int n = 0; n < C::kKVInstr / 2; ++n) {   // row lookups first; K and V share rows
-            const int lin = n * 1024 + lane * 16;
-            const int r = lin / C::kRowB;
-            const int c = ((lin % C::kRowB) / 16) ^ (r & (C::kChunks - 1));
-            const int64_t e = er[r];
-            off[n] = e >= 0 ? e * C::kRowB + c * 16 : -1;
+          for (int n = 0; n < C::kHalfOps; ++n) {
+            const int r = n * kRowsPerOp + lane / C::kChunks;
+            ks[n] = (const uint8_t *)sm.kptr[0][r] + cs16[n % kPeriod];
+            vs[n] = (const uint8_t *)sm.vptr[0][r] + cs16[n % kPeriod];
           }
 #pragma unroll
-          for (int n = 0; n < C::kKVInstr / 2; ++n)
-            dma16(off[n] >= 0 ? kb + off[n] : kZeroRow + (lane & 15) * 16, &sm.kv[buf][0][n * 1024]);
+          for (int n = 0; n < C::kHalfOps; ++n) dma16(ks[n], &sm.kr[slot][n * 1024]);
 #pragma unroll
-          for (int n = 0; n < C::kKVInstr / 2; ++n)
-            dma16(off[n] >= 0 ? vb + off[n] : kZeroRow + (lane & 15) * 16, &sm.kv[buf][1][n * 1024]);
+          for (int n = 0; n < C::kHalfOps; ++n) dma16(vs[n], &sm.vr[slot][n * 1024]);
         } else {
-          int64_t off[C::kF8Instr / 2];
+          const uint8_t *ks[C::kF8HalfOps], *vs[C::kF8HalfOps];
 #pragma unroll
-          for (int n = 0; n < C::kF8Instr / 2; ++n) {
+          for (int n = 0; n < C::kF8HalfOps; ++n) {
             const int lin = n * 1024 + lane * 16;
-            const int r = lin / D;
-            const int c = (lin % D) / 16;
-            const int64_t e = er[r];
-            off[n] = e >= 0 ? e * D + c * 16 : -1;
+            ks[n] = (const uint8_t *)sm.kptr[0][lin / C::kF8RowB] + (lin % C::kF8RowB);
+            vs[n] = (const uint8_t *)sm.vptr[0][lin / C::kF8RowB] + (lin % C::kF8RowB);
           }
-          const int64_t es = er[lane & 31];
+          const void *ssrc = (const void *)sm.sptr[0][lane];
 #pragma unroll
-          for (int n = 0; n < C::kF8Instr / 2; ++n)
-            dma16(off[n] >= 0 ? p.k_cmp + off[n] : kZeroRow + (lane & 15) * 16, &sm.stage[FP8 ? buf : 0][0][n * 1024]);
+          for (int n = 0; n < C::kF8HalfOps; ++n) dma16(ks[n], &sm.stk[FP8 ? slot : 0][n * 1024]);
 #pragma unroll
-          for (int n = 0; n < C::kF8Instr / 2; ++n)
-            dma16(off[n] >= 0 ? p.v_cmp + off[n] : kZeroRow + (lane & 15) * 16, &sm.stage[FP8 ? buf : 0][1][n * 1024]);
-          // the per-token scales: lanes 0-31 k, lanes 32-63 v
-          const float *sc = hi ? p.v_cmp_scale : p.k_cmp_scale;
-          dma4(es >= 0 ? (const void *)(sc + es) : (const void *)kZeroRow, &sm.scl[FP8 ? buf : 0][0]);
+          for (int n = 0; n < C::kF8HalfOps; ++n) dma16(vs[n], &sm.stv[FP8 ? slot : 0][n * 1024]);
+          dma4(ssrc, &sm.scl[FP8 ? slot : 0][0]);
 #pragma unroll
-          for (int n = C::kF8Instr + 1; n < C::kKVInstr; ++n)
-            dma4(kZeroRow + lane * 4, &sm.dummy[0]);   // keeps the per-tile count uniform
+          for (int n = 2 * C::kF8HalfOps + 1; n < 2 * C::kHalfOps; ++n) dma16(zero16, sm.dummy);
         }
-      };
-
-      if (producer) {
-        const int pre = min(NBUF - 1, ct);
-        for (int jj = 0; jj < pre; ++jj) issue(jj);
+        uint32_t f = kTileKV;
+        if (cmp) f |= kTileCmp;
+        if (f8) f |= kTileWiden;
+        if (c.v == c.j.nkv) f |= kTileLast;
+        d = make_uint4(mask, f, (uint32_t)c.k, 0u);
       }
+      if (lane == 0) sm.desc[slot] = d;
+    };
 
-      for (int jj = 0; jj < ct; ++jj) {
-        // the producer waits for tile jj; the barrier then hands it to the compute
-        // waves and tells the producer that tile jj-1's buffer is free
-        if (producer) wait_tiles<C::kOps, NBUF - 2>(min(NBUF - 2, ct - 1 - jj));
-        block_sync();
-        if (producer && jj + NBUF - 1 < ct) issue(jj + NBUF - 1);
-
-        int k0, len;
-        bool cmp;
-        st.tile(cbase + jj, k0, len, cmp);
-        const int buf = jj % NBUF;
-
-        if (FP8 && cmp) {
-          // widen the staged e4m3 rows to bf16 (exact) into the swizzled tile
-          constexpr int kPieces = kTile * D / 8;   // 8-byte pieces per tile
-          for (int idx = producer ? 2 * kPieces : tid; idx < 2 * kPieces; idx += C::kThreads) {
-            const int which = idx / kPieces;
-            const int pidx = idx - which * kPieces;
-            const int r = pidx / (D / 8);
-            const int piece = pidx - r * (D / 8);
-            const uint2 w = *(const uint2 *)&sm.stage[FP8 ? buf : 0][which][r * D + piece * 8];
-            const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-            const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-            const f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-            const f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-            uint4 o;
-            o.x = pack_bf16_hi(a0[0], a0[1]);
-            o.y = pack_bf16_hi(a1[0], a1[1]);
-            o.z = pack_bf16_hi(a2[0], a2[1]);
-            o.w = pack_bf16_hi(a3[0], a3[1]);
-            *(uint4 *)&sm.kv[buf][which][r * C::kRowB + ((piece ^ (r & (C::kChunks - 1))) * 16)] = o;
-          }
-          block_sync();
-        }
-
-        const uint32_t tm = sm.tmask[jj][qt];
-        if (wave_ok && tm != 0u) {
-          const uint8_t *Kt = sm.kv[buf][0];
-          const uint8_t *Vt = sm.kv[buf][1];
-          // S^T = K . Q^T
-          f32x16 s = f32x16{};
-          {
-            const int r = lane & 31;
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-              const int c = 2 * kk + hi;
-              const bf16x8 a = *(const bf16x8 *)(Kt + r * C::kRowB + ((c ^ (r & (C::kChunks - 1))) * 16));
-              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
-            }
-          }
-          // online softmax.  Lane rows: 8*(i/4) + 4*hi + i%4.  The max is taken
-          // on the raw scores (the scale c = scale*log2 e is positive), and
-          // p = exp2(s*c - m) is one FMA and one exp per score.
-          float sc[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[i] = s[i];
-          if (FP8 && cmp) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const float4 kk4 = *(const float4 *)(&sm.scl[FP8 ? buf : 0][8 * q4 + 4 * hi]);
-              sc[4 * q4 + 0] *= kk4.x;
-              sc[4 * q4 + 1] *= kk4.y;
-              sc[4 * q4 + 2] *= kk4.z;
-              sc[4 * q4 + 3] *= kk4.w;
-            }
-          }
-          if (tm != 0xFFFFFFFFu) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int r = 8 * (i >> 2) + 4 * hi + (i & 3);
-              sc[i] = ((tm >> r) & 1u) ? sc[i] : -INFINITY;
-            }
-          }
-          float smax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-          smax = fmaxf(smax, fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])),
-                                   fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]))));
-          smax = fmaxf(smax, __shfl_xor(smax, 32));
-          const float tmax = smax * p.scale_log2;               // -inf stays -inf
-          const bool need = tmax > m + kTau;                     // same on both lanes of a head
-          if (__any(need)) {
-            const float alpha = need ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;   // m = -inf -> 0
-            m = need ? tmax : m;
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-          }
-          const float negm = m == -INFINITY ? 0.f : -m;          // all scores are -inf then
-          float pr[16];
-          float psum = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.scale_log2, negm));
-            psum += pr[i];
-          }
-          l += psum;
-          if (FP8 && cmp) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const float4 vv = *(const float4 *)(&sm.scl[FP8 ? buf : 0][32 + 8 * q4 + 4 * hi]);
-              pr[4 * q4 + 0] *= vv.x;
-              pr[4 * q4 + 1] *= vv.y;
-              pr[4 * q4 + 2] *= vv.z;
-              pr[4 * q4 + 3] *= vv.w;
-            }
-          }
-          bf16x8 pb[2];
-#pragma unroll
-          for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) pb[k2][j] = (__bf16)pr[8 * k2 + j];
-
-          // O^T += V^T . P^T ; V^T from the transpose read of the row-major tile
-          const int G = lane >> 4;
-          const int L = lane & 15;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-              i16x4 part[2];
-#pragma unroll
-              for (int rr = 0; rr < 2; ++rr) {
-                const int row = 16 * k2 + 8 * rr + 4 * (G >> 1) + (L >> 2);
-                const int d = 32 * db + 16 * (G & 1) + 4 * (L & 3);
-                const int off = row * C::kRowB + (((d >> 3) ^ (row & (C::kChunks - 1))) * 16) + (L & 1) * 8;
-                part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(Vt + off));
-              }
-              const i16x8 cat = {part[0][0], part[0][1], part[0][2], part[0][3],
-                                 part[1][0], part[1][1], part[1][2], part[1][3]};
-              acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[k2],
-                                                                acc[db], 0, 0, 0);
-            }
-          }
-        }
+    // ---- the stream.  Step t (after barrier t): the load wave issues tile
+    // t+3 (K and V), the translation wave the page entries of tile t+6 and
+    // the list entries of tile t+9.  Each wave issues a fixed number of loads
+    // per step and, before barrier t+1, waits for its own loads of steps
+    // <= t-2: tile t+1 for the compute waves, and every stage's input three
+    // steps after it was issued.
+    //
+    // Priming, before barrier 0: the translation wave issues the lists of
+    // tiles 0-5 (those not loaded early), then their page entries and the
+    // lists of tiles 6-8 (each phase complete before the next); after a
+    // barrier the load wave issues tiles 1 and 2 (tile 0, job 0's Q tile,
+    // was issued at the start).
+    Cur c0{0, loader ? 1 : 0, loader ? 1 : 0, job(0)}, c1{0, 0, 0, job(0)};   // load: tiles; translation: page, list
+    if (!loader) {
+      wait_vmcnt<0>();   // the early list loads land before any stage reuses their slots
+      for (int n = 0; n < 6; ++n) {
+        // the early loads hold the lists of job 0's first compressed tiles
+        const bool early = c1.k == 0 && c1.v >= 1 && c1.v <= nspec && c1.v - 1 < c1.j.nct;
+        if (!early) stage_list(c1);
+        advance(c1);
+      }
+      wait_vmcnt<0>();
+      for (int n = 0; n < 6; ++n) {
+        stage_page(c0);
+        advance(c0);
+      }
+      for (int n = 0; n < 3; ++n) {
+        stage_list(c1);
+        advance(c1);
+      }
+      wait_vmcnt<0>();
+    }
+    block_sync();   // page entries of tiles 0-5 are in
+    if (loader) {
+      for (int n = 0; n < 2; ++n) {
+        stage_kv(c0);
+        advance(c0);
+      }
+      wait_vmcnt<2 * C::kLoadOps>();   // tile 0
+    }
+    for (int t = 0; t < T; ++t) {
+      block_sync();   // barrier t
+      if (sm.desc[t % kRing].y & kTileWiden) block_sync();   // the compute waves widen tile t
+      if (loader) {
+        stage_kv(c0);
+        advance(c0);
+        wait_vmcnt<2 * C::kLoadOps>();
+      } else {
+        stage_page(c0);
+        advance(c0);
+        stage_list(c1);
+        advance(c1);
+        wait_vmcnt<2 * 2>();
       }
     }
-  }
-  if (producer) return;
-
-  // ---- epilogue
-  const float lt = l + __shfl_xor(l, 32);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const float lse2 = (m == -INFINITY || !(lt > 0.f)) ? -INFINITY : m + __builtin_amdgcn_logf(lt);
-  const float lse = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
-  if (!head_ok) return;
-  if (S == 1) {
-    uint16_t *orow = p.o + ((int64_t)qi * p.hq + h) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = 32 * db + 8 * i4 + 4 * hi;
-        uint2 w;
-        w.x = bf16_bits(acc[db][4 * i4 + 0] * inv) | (bf16_bits(acc[db][4 * i4 + 1] * inv) << 16);
-        w.y = bf16_bits(acc[db][4 * i4 + 2] * inv) | (bf16_bits(acc[db][4 * i4 + 3] * inv) << 16);
-        *(uint2 *)(orow + d0) = w;
-      }
-    }
-    if (hi == 0 && p.lse) p.lse[(int64_t)qi * p.hq + h] = lse;
+    wait_vmcnt<0>();
+    const int32_t eb = (__any(errbits & kErrCmpId) ? kErrCmpId : 0) | (__any(errbits & kErrPage) ? kErrPage : 0);
+    if (lane == 0 && eb != 0 && p.err_flag != nullptr) atomicOr(p.err_flag, eb);
     return;
   }
 
-  // split: write the sink-free partial; the merge kernel adds the sink
-  const int64_t prow = ((int64_t)split * p.num_queries + qi) * p.hq + h;
-  float *orow = p.part_o + prow * D;
+  // =================================================================
+  // Compute waves
+  // =================================================================
+  const int hw = wave;                        // this wave's 32-head block within the job's heads
+  block_sync();                               // priming: the page entries of tiles 0-5 are in
+  const int32_t T = sm.ntiles;
+  block_sync();                               // barrier 0: tile 0 is in
+
+  // per-job state
+  bf16x8 qf[D / 16];                          // Q^T as the B operand: head lane%32, d = 16kk + 8hi ..+7
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[D / 32];
+  // sink logit of this lane's head in job k (-inf: none), loaded one job
+  // ahead so that its load is long complete when the job starts
+  auto load_sink = [&](int32_t k) {
+    const JobId j = job_id(p, x, y, Gx, k);
+    const int hl = j.hb * p.heads_per_block + hw * 32 + (lane & 31);
+    return (j.valid && S == 1 && p.sink != nullptr && hl < p.group) ? p.sink[j.g * p.group + hl] : -INFINITY;
+  };
+  float sink_next = load_sink(0);
+  auto init_job = [&](int32_t k) {
+    m = sink_next == -INFINITY ? -INFINITY : sink_next * kLog2e;
+    l = (sink_next != -INFINITY && hi == 0) ? 1.f : 0.f;   // exp2(sink - m) = 1, counted once per head
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    sink_next = load_sink(k + 1);
+  };
+  auto epilogue = [&](int32_t k) {
+    const JobId j = job_id(p, x, y, Gx, k);
+    const int hl = j.hb * p.heads_per_block + hw * 32 + (lane & 31);
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse2 = (m == -INFINITY || !(lt > 0.f)) ? -INFINITY : m + __builtin_amdgcn_logf(lt);
+    const float lse = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
+    if (hl >= p.group) return;
+    const int h = j.g * p.group + hl;
+    if (S == 1) {
+      uint16_t *orow = p.o + ((int64_t)j.qi * p.hq + h) * D;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = 32 * db + 8 * i4 + 4 * hi;
-      *(float4 *)(orow + d0) = make_float4(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv,
-                                           acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv);
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = 32 * db + 8 * i4 + 4 * hi;
+          uint2 w;
+          w.x = bf16_bits(acc[db][4 * i4 + 0] * inv) | (bf16_bits(acc[db][4 * i4 + 1] * inv) << 16);
+          w.y = bf16_bits(acc[db][4 * i4 + 2] * inv) | (bf16_bits(acc[db][4 * i4 + 3] * inv) << 16);
+          *(uint2 *)(orow + d0) = w;
+        }
+      }
+      if (hi == 0 && p.lse) p.lse[(int64_t)j.qi * p.hq + h] = lse;
+    } else {
+      // split: the sink-free partial; the merge kernel adds the sink
+      const int64_t prow = ((int64_t)j.split * p.num_queries + j.qi) * p.hq + h;
+      float *orow = p.part_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = 32 * db + 8 * i4 + 4 * hi;
+          *(float4 *)(orow + d0) = make_float4(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv,
+                                               acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv);
+        }
+      }
+      if (hi == 0) p.part_lse[prow] = lse;
+    }
+  };
+
+  // Q fragments of this wave's heads from a Q tile in ring slot `slot`
+  // (heads 0-31 in the K slot, 32-63 in the V slot, swizzled like a K tile)
+  auto load_q = [&](int slot) {
+    const uint8_t *Qt = hw == 0 ? sm.kr[slot] : sm.vr[slot];
+    const int r = lane & 31;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int c = 2 * kk + hi;
+      qf[kk] = *(const bf16x8 *)(Qt + r * C::kRowB + ((c ^ swz<C::kChunks>(r)) * 16));
+    }
+  };
+
+  // FP8: widen a staged e4m3 tile to bf16 (exact) into its swizzled slot
+  auto widen = [&](const uint8_t *src, uint8_t *dst) {
+    constexpr int kPieces = kTile * D / 8;   // 8-byte pieces per tile
+    for (int idx = tid; idx < kPieces; idx += C::kThreads) {
+      const int r = idx / (D / 8);
+      const int piece = idx - r * (D / 8);
+      const uint2 w = *(const uint2 *)(src + r * D + piece * 8);
+      const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+      const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+      const f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+      const f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+      uint4 o;
+      o.x = pack_bf16_hi(a0[0], a0[1]);
+      o.y = pack_bf16_hi(a1[0], a1[1]);
+      o.z = pack_bf16_hi(a2[0], a2[1]);
+      o.w = pack_bf16_hi(a3[0], a3[1]);
+      *(uint4 *)(dst + r * C::kRowB + ((piece ^ swz<C::kChunks>(r)) * 16)) = o;
+    }
+  };
+
+  // S^T = K . Q^T for the tile in K slot `slot`
+  auto scores = [&](int slot) {
+    const uint8_t *Kt = sm.kr[slot];
+    const int r = lane & 31;
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int c = 2 * kk + hi;
+      const bf16x8 a = *(const bf16x8 *)(Kt + r * C::kRowB + ((c ^ swz<C::kChunks>(r)) * 16));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
+    }
+    return s;
+  };
+
+  // Online softmax of a tile's scores, then O^T += V^T . P^T.  Lane rows:
+  // 8*(i/4) + 4*hi + i%4.  The max is taken on the raw scores (the scale
+  // c = scale*log2 e is positive), and p = exp2(s*c - m) is one FMA and one
+  // exp per score.
+  auto softmax_pv = [&](auto masked, const f32x16 &s, uint32_t tm, int slot, bool cmp) {
+    float sc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = s[i];
+    if (FP8 && cmp) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 kk4 = *(const float4 *)(&sm.scl[FP8 ? slot : 0][8 * q4 + 4 * hi]);
+        sc[4 * q4 + 0] *= kk4.x;
+        sc[4 * q4 + 1] *= kk4.y;
+        sc[4 * q4 + 2] *= kk4.z;
+        sc[4 * q4 + 3] *= kk4.w;
+      }
+    }
+    if constexpr (decltype(masked)::value) {
+      const uint32_t tmh = tm >> (4 * hi);   // row 8*(i/4) + 4*hi + i%4 is bit 8*(i/4) + i%4 of tmh
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = ((tmh >> (8 * (i >> 2) + (i & 3))) & 1u) ? sc[i] : -INFINITY;
+    }
+    float smax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    smax = fmaxf(smax, fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])),
+                             fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]))));
+    smax = max_lane_pair(smax);
+    const float tmax = smax * p.scale_log2;               // -inf stays -inf
+    const bool need = tmax > m + kTau;                     // same on both lanes of a head
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m - tmax) : 1.f;   // m = -inf -> 0
+      m = need ? tmax : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    }
+    const float negm = m == -INFINITY ? 0.f : -m;          // all scores are -inf then
+    float pr[16];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.scale_log2, negm));
+      psum += pr[i];
+    }
+    l += psum;
+    if (FP8 && cmp) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 vv = *(const float4 *)(&sm.scl[FP8 ? slot : 0][32 + 8 * q4 + 4 * hi]);
+        pr[4 * q4 + 0] *= vv.x;
+        pr[4 * q4 + 1] *= vv.y;
+        pr[4 * q4 + 2] *= vv.z;
+        pr[4 * q4 + 3] *= vv.w;
+      }
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[k2][j] = (__bf16)pr[8 * k2 + j];
+
+    // V^T from the transpose read of the row-major tile
+    const uint8_t *Vt = sm.vr[slot];
+    const int G = lane >> 4;
+    const int L = lane & 15;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        i16x4 part[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int row = 16 * k2 + 8 * rr + 4 * (G >> 1) + (L >> 2);
+          const int d = 32 * db + 16 * (G & 1) + 4 * (L & 3);
+          const int off = row * C::kRowB + (((d >> 3) ^ swz<C::kChunks>(row)) * 16) + (L & 1) * 8;
+          part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(Vt + off));
+        }
+        const i16x8 cat = {part[0][0], part[0][1], part[0][2], part[0][3],
+                           part[1][0], part[1][1], part[1][2], part[1][3]};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[k2], acc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // The stream: step t (after barrier t) consumes tile t, either a job's Q
+  // tile (its fragments into registers) or one of its KV tiles (scores,
+  // online softmax, PV product; the job's output after its last tile).  The
+  // load wave refills tile t's slot only after barrier t+1.
+  init_job(0);
+  for (int t = 0; t < T; ++t) {
+    if (t > 0) block_sync();                  // barrier t (barrier 0 was taken above)
+    const int slot = t % kRing;
+    const uint4 d = sm.desc[slot];
+    if (d.y & kTileWiden) {
+      if (FP8) {
+        widen(sm.stk[FP8 ? slot : 0], sm.kr[slot]);
+        widen(sm.stv[FP8 ? slot : 0], sm.vr[slot]);
+      }
+      block_sync();
+    }
+    if (d.y & kTileQ) {
+      load_q(slot);
+    } else if (d.y & kTileKV) {
+      const bool cmp = (d.y & kTileCmp) != 0;
+      const f32x16 s = scores(slot);
+      if (d.x == 0xFFFFFFFFu) softmax_pv(std::false_type{}, s, d.x, slot, cmp);
+      else softmax_pv(std::true_type{}, s, d.x, slot, cmp);
+      if (d.y & kTileLast) {
+        epilogue((int32_t)d.z);
+        init_job((int32_t)d.z + 1);
+      }
     }
   }
-  if (hi == 0) p.part_lse[prow] = lse;
 }
 
-template <int D, int NH, int NQ, bool FP8>
-hipError_t launch_t(const Params &p, hipStream_t stream) {
-  constexpr int NBUF = 4;   // 3 tiles in flight behind the one being computed
-  const unsigned grid = (unsigned)p.jobs_per_xcd * 8u;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NH, NQ, FP8, NBUF>), dim3(grid), dim3((NH * NQ + 1) * 64), 0, stream, p);
-  return hipGetLastError();
+template <int D, int NH, bool FP8>
+hipError_t launch_t(const Params &p0, hipStream_t stream) {
+  using C = Cfg<D, NH, FP8>;
+  static int resident[64] = {};   // workgroups resident at once, per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (resident[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_kernel<D, NH, FP8>, C::kBlock, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    resident[dev] = std::max(8, per_cu * cus / 8 * 8);
+  }
+  const int64_t units = (int64_t)p0.num_queries * p0.hkv;
+  const int64_t R = p0.jobs_per_unit;
+  const int64_t G = std::min<int64_t>(resident[dev], (units * R + 7) / 8 * 8);
+  const int64_t Gx = G / 8;
+  // units per launch: 8 * floor(kMaxJobs * Gx / R), so that no workgroup
+  // gets more than kMaxJobs jobs (every XCD gets at most upl / 8 units)
+  const int64_t upl = 8 * std::max<int64_t>(1, C::kMaxJobs * Gx / R);
+  if ((upl / 8) * R > C::kMaxJobs * Gx) return hipErrorInvalidConfiguration;
+  Params p = p0;
+  for (int64_t u0 = 0; u0 < units; u0 += upl) {
+    p.unit_begin = (int32_t)u0;
+    p.unit_end = (int32_t)std::min(units, u0 + upl);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NH, FP8>), dim3((unsigned)G), dim3(C::kBlock), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int D, bool FP8>
 hipError_t launch_d(const Params &p, hipStream_t stream) {
   const int heads = p.group < p.heads_per_block ? p.group : p.heads_per_block;
-  const int nh = heads <= 32 ? 1 : (heads <= 64 ? 2 : 4);
-  const int nq = p.queries_per_group;
-  switch (nh * 16 + nq) {
-    case 1 * 16 + 1: return launch_t<D, 1, 1, FP8>(p, stream);
-    case 2 * 16 + 1: return launch_t<D, 2, 1, FP8>(p, stream);
-    case 4 * 16 + 1: return launch_t<D, 4, 1, FP8>(p, stream);
-    case 1 * 16 + 2: return launch_t<D, 1, 2, FP8>(p, stream);
-    case 2 * 16 + 2: return launch_t<D, 2, 2, FP8>(p, stream);
-    case 1 * 16 + 4: return launch_t<D, 1, 4, FP8>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return heads <= 32 ? launch_t<D, 1, FP8>(p, stream) : launch_t<D, 2, FP8>(p, stream);
 }
 
 }  // namespace

@@ -28,11 +28,15 @@ struct Params {
   int32_t raw_pt_stride, cmp_pt_stride;
   int32_t num_seqs, num_queries, hq, hkv, head_dim, page_size, window, ratio, topk, num_splits;
   int32_t group;                      // Hq / Hkv
-  int32_t heads_per_block;            // query heads per workgroup: 32, 64 or 128
-  int32_t queries_per_group;          // queries a workgroup serves together: 1, 2 or 4
+  int32_t heads_per_block;            // query heads per job: 32 or 64
   int32_t head_groups;                // ceil(group / heads_per_block)
-  int32_t total_jobs;                 // ceil(Nq / queries_per_group) * Hkv * num_splits * head_groups
-  int32_t jobs_per_xcd;               // ceil(total_jobs / 8)
+  // Jobs: (query i, KV head g, split s, head block hb).  A unit is one
+  // (i, g) pair: u = i * Hkv + g, holding jobs_per_unit = num_splits *
+  // head_groups jobs, r = s * head_groups + hb.  One launch covers the units
+  // [unit_begin, unit_end).
+  int32_t jobs_per_unit;
+  int32_t unit_begin, unit_end;
+  int32_t page_shift;                 // log2(page_size) when a power of two, else -1
   int32_t cmp_fp8;
   float scale_log2;                   // scale * log2(e)
 };

@@ -101,9 +101,8 @@ FAULTS = [
     ("scale_zero", lambda a: setattr(a, "scale", 0.0), -2),
     ("heads_per_block_48", lambda a: setattr(a, "heads_per_block", 48), -4),
     ("queries_per_block_3", lambda a: setattr(a, "queries_per_block", 3), -4),
-    ("group_too_wide", lambda a: (setattr(a, "num_q_heads", 128), setattr(a, "heads_per_block", 64),
-                                  setattr(a, "queries_per_block", 4)), -4),
-    ("groups_with_splits", lambda a: (setattr(a, "queries_per_block", 2), setattr(a, "num_splits", 2)), -4),
+    ("queries_per_block_2", lambda a: setattr(a, "queries_per_block", 2), -4),
+    ("heads_per_block_128", lambda a: (setattr(a, "num_q_heads", 128), setattr(a, "heads_per_block", 128)), -4),
     ("splits_zero", lambda a: setattr(a, "num_splits", 0), -7),
     ("splits_too_many", lambda a: setattr(a, "num_splits", 65), -7),
     ("decode_with_positions", lambda a: setattr(a, "query_pos", 0x20000000), -9),

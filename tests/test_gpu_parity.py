@@ -77,7 +77,7 @@ def test_split_invariance_decode():
             assert accept(O, L, ref[0], ref[1]).ok
 
 
-@pytest.mark.parametrize("hpb", [32, 64, 128])
+@pytest.mark.parametrize("hpb", [32, 64, 0])
 @pytest.mark.parametrize("splits", [1, 2, 5])
 def test_heads_per_block_variants(hpb, splits):
     p = synth.make_workload("decode_csa", batch=3)
