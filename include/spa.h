@@ -64,7 +64,7 @@ typedef enum spa_status {
   SPA_ERR_DTYPE = -3,       /* unknown dtype code, or raw KV not bf16              */
   SPA_ERR_UNSUPPORTED = -4, /* valid request this library does not implement
                                (head_dim other than 64/128, ...)                  */
-  SPA_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                    */
+  SPA_ERR_ALIGN = -5,       /* a pointer lacks the alignment its call requires     */
   SPA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than attn_workspace_size  */
   SPA_ERR_SPLITS = -7,      /* num_splits outside [1, SPA_MAX_SPLITS]              */
   SPA_ERR_LAUNCH = -8,      /* HIP reported an error when launching                */
@@ -160,7 +160,8 @@ spa_status attn_fwd_prefill(const spa_fwd_args *args, void *stream);
    gets O = 0, LSE = -inf.  o_parts f32 [num_parts, rows, head_dim],
    lse_parts f32 [num_parts, rows] (device); sink f32 [num_q_heads] or NULL;
    o_out bf16 [rows, head_dim]; lse_out f32 [rows] or NULL.
-   head_dim in {64, 128}; 1 <= num_parts <= SPA_MAX_SPLITS. */
+   head_dim in {64, 128}; 1 <= num_parts <= SPA_MAX_SPLITS; o_parts 16-byte
+   and o_out 8-byte aligned (else SPA_ERR_ALIGN). */
 spa_status attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t num_parts,
                           int64_t rows, int32_t head_dim, int32_t num_q_heads,
                           const float *sink, void *o_out, float *lse_out, void *stream);

@@ -236,8 +236,9 @@ spa_status attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t 
   if (num_q_heads < 1) return fail(SPA_ERR_SHAPE, "num_q_heads must be >= 1");
   if (head_dim != 64 && head_dim != 128)
     return fail(SPA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
-  if ((rows + 3) / 4 > 0x7FFFFFFFLL) return fail(SPA_ERR_SHAPE, "rows exceed the launch grid");
-  if ((reinterpret_cast<uintptr_t>(o_parts) & 7u) != 0) return fail(SPA_ERR_ALIGN, "o_parts must be 8-byte aligned");
+  if ((rows + 7) / 8 > 0x7FFFFFFFLL) return fail(SPA_ERR_SHAPE, "rows exceed the launch grid");
+  if (!aligned16(o_parts)) return fail(SPA_ERR_ALIGN, "o_parts must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(o_out) & 7u) != 0) return fail(SPA_ERR_ALIGN, "o_out must be 8-byte aligned");
   hipError_t e = spa::launch_merge(o_parts, lse_parts, num_parts, rows, head_dim, num_q_heads, sink,
                                    static_cast<uint16_t *>(o_out), lse_out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));

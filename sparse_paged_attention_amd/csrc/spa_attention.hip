@@ -102,6 +102,16 @@ constexpr float kTau = 8.f;
 // Tile descriptor flags.
 enum : uint32_t { kTileQ = 1, kTileKV = 2, kTileCmp = 4, kTileLast = 8, kTileWiden = 16 };
 
+// A kernel argument held in scalar registers.  Without it, a select between
+// two argument fields (raw or compressed pool, K or V side) can become one
+// vector load from the argument block, and the wait for that load would also
+// drain every tile load in flight.
+template <typename T>
+__device__ __forceinline__ T in_sgpr(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
 // Source of the padding loads and of the loads for masked rows.
 __device__ __attribute__((aligned(16))) const uint8_t kZeroRow[256] = {};
 
@@ -209,7 +219,7 @@ template <int D, int NH, bool FP8>
 struct Cfg {
   static constexpr int NC = NH;                        // compute waves
   static constexpr int kThreads = NC * 64;             // compute threads
-  static constexpr int kBlock = kThreads + 128;        // + the load wave and the translation wave
+  static constexpr int kBlock = kThreads + 192;        // + two load waves (K, V) and the translation wave
   static constexpr int kRowB = 2 * D;                  // bf16 row bytes
   static constexpr int kChunks = kRowB / 16;           // 16-byte chunks per row
   static constexpr int kTileB = kTile * kRowB;         // one K (or V) tile, bytes
@@ -217,9 +227,9 @@ struct Cfg {
   static constexpr int kF8RowB = D;                    // e4m3 row bytes
   static constexpr int kF8TileB = kTile * D;           // one e4m3 K (or V) tile
   static constexpr int kF8HalfOps = kF8TileB / 1024;
-  static constexpr int kLoadOps = 2 * kHalfOps;        // load wave: loads per stream step (K + V)
+  static constexpr int kLoadOps = kHalfOps;            // loads per stream step for one side (K or V) of a tile
   static constexpr int kMaxJobs = 64;                  // jobs per workgroup per launch
-  static_assert(!FP8 || 2 * kF8HalfOps + 1 <= kLoadOps, "fp8 tile: data + scale loads fit the per-tile count");
+  static_assert(!FP8 || kF8HalfOps + 1 <= kLoadOps, "fp8 tile: data + scale loads fit the per-tile count");
   static_assert(2 * kLoadOps < 64, "vmcnt range");
 };
 
@@ -230,26 +240,27 @@ struct Smem {
   alignas(16) uint8_t vr[kRing][C::kTileB];                       // V tiles (a Q tile: heads 32-63)
   alignas(16) uint8_t stk[FP8 ? kRing : 1][FP8 ? C::kF8TileB : 16];   // e4m3 K staging
   alignas(16) uint8_t stv[FP8 ? kRing : 1][FP8 ? C::kF8TileB : 16];   // e4m3 V staging
-  alignas(16) float scl[FP8 ? kRing : 1][64];                     // k scales [0,32), v scales [32,64)
+  alignas(16) float scl_k[FP8 ? kRing : 1][64];                   // k scales [0,32)
+  alignas(16) float scl_v[FP8 ? kRing : 1][64];                   // v scales [0,32)
   alignas(16) int32_t lst[kXRing][64];                            // list entries (lanes 0-31)
   alignas(16) int32_t pg[kXRing][64];                             // page-table entries (lanes 0-31)
   alignas(16) int32_t xid[kXRing][32];                            // logical id per row, -1 = masked
-  // source address of each row of the tile being issued (K rows, V rows;
-  // masked rows point into the zero row) and of its fp8 scales (lanes 0-31
-  // k, 32-63 v)
-  alignas(16) uint64_t kptr[1][32];
-  alignas(16) uint64_t vptr[1][32];
-  alignas(16) uint64_t sptr[1][64];
+  // pool row of every row of a tile (-1: masked), by tile slot, and the
+  // mask of its valid rows
+  alignas(16) int64_t erow[kRing][32];
+  uint32_t emask[kRing];
   alignas(16) uint8_t dummy[1024];                                // destination of padding loads
   alignas(16) uint4 desc[kRing];                                  // tile descriptors
   int32_t ntiles;
 };
 
-template <int D, int NH, bool FP8>
-__global__ __launch_bounds__((NH + 2) * 64) __attribute__((amdgpu_waves_per_eu(2)))  // <= 256 VGPRs
+template <int D, int NH, int NS, bool FP8>
+__global__ __launch_bounds__(NS * (NH + 3) * 64) __attribute__((amdgpu_waves_per_eu(3)))  // <= 168 VGPRs
 void attn_fwd_kernel(const Params p) {
   using C = Cfg<D, NH, FP8>;
-  __shared__ Smem<D, NH, FP8> sm;
+  static_assert(NS == 1 || NS == 2, "one or two streams per workgroup");
+  static_assert(!FP8 || NS == 1, "fp8 staging leaves LDS for one stream only");
+  __shared__ Smem<D, NH, FP8> sm_all[NS];
 
   const int32_t x = (int32_t)(blockIdx.x & 7);
   const int32_t y = (int32_t)(blockIdx.x >> 3);
@@ -261,16 +272,41 @@ void attn_fwd_kernel(const Params p) {
   const int wave = tid >> 6;
   const int hi = lane >> 5;                    // which half of the wave
   const int S = p.num_splits;
+  // NS independent streams (job sequences) share the workgroup and its
+  // barriers: waves [0, NS*NC) compute (stream wave / NC), then the K and
+  // V load waves of each stream, then each stream's translation wave.  A
+  // workgroup's waves 0-3 sit on four different SIMDs and every further
+  // four on the same four, so with NS = 2 and NC = 2 every SIMD runs one
+  // compute wave and one load wave: a SIMD's wave issues its loads into
+  // LDS at a bounded rate, which the load waves then share evenly.
+  constexpr int NCW = NS * C::NC;
+  const bool helper = wave >= NCW;
+  const int hidx = wave - NCW;                 // helper index
+  const int strm = !helper ? wave / C::NC : hidx < 2 * NS ? hidx >> 1 : hidx - 2 * NS;
+  Smem<D, NH, FP8> &sm = sm_all[strm];
+  // stream strm's k-th job is the workgroup's job NS*k + strm
+  auto jid = [&](int32_t k) { return job_id(p, x, y, Gx, NS * k + strm); };
 
   // =================================================================
   // Load wave (K, V and Q tiles) and translation wave (page-table and
   // list entries)
   // =================================================================
-  if (wave >= C::NC) {
-    const bool loader = wave == C::NC;
+  if (helper) {
+    // the K load wave issues the K side of every tile (K rows, Q heads
+    // 0-31) and its descriptor, the V load wave the V side (V rows, Q heads
+    // 32-63), and the translation wave the list and page-table entries and
+    // the pool row of every tile row
+    const bool loader = hidx < 2 * NS;
+    const bool vload = loader && (hidx & 1) != 0;
+    const int64_t raw_np = in_sgpr(p.raw_pages), cmp_np = in_sgpr(p.cmp_pages);
+    const int32_t raw_st = in_sgpr(p.raw_pt_stride), cmp_st = in_sgpr(p.cmp_pt_stride);
+    const int32_t *const raw_pt = in_sgpr(p.raw_pt), *const cmp_pt = in_sgpr(p.cmp_pt);
+    const uint8_t *const raw_b = vload ? in_sgpr(p.v_raw) : in_sgpr(p.k_raw);   // this load wave's side
+    const uint8_t *const cmp_b = vload ? in_sgpr(p.v_cmp) : in_sgpr(p.k_cmp);
+    const float *const cmp_sc = vload ? in_sgpr(p.v_cmp_scale) : in_sgpr(p.k_cmp_scale);
     // ---- per-job metadata, one job per lane (ordinary loads: nothing is in
     // flight yet); both waves compute the same records
-    const JobId jl = job_id(p, x, y, Gx, lane);
+    const JobId jl = jid(lane);
     const bool jvalid = lane < C::kMaxJobs && jl.valid;
     int32_t jnc = 0, jcs = 0, jncr = 0, jwb = 0, jnwr = 0, jnct = 0, jnkv = 1;
     int64_t jrpt = 0, jcpt = 0, jlst = 0;   // row bases: page tables, list
@@ -285,8 +321,8 @@ void attn_fwd_kernel(const Params p) {
     // ones.
     constexpr int kSpec = 5;                 // tiles 1..kSpec of the stream at most
     int32_t nspec = 0;
-    if (wave == C::NC + 1 && p.topk > 0) {
-      const JobId j0 = job_id(p, x, y, Gx, 0);
+    if (!loader && p.topk > 0 && jid(0).valid) {   // (a stream may have no job at all)
+      const JobId j0 = jid(0);
       const int cper = round_up((p.topk + S - 1) / S, kTile);
       const int cs0 = min(p.topk, j0.split * cper);
       const int cap0 = min(p.topk, cs0 + cper) - cs0;
@@ -310,23 +346,21 @@ void attn_fwd_kernel(const Params p) {
       cs16[n] = ((lane % C::kChunks) ^ swz<C::kChunks>(r)) * 16;
     }
 
-    if (wave == C::NC) {
-      // job 0's Q tile: heads 0-31 into K slot 0, 32-63 into V slot 0
+    if (loader) {
+      // job 0's Q tile: heads 0-31 into K slot 0 (K load wave), 32-63 into
+      // V slot 0 (V load wave)
       const int64_t q0 = (int64_t)(((uint64_t)__builtin_amdgcn_readlane((uint32_t)(jq >> 32), 0) << 32) |
                                    __builtin_amdgcn_readlane((uint32_t)jq, 0));
       const int32_t nh0 = __builtin_amdgcn_readlane(jnh, 0);
-      const uint8_t *qb = (const uint8_t *)(p.q + q0) + (lane / C::kChunks) * C::kRowB;
+      const int r0 = vload ? 32 : 0;
+      const uint8_t *qb = (const uint8_t *)(p.q + q0) + (r0 + lane / C::kChunks) * C::kRowB;
+      uint8_t *dst = vload ? sm.vr[0] : sm.kr[0];
 #pragma unroll
       for (int n = 0; n < C::kHalfOps; ++n) {
-        const int r = n * kRowsPerOp + lane / C::kChunks;
-        dma16(r < nh0 ? qb + n * 1024 + cs16[n % kPeriod] : zero16, &sm.kr[0][n * 1024]);
+        const int r = r0 + n * kRowsPerOp + lane / C::kChunks;
+        dma16(r < nh0 ? qb + n * 1024 + cs16[n % kPeriod] : zero16, dst + n * 1024);
       }
-#pragma unroll
-      for (int n = 0; n < C::kHalfOps; ++n) {
-        const int r = 32 + n * kRowsPerOp + lane / C::kChunks;
-        dma16(r < nh0 ? qb + 32 * C::kRowB + n * 1024 + cs16[n % kPeriod] : zero16, &sm.vr[0][n * 1024]);
-      }
-      if (lane == 0) sm.desc[0] = make_uint4(0u, kTileQ, 0u, 0u);
+      if (!vload && lane == 0) sm.desc[0] = make_uint4(0u, kTileQ, 0u, 0u);
     }
     if (jvalid) {
       const QueryKV kv = query_kv(p, jl.qi);
@@ -409,7 +443,9 @@ void attn_fwd_kernel(const Params p) {
     const int32_t P = p.page_size;
     // ---------------- translation wave stages
     // -- list stage: list entries of a compressed KV tile of a top-k layer
-    auto stage_list = [&](const Cur &c) {
+    // (pad = false: a tile with nothing to load issues no padding load;
+    // only where the wave then waits for all of its loads)
+    auto stage_list = [&](const Cur &c, bool pad) {
       const void *src = zero4;
       void *dst = sm.dummy;
       if (c.k < njobs && c.v > 0 && p.topk > 0 && c.v - 1 < c.j.nct) {
@@ -417,11 +453,11 @@ void attn_fwd_kernel(const Params p) {
         if (lane < kTile && idx < c.j.ncr) src = p.cmp_idx + c.j.lst + idx;
         dst = &sm.lst[c.u % kXRing][0];
       }
-      dma4(src, dst);
+      if (pad || dst != (void *)sm.dummy) dma4(src, dst);
     };
-    // -- page stage: logical id of every row of a KV tile, then its
-    // page-table entry
-    auto stage_page = [&](const Cur &c) {
+    // -- page stage: logical id of every row of a KV tile (from its list
+    // entry `le`, read by the caller), then its page-table entry
+    auto stage_page = [&](const Cur &c, int32_t le, bool pad) {
       const void *src = zero4;
       void *dst = sm.dummy;
       if (c.k < njobs && c.v > 0) {
@@ -433,8 +469,7 @@ void attn_fwd_kernel(const Params p) {
             const int32_t idx = e0 * kTile + lane;
             if (idx < c.j.ncr) {
               if (p.topk > 0) {
-                const int32_t c_id = sm.lst[c.u % kXRing][lane];
-                if (c_id >= 0 && c_id < c.j.nc) xv = c_id;
+                if (le >= 0 && le < c.j.nc) xv = le;
                 else errbits |= kErrCmpId;
               } else {
                 xv = c.j.cs + idx;   // all-groups layer: ids in order
@@ -446,8 +481,8 @@ void attn_fwd_kernel(const Params p) {
           }
           if (xv >= 0) {
             const int32_t col = pow2 ? (xv >> p.page_shift) : xv / P;
-            if (col < (cmp ? p.cmp_pt_stride : p.raw_pt_stride)) {
-              src = cmp ? (const void *)(p.cmp_pt + c.j.cpt + col) : (const void *)(p.raw_pt + c.j.rpt + col);
+            if (col < (cmp ? cmp_st : raw_st)) {
+              src = cmp ? (const void *)(cmp_pt + c.j.cpt + col) : (const void *)(raw_pt + c.j.rpt + col);
             } else {
               errbits |= kErrPage;
               xv = -1;
@@ -457,155 +492,177 @@ void attn_fwd_kernel(const Params p) {
         }
         dst = &sm.pg[c.u % kXRing][0];
       }
-      dma4(src, dst);
+      if (pad || dst != (void *)sm.dummy) dma4(src, dst);
+    };
+    auto list_entry = [&](const Cur &c) { return sm.lst[c.u % kXRing][lane & 31]; };
+    // -- row stage: pool row of every row of a KV tile from its id and page
+    // entry (read by the caller), and the mask of the valid rows
+    auto stage_rows = [&](const Cur &c, int32_t xv, int32_t page) {
+      if (c.k >= njobs || c.v == 0) return;
+      const bool cmp = c.v - 1 < c.j.nct;
+      int64_t er = -1;
+      if (lane < kTile && xv >= 0) {
+        if (page >= 0 && (int64_t)page < (cmp ? cmp_np : raw_np)) {
+          const int32_t off = pow2 ? (xv & (P - 1)) : xv - (xv / P) * P;
+          er = ((int64_t)page * P + off) * p.hkv + c.j.g;
+        } else {
+          errbits |= kErrPage;
+        }
+      }
+      const uint32_t mask = (uint32_t)__ballot(er >= 0);
+      if (lane < kTile) sm.erow[c.u % kRing][lane] = er;
+      if (lane == 0) sm.emask[c.u % kRing] = mask;
     };
 
-    // ---------------- load wave stage
-    // -- the tile's loads: K and V (or the two head halves of a Q tile) and
-    // its descriptor
-    auto stage_kv = [&](const Cur &c) {
+    // ---------------- tile loads
+    // -- one side of a tile (K: load wave, V: translation wave).  The pool
+    // rows each lane loads are read first, in one batch of LDS reads (a
+    // load's asm orders every later LDS access behind it) ...
+    struct Rows {
+      int64_t r[C::kHalfOps];
+      int64_t own;   // row `lane` (lanes 0-31), for the fp8 scales
+    };
+    auto side_rows = [&](const Cur &c) {
+      Rows w;
+      const int es = c.u % kRing;
+      const bool f8 = FP8 && c.k < njobs && c.v > 0 && c.v - 1 < c.j.nct;
+#pragma unroll
+      for (int n = 0; n < C::kHalfOps; ++n) {
+        const int r = f8 ? min((n * 1024 + lane * 16) / C::kF8RowB, kTile - 1) : n * kRowsPerOp + lane / C::kChunks;
+        w.r[n] = sm.erow[es][r];
+      }
+      w.own = sm.erow[es][lane & 31];
+      return w;
+    };
+    // ... then its loads: K or V rows (the zero row for a masked one), or
+    // the matching head half of a Q tile, or padding past the last job
+    auto side_loads = [&](const Cur &c, const Rows &w) {
       const int slot = c.u % kRing;
-      uint4 d = make_uint4(0u, 0u, 0u, 0u);
+      uint8_t *dst = vload ? sm.vr[slot] : sm.kr[slot];
       if (c.k >= njobs) {
 #pragma unroll
-        for (int n = 0; n < 2 * C::kHalfOps; ++n) dma16(zero16, sm.dummy);
-      } else if (c.v == 0) {
+        for (int n = 0; n < C::kHalfOps; ++n) dma16(zero16, sm.dummy);
+        return;
+      }
+      if (c.v == 0) {
         // Q rows of the block's heads, swizzled like a K tile: heads 0-31 in
         // the K slot, 32-63 in the V slot; heads past the KV group read zeros
-        const uint8_t *qb = (const uint8_t *)(p.q + c.j.q) + (lane / C::kChunks) * C::kRowB;
+        const int r0 = vload ? 32 : 0;
+        const uint8_t *qb = (const uint8_t *)(p.q + c.j.q) + (r0 + lane / C::kChunks) * C::kRowB;
 #pragma unroll
         for (int n = 0; n < C::kHalfOps; ++n) {
-          const int r = n * kRowsPerOp + lane / C::kChunks;
-          dma16(r < c.j.nh ? qb + n * 1024 + cs16[n % kPeriod] : zero16, &sm.kr[slot][n * 1024]);
+          const int r = r0 + n * kRowsPerOp + lane / C::kChunks;
+          dma16(r < c.j.nh ? qb + n * 1024 + cs16[n % kPeriod] : zero16, dst + n * 1024);
         }
-#pragma unroll
-        for (int n = 0; n < C::kHalfOps; ++n) {
-          const int r = 32 + n * kRowsPerOp + lane / C::kChunks;
-          dma16(r < c.j.nh ? qb + 32 * C::kRowB + n * 1024 + cs16[n % kPeriod] : zero16, &sm.vr[slot][n * 1024]);
-        }
-        d = make_uint4(0u, kTileQ, (uint32_t)c.k, 0u);
-      } else {
-        const int xs = c.u % kXRing;
-        const bool cmp = c.v - 1 < c.j.nct;
-        const bool f8 = FP8 && cmp;
-        // row addresses (lanes 0-31 = rows), page ids checked
-        bool ok = false;
-        if (lane < kTile) {
-          const int32_t xv = sm.xid[xs][lane];
-          int64_t er = -1;
-          if (xv >= 0) {
-            const int32_t page = sm.pg[xs][lane];
-            if (page >= 0 && (int64_t)page < (cmp ? p.cmp_pages : p.raw_pages)) {
-              const int32_t off = pow2 ? (xv & (P - 1)) : xv - (xv / P) * P;
-              er = ((int64_t)page * P + off) * p.hkv + c.j.g;
-            } else {
-              errbits |= kErrPage;
-            }
-          }
-          ok = er >= 0;
-          const int64_t rb = f8 ? C::kF8RowB : C::kRowB;
-          const uint8_t *kb = cmp ? p.k_cmp : p.k_raw;
-          const uint8_t *vb = cmp ? p.v_cmp : p.v_raw;
-          sm.kptr[0][lane] = (uint64_t)(ok ? kb + er * rb : kZeroRow);
-          sm.vptr[0][lane] = (uint64_t)(ok ? vb + er * rb : kZeroRow);
-          if (FP8 && f8) {
-            sm.sptr[0][lane] = (uint64_t)(ok ? (const void *)(p.k_cmp_scale + er) : zero4);
-            sm.sptr[0][32 + lane] = (uint64_t)(ok ? (const void *)(p.v_cmp_scale + er) : zero4);
-          }
-        }
-        const uint32_t mask = (uint32_t)__ballot(ok);
-        // all row lookups before the first load: a load's asm orders every
-        // later LDS access behind it
-        if (!f8) {
-          const uint8_t *ks[C::kHalfOps], *vs[C::kHalfOps];
-#pragma unroll
-          for (int n = 0; n < C::kHalfOps; ++n) {
-            const int r = n * kRowsPerOp + lane / C::kChunks;
-            ks[n] = (const uint8_t *)sm.kptr[0][r] + cs16[n % kPeriod];
-            vs[n] = (const uint8_t *)sm.vptr[0][r] + cs16[n % kPeriod];
-          }
-#pragma unroll
-          for (int n = 0; n < C::kHalfOps; ++n) dma16(ks[n], &sm.kr[slot][n * 1024]);
-#pragma unroll
-          for (int n = 0; n < C::kHalfOps; ++n) dma16(vs[n], &sm.vr[slot][n * 1024]);
-        } else {
-          const uint8_t *ks[C::kF8HalfOps], *vs[C::kF8HalfOps];
-#pragma unroll
-          for (int n = 0; n < C::kF8HalfOps; ++n) {
-            const int lin = n * 1024 + lane * 16;
-            ks[n] = (const uint8_t *)sm.kptr[0][lin / C::kF8RowB] + (lin % C::kF8RowB);
-            vs[n] = (const uint8_t *)sm.vptr[0][lin / C::kF8RowB] + (lin % C::kF8RowB);
-          }
-          const void *ssrc = (const void *)sm.sptr[0][lane];
-#pragma unroll
-          for (int n = 0; n < C::kF8HalfOps; ++n) dma16(ks[n], &sm.stk[FP8 ? slot : 0][n * 1024]);
-#pragma unroll
-          for (int n = 0; n < C::kF8HalfOps; ++n) dma16(vs[n], &sm.stv[FP8 ? slot : 0][n * 1024]);
-          dma4(ssrc, &sm.scl[FP8 ? slot : 0][0]);
-#pragma unroll
-          for (int n = 2 * C::kF8HalfOps + 1; n < 2 * C::kHalfOps; ++n) dma16(zero16, sm.dummy);
-        }
-        uint32_t f = kTileKV;
-        if (cmp) f |= kTileCmp;
-        if (f8) f |= kTileWiden;
-        if (c.v == c.j.nkv) f |= kTileLast;
-        d = make_uint4(mask, f, (uint32_t)c.k, 0u);
+        return;
       }
-      if (lane == 0) sm.desc[slot] = d;
+      const bool cmp = c.v - 1 < c.j.nct;
+      const uint8_t *const base = cmp ? cmp_b : raw_b;
+      if (!(FP8 && cmp)) {
+        const uint8_t *src[C::kHalfOps];
+#pragma unroll
+        for (int n = 0; n < C::kHalfOps; ++n)
+          src[n] = (w.r[n] >= 0 ? base + w.r[n] * C::kRowB : kZeroRow) + cs16[n % kPeriod];
+#pragma unroll
+        for (int n = 0; n < C::kHalfOps; ++n) dma16(src[n], dst + n * 1024);
+      } else {
+        const uint8_t *src[C::kF8HalfOps];
+#pragma unroll
+        for (int n = 0; n < C::kF8HalfOps; ++n)
+          src[n] = (w.r[n] >= 0 ? base + w.r[n] * C::kF8RowB : kZeroRow) + (n * 1024 + lane * 16) % C::kF8RowB;
+        const void *ssrc = (lane < kTile && w.own >= 0) ? (const void *)(cmp_sc + w.own) : zero4;
+        uint8_t *sdst = vload ? sm.stv[FP8 ? slot : 0] : sm.stk[FP8 ? slot : 0];
+#pragma unroll
+        for (int n = 0; n < C::kF8HalfOps; ++n) dma16(src[n], sdst + n * 1024);
+        dma4(ssrc, vload ? sm.scl_v[FP8 ? slot : 0] : sm.scl_k[FP8 ? slot : 0]);
+#pragma unroll
+        for (int n = C::kF8HalfOps + 1; n < C::kHalfOps; ++n) dma16(zero16, sm.dummy);
+      }
+    };
+    // -- descriptor of a tile (load wave)
+    auto tile_desc = [&](const Cur &c, uint32_t mask) {
+      if (c.k >= njobs) return make_uint4(0u, 0u, 0u, 0u);
+      if (c.v == 0) return make_uint4(0u, kTileQ, (uint32_t)c.k, 0u);
+      const bool cmp = c.v - 1 < c.j.nct;
+      uint32_t f = kTileKV;
+      if (cmp) f |= kTileCmp;
+      if (FP8 && cmp) f |= kTileWiden;
+      if (c.v == c.j.nkv) f |= kTileLast;
+      return make_uint4(mask, f, (uint32_t)c.k, 0u);
+    };
+    auto load_step = [&](Cur &c) {
+      const Rows w = side_rows(c);
+      const uint32_t mask = sm.emask[c.u % kRing];
+      side_loads(c, w);
+      if (!vload && lane == 0) sm.desc[c.u % kRing] = tile_desc(c, mask);
+      advance(c);
     };
 
-    // ---- the stream.  Step t (after barrier t): the load wave issues tile
-    // t+3 (K and V), the translation wave the page entries of tile t+6 and
-    // the list entries of tile t+9.  Each wave issues a fixed number of loads
-    // per step and, before barrier t+1, waits for its own loads of steps
-    // <= t-2: tile t+1 for the compute waves, and every stage's input three
-    // steps after it was issued.
+    // ---- the stream.  Step t (after barrier t): the load waves issue the K
+    // and V sides of tile t+3; the translation wave forms the pool rows of
+    // tile t+4 and issues the page entries of tile t+7 and the list entries
+    // of tile t+10.  Each wave issues a fixed number of loads per step and,
+    // before barrier t+1, waits for its own loads of steps <= t-2: tile t+1
+    // for the compute waves, and every stage's input two steps before it is
+    // read.
     //
     // Priming, before barrier 0: the translation wave issues the lists of
-    // tiles 0-5 (those not loaded early), then their page entries and the
-    // lists of tiles 6-8 (each phase complete before the next); after a
-    // barrier the load wave issues tiles 1 and 2 (tile 0, job 0's Q tile,
-    // was issued at the start).
-    Cur c0{0, loader ? 1 : 0, loader ? 1 : 0, job(0)}, c1{0, 0, 0, job(0)};   // load: tiles; translation: page, list
-    if (!loader) {
+    // tiles 0-6 (those not loaded early), then their page entries and the
+    // lists of tiles 7-9 (each phase complete before the next), and forms
+    // the pool rows of tiles 0-3; after a barrier the load waves issue tiles
+    // 1 and 2 (tile 0, job 0's Q tile, was issued at the start).
+    Cur cv{0, 0, 0, job(0)};   // load waves: tiles; translation wave: rows, page entries, lists
+    Cur cp = cv, cl = cv;
+    if (loader) {
+      advance(cv);
+    } else {
       wait_vmcnt<0>();   // the early list loads land before any stage reuses their slots
-      for (int n = 0; n < 6; ++n) {
+      for (int n = 0; n < 7; ++n) {
         // the early loads hold the lists of job 0's first compressed tiles
-        const bool early = c1.k == 0 && c1.v >= 1 && c1.v <= nspec && c1.v - 1 < c1.j.nct;
-        if (!early) stage_list(c1);
-        advance(c1);
+        const bool early = cl.k == 0 && cl.v >= 1 && cl.v <= nspec && cl.v - 1 < cl.j.nct;
+        if (!early) stage_list(cl, false);
+        advance(cl);
       }
       wait_vmcnt<0>();
-      for (int n = 0; n < 6; ++n) {
-        stage_page(c0);
-        advance(c0);
+      for (int n = 0; n < 7; ++n) {
+        stage_page(cp, list_entry(cp), false);
+        advance(cp);
       }
       for (int n = 0; n < 3; ++n) {
-        stage_list(c1);
-        advance(c1);
+        stage_list(cl, false);
+        advance(cl);
       }
       wait_vmcnt<0>();
-    }
-    block_sync();   // page entries of tiles 0-5 are in
-    if (loader) {
-      for (int n = 0; n < 2; ++n) {
-        stage_kv(c0);
-        advance(c0);
+      for (int n = 0; n < 4; ++n) {
+        stage_rows(cv, sm.xid[cv.u % kXRing][lane & 31], sm.pg[cv.u % kXRing][lane & 31]);
+        advance(cv);
       }
-      wait_vmcnt<2 * C::kLoadOps>();   // tile 0
+    }
+    block_sync();   // pool rows of tiles 0-3 are in
+    // every stream takes as many steps as the longest (a finished one pads)
+    if (NS > 1) T = max(sm_all[0].ntiles, sm_all[NS - 1].ntiles);
+    if (loader) {
+      load_step(cv);
+      load_step(cv);
+      wait_vmcnt<2 * C::kLoadOps>();   // tile 0 (its side)
     }
     for (int t = 0; t < T; ++t) {
       block_sync();   // barrier t
-      if (sm.desc[t % kRing].y & kTileWiden) block_sync();   // the compute waves widen tile t
+      if (FP8 && (sm.desc[t % kRing].y & kTileWiden)) block_sync();   // the compute waves widen tile t
       if (loader) {
-        stage_kv(c0);
-        advance(c0);
+        load_step(cv);
         wait_vmcnt<2 * C::kLoadOps>();
       } else {
-        stage_page(c0);
-        advance(c0);
-        stage_list(c1);
-        advance(c1);
+        // every LDS read of the step first, in one batch
+        const int32_t xv = sm.xid[cv.u % kXRing][lane & 31];
+        const int32_t pgv = sm.pg[cv.u % kXRing][lane & 31];
+        const int32_t le = list_entry(cp);
+        stage_rows(cv, xv, pgv);
+        advance(cv);
+        stage_page(cp, le, true);
+        advance(cp);
+        stage_list(cl, true);
+        advance(cl);
         wait_vmcnt<2 * 2>();
       }
     }
@@ -618,9 +675,9 @@ void attn_fwd_kernel(const Params p) {
   // =================================================================
   // Compute waves
   // =================================================================
-  const int hw = wave;                        // this wave's 32-head block within the job's heads
+  const int hw = wave % C::NC;                // this wave's 32-head block within the job's heads
   block_sync();                               // priming: the page entries of tiles 0-5 are in
-  const int32_t T = sm.ntiles;
+  const int32_t T = NS == 1 ? sm.ntiles : max(sm_all[0].ntiles, sm_all[NS - 1].ntiles);
   block_sync();                               // barrier 0: tile 0 is in
 
   // per-job state
@@ -630,7 +687,7 @@ void attn_fwd_kernel(const Params p) {
   // sink logit of this lane's head in job k (-inf: none), loaded one job
   // ahead so that its load is long complete when the job starts
   auto load_sink = [&](int32_t k) {
-    const JobId j = job_id(p, x, y, Gx, k);
+    const JobId j = jid(k);
     const int hl = j.hb * p.heads_per_block + hw * 32 + (lane & 31);
     return (j.valid && S == 1 && p.sink != nullptr && hl < p.group) ? p.sink[j.g * p.group + hl] : -INFINITY;
   };
@@ -643,7 +700,7 @@ void attn_fwd_kernel(const Params p) {
     sink_next = load_sink(k + 1);
   };
   auto epilogue = [&](int32_t k) {
-    const JobId j = job_id(p, x, y, Gx, k);
+    const JobId j = jid(k);
     const int hl = j.hb * p.heads_per_block + hw * 32 + (lane & 31);
     const float lt = l + __shfl_xor(l, 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -697,7 +754,7 @@ void attn_fwd_kernel(const Params p) {
   // FP8: widen a staged e4m3 tile to bf16 (exact) into its swizzled slot
   auto widen = [&](const uint8_t *src, uint8_t *dst) {
     constexpr int kPieces = kTile * D / 8;   // 8-byte pieces per tile
-    for (int idx = tid; idx < kPieces; idx += C::kThreads) {
+    for (int idx = hw * 64 + lane; idx < kPieces; idx += C::kThreads) {
       const int r = idx / (D / 8);
       const int piece = idx - r * (D / 8);
       const uint2 w = *(const uint2 *)(src + r * D + piece * 8);
@@ -739,7 +796,7 @@ void attn_fwd_kernel(const Params p) {
     if (FP8 && cmp) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 kk4 = *(const float4 *)(&sm.scl[FP8 ? slot : 0][8 * q4 + 4 * hi]);
+        const float4 kk4 = *(const float4 *)(&sm.scl_k[FP8 ? slot : 0][8 * q4 + 4 * hi]);
         sc[4 * q4 + 0] *= kk4.x;
         sc[4 * q4 + 1] *= kk4.y;
         sc[4 * q4 + 2] *= kk4.z;
@@ -776,7 +833,7 @@ void attn_fwd_kernel(const Params p) {
     if (FP8 && cmp) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 vv = *(const float4 *)(&sm.scl[FP8 ? slot : 0][32 + 8 * q4 + 4 * hi]);
+        const float4 vv = *(const float4 *)(&sm.scl_v[FP8 ? slot : 0][8 * q4 + 4 * hi]);
         pr[4 * q4 + 0] *= vv.x;
         pr[4 * q4 + 1] *= vv.y;
         pr[4 * q4 + 2] *= vv.z;
@@ -843,9 +900,10 @@ void attn_fwd_kernel(const Params p) {
   }
 }
 
-template <int D, int NH, bool FP8>
+template <int D, int NH, int NS, bool FP8>
 hipError_t launch_t(const Params &p0, hipStream_t stream) {
   using C = Cfg<D, NH, FP8>;
+  constexpr int kBlock = NS * C::kBlock;
   static int resident[64] = {};   // workgroups resident at once, per device
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -853,7 +911,7 @@ hipError_t launch_t(const Params &p0, hipStream_t stream) {
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (resident[dev] == 0) {
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_kernel<D, NH, FP8>, C::kBlock, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_kernel<D, NH, NS, FP8>, kBlock, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -863,15 +921,15 @@ hipError_t launch_t(const Params &p0, hipStream_t stream) {
   const int64_t R = p0.jobs_per_unit;
   const int64_t G = std::min<int64_t>(resident[dev], (units * R + 7) / 8 * 8);
   const int64_t Gx = G / 8;
-  // units per launch: 8 * floor(kMaxJobs * Gx / R), so that no workgroup
+  // units per launch: 8 * floor(NS * kMaxJobs * Gx / R), so that no stream
   // gets more than kMaxJobs jobs (every XCD gets at most upl / 8 units)
-  const int64_t upl = 8 * std::max<int64_t>(1, C::kMaxJobs * Gx / R);
-  if ((upl / 8) * R > C::kMaxJobs * Gx) return hipErrorInvalidConfiguration;
+  const int64_t upl = 8 * std::max<int64_t>(1, NS * C::kMaxJobs * Gx / R);
+  if ((upl / 8) * R > NS * C::kMaxJobs * Gx) return hipErrorInvalidConfiguration;
   Params p = p0;
   for (int64_t u0 = 0; u0 < units; u0 += upl) {
     p.unit_begin = (int32_t)u0;
     p.unit_end = (int32_t)std::min(units, u0 + upl);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, NH, FP8>), dim3((unsigned)G), dim3(C::kBlock), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, NH, NS, FP8>), dim3((unsigned)G), dim3(kBlock), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -881,7 +939,12 @@ hipError_t launch_t(const Params &p0, hipStream_t stream) {
 template <int D, bool FP8>
 hipError_t launch_d(const Params &p, hipStream_t stream) {
   const int heads = p.group < p.heads_per_block ? p.group : p.heads_per_block;
-  return heads <= 32 ? launch_t<D, 1, FP8>(p, stream) : launch_t<D, 2, FP8>(p, stream);
+  // 64-head jobs in bf16: two streams per workgroup (one workgroup per CU,
+  // a compute wave on every SIMD); otherwise one stream (two workgroups per
+  // CU)
+  if (heads <= 32) return launch_t<D, 1, 1, FP8>(p, stream);
+  if constexpr (FP8) return launch_t<D, 2, 1, FP8>(p, stream);
+  else return launch_t<D, 2, 2, FP8>(p, stream);
 }
 
 }  // namespace

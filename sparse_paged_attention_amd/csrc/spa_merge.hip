@@ -8,7 +8,8 @@
 // part with O = 0.  The order of the sums is fixed (s ascending), so the
 // result is bitwise deterministic.
 //
-// HBM-bound: one wave per row, each lane owns D/64 consecutive floats.
+// HBM-bound: D/4 lanes per row, one float4 of O each; up to 8 parts are
+// loaded (LSE and O together) in one round trip, more in chunks of 8.
 
 #include <hip/hip_runtime.h>
 
@@ -26,59 +27,85 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ o_
                                                     const float *__restrict__ sink,
                                                     uint16_t *__restrict__ o_out,
                                                     float *__restrict__ lse_out) {
-  constexpr int E = D / 64;   // floats per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int LPR = D / 4;          // lanes per row
+  constexpr int RPB = 256 / LPR;      // rows per block
+  const int c = threadIdx.x % LPR;    // this lane's float4 of the row
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   if (row >= rows) return;
   const float sk = sink ? sink[row % hq] : -INFINITY;
-  // loads are issued 8 parts at a time so that they are in flight together
   float M = sk;
-  for (int s0 = 0; s0 < S; s0 += 8) {
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float Z = 0.f;
+  auto part = [&](int s) { return *(const float4 *)(o_parts + ((int64_t)s * rows + row) * D + 4 * c); };
+  auto add = [&](float w, const float4 &v) {
+    o.x += w * v.x;
+    o.y += w * v.y;
+    o.z += w * v.z;
+    o.w += w * v.w;
+  };
+  if (S <= 8) {
+    // one round trip: every part's LSE and O in flight together
     float ls[8];
+    float4 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) ls[k] = s0 + k < S ? lse_parts[(int64_t)(s0 + k) * rows + row] : -INFINITY;
+    for (int k = 0; k < 8; ++k) {
+      const bool in = k < S;
+      ls[k] = in ? lse_parts[(int64_t)k * rows + row] : -INFINITY;
+      v[k] = in ? part(k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) M = fmaxf(M, ls[k]);
-  }
-  float o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-  float lse = -INFINITY;
-  if (M != -INFINITY) {
-    float Z = sk == -INFINITY ? 0.f : __expf(sk - M);
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      float ls[8];
-      float v[8][E];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const bool in = s0 + k < S;
-        ls[k] = in ? lse_parts[(int64_t)(s0 + k) * rows + row] : -INFINITY;
-        const float *src = o_parts + ((int64_t)(s0 + k) * rows + row) * D + lane * E;
-        if constexpr (E == 2) {
-          const float2 t = in ? *(const float2 *)src : make_float2(0.f, 0.f);
-          v[k][0] = t.x;
-          v[k][E - 1] = t.y;
-        } else {
-          v[k][0] = in ? src[0] : 0.f;
-        }
-      }
+    if (M != -INFINITY) {
+      Z = sk == -INFINITY ? 0.f : __expf(sk - M);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float w = ls[k] == -INFINITY ? 0.f : __expf(ls[k] - M);
         Z += w;
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[e] += w * v[k][e];
+        add(w, v[k]);
       }
     }
-    const float inv = 1.f / Z;
+  } else {
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float ls[8];
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] *= inv;
+      for (int k = 0; k < 8; ++k) ls[k] = s0 + k < S ? lse_parts[(int64_t)(s0 + k) * rows + row] : -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) M = fmaxf(M, ls[k]);
+    }
+    if (M != -INFINITY) {
+      Z = sk == -INFINITY ? 0.f : __expf(sk - M);
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        float ls[8];
+        float4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const bool in = s0 + k < S;
+          ls[k] = in ? lse_parts[(int64_t)(s0 + k) * rows + row] : -INFINITY;
+          v[k] = in ? part(s0 + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float w = ls[k] == -INFINITY ? 0.f : __expf(ls[k] - M);
+          Z += w;
+          add(w, v[k]);
+        }
+      }
+    }
+  }
+  float lse = -INFINITY;
+  if (M != -INFINITY) {
+    const float inv = 1.f / Z;
+    o.x *= inv;
+    o.y *= inv;
+    o.z *= inv;
+    o.w *= inv;
     lse = M + __logf(Z);
   }
-  uint16_t *dst = o_out + row * D + lane * E;
-#pragma unroll
-  for (int e = 0; e < E; ++e) dst[e] = __builtin_bit_cast(uint16_t, (__bf16)o[e]);
-  if (lse_out && lane == 0) lse_out[row] = lse;
+  uint2 w;
+  w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o.x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o.y) << 16);
+  w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o.w) << 16);
+  *(uint2 *)(o_out + row * D + 4 * c) = w;
+  if (lse_out && c == 0) lse_out[row] = lse;
 }
 
 }  // namespace
@@ -87,7 +114,8 @@ hipError_t launch_merge(const float *o_parts, const float *lse_parts, int32_t nu
                         int64_t rows, int32_t head_dim, int32_t num_q_heads, const float *sink,
                         uint16_t *o_out, float *lse_out, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const int64_t rpb = 256 / (head_dim / 4);
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, o_parts, lse_parts,
                        num_parts, rows, num_q_heads, sink, o_out, lse_out);

@@ -151,6 +151,9 @@ def test_merge_validation(lib):
     assert lib.attn_merge_lse(good["o"], good["l"], 65, 10, 128, 4, None, good["out"], None, None) == -7
     assert lib.attn_merge_lse(good["o"], good["l"], 2, -1, 128, 4, None, good["out"], None, None) == -2
     assert lib.attn_merge_lse(good["o"], good["l"], 2, 10, 96, 4, None, good["out"], None, None) == -4
+    # o_parts is read 16 bytes per lane, o_out written 8 bytes per lane
+    assert lib.attn_merge_lse(good["o"] + 8, good["l"], 2, 10, 128, 4, None, good["out"], None, None) == -5
+    assert lib.attn_merge_lse(good["o"], good["l"], 2, 10, 128, 4, None, good["out"] + 4, None, None) == -5
 
 
 def test_gather_validation(lib):
