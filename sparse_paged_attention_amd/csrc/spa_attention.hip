@@ -319,7 +319,7 @@ void attn_fwd_kernel(const Params p) {
     // so that their loads overlap the metadata loads.  The list entries are
     // taken up to the slice's capacity; the page stage uses only the valid
     // ones.
-    constexpr int kSpec = 5;                 // tiles 1..kSpec of the stream at most
+    constexpr int kSpec = 6;                 // tiles 1..kSpec of the stream at most
     int32_t nspec = 0;
     if (!loader && p.topk > 0 && jid(0).valid) {   // (a stream may have no job at all)
       const JobId j0 = jid(0);
@@ -615,6 +615,88 @@ void attn_fwd_kernel(const Params p) {
     Cur cp = cv, cl = cv;
     if (loader) {
       advance(cv);
+    } else if (njobs == 0) {
+      // a stream with no job: its stages pad
+      for (int n = 0; n < 7; ++n) advance(cp);
+      for (int n = 0; n < 10; ++n) advance(cl);
+      for (int n = 0; n < 4; ++n) advance(cv);
+    } else if (njobs == 1 || cv.j.nkv >= 6) {
+      // Tiles 1-6 belong to job 0 (or lie past the last job), and the early
+      // loads hold the lists of its compressed ones: their rows are resolved
+      // lane-parallel, 64 entries (two tiles) per pass, with the page-table
+      // loads of all three passes in flight together.  Same results as the
+      // per-tile stages below.
+      wait_vmcnt<0>();   // the early list loads
+      const Job &j0 = cv.j;
+      int32_t xr[3], pr[3];
+#pragma unroll
+      for (int it = 0; it < 3; ++it) {
+        const int32_t v = 2 * it + 1 + (lane >> 5);   // tile (stream index) of this lane's entry
+        const int32_t row = lane & 31;
+        int32_t xv = -1;
+        const int32_t *src = nullptr;
+        if (v <= j0.nkv) {
+          const bool cmp = v - 1 < j0.nct;
+          if (cmp) {
+            const int32_t idx = (v - 1) * kTile + row;
+            if (idx < j0.ncr) {
+              if (p.topk > 0) {
+                const int32_t le = sm.lst[v % kXRing][row];
+                if (le >= 0 && le < j0.nc) xv = le;
+                else errbits |= kErrCmpId;
+              } else {
+                xv = j0.cs + idx;
+              }
+            }
+          } else {
+            const int32_t idx = (v - 1 - j0.nct) * kTile + row;
+            if (idx < j0.nwr) xv = j0.wb + idx;
+          }
+          if (xv >= 0) {
+            const int32_t col = pow2 ? (xv >> p.page_shift) : xv / P;
+            if (col < (cmp ? cmp_st : raw_st)) {
+              src = cmp ? cmp_pt + j0.cpt + col : raw_pt + j0.rpt + col;
+            } else {
+              errbits |= kErrPage;
+              xv = -1;
+            }
+          }
+        }
+        xr[it] = xv;
+        pr[it] = src != nullptr ? *src : 0;
+      }
+#pragma unroll
+      for (int it = 0; it < 3; ++it) {
+        const int32_t v = 2 * it + 1 + (lane >> 5);
+        const int32_t row = lane & 31;
+        sm.xid[v % kXRing][row] = xr[it];
+        sm.pg[v % kXRing][row] = pr[it];
+        // pool rows of tiles 1-3 (tile 0 is a Q tile)
+        if (it < 2) {
+          int64_t er = -1;
+          if (xr[it] >= 0 && v <= j0.nkv) {
+            const bool cmp = v - 1 < j0.nct;
+            if (pr[it] >= 0 && (int64_t)pr[it] < (cmp ? cmp_np : raw_np)) {
+              const int32_t off = pow2 ? (xr[it] & (P - 1)) : xr[it] - (xr[it] / P) * P;
+              er = ((int64_t)pr[it] * P + off) * p.hkv + j0.g;
+            } else {
+              errbits |= kErrPage;
+            }
+          }
+          const uint64_t m = __ballot(er >= 0);
+          if (v <= 3) sm.erow[v % kRing][row] = er;
+          if (lane == 0) sm.emask[(2 * it + 1) % kRing] = (uint32_t)m;
+          if (lane == 0 && it == 0) sm.emask[2 % kRing] = (uint32_t)(m >> 32);
+        }
+      }
+      for (int n = 0; n < 7; ++n) advance(cp);
+      for (int n = 0; n < 7; ++n) advance(cl);
+      for (int n = 0; n < 3; ++n) {
+        stage_list(cl, false);
+        advance(cl);
+      }
+      for (int n = 0; n < 4; ++n) advance(cv);
+      wait_vmcnt<0>();
     } else {
       wait_vmcnt<0>();   // the early list loads land before any stage reuses their slots
       for (int n = 0; n < 7; ++n) {
@@ -642,14 +724,14 @@ void attn_fwd_kernel(const Params p) {
     // every stream takes as many steps as the longest (a finished one pads)
     if (NS > 1) T = max(sm_all[0].ntiles, sm_all[NS - 1].ntiles);
     if (loader) {
-      load_step(cv);
-      load_step(cv);
-      wait_vmcnt<2 * C::kLoadOps>();   // tile 0 (its side)
+      load_step(cv);                   // tile 1; tile 2 waits for step 0 (the Q tile's short step)
+      wait_vmcnt<C::kLoadOps>();       // tile 0 (its side)
     }
     for (int t = 0; t < T; ++t) {
       block_sync();   // barrier t
       if (FP8 && (sm.desc[t % kRing].y & kTileWiden)) block_sync();   // the compute waves widen tile t
       if (loader) {
+        if (t == 0) load_step(cv);
         load_step(cv);
         wait_vmcnt<2 * C::kLoadOps>();
       } else {
