@@ -205,7 +205,7 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
   if (a->num_splits > 1) {
     e = spa::launch_merge(p.part_o, p.part_lse, a->num_splits, (int64_t)a->num_queries * a->num_q_heads,
-                          a->head_dim, a->num_q_heads, a->sink, p.o, a->lse, s);
+                          a->head_dim, a->num_q_heads, a->sink, p.o, a->lse, p.group, s);
     if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
   }
   return ok();
@@ -240,7 +240,7 @@ spa_status attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t 
   if (!aligned16(o_parts)) return fail(SPA_ERR_ALIGN, "o_parts must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(o_out) & 7u) != 0) return fail(SPA_ERR_ALIGN, "o_out must be 8-byte aligned");
   hipError_t e = spa::launch_merge(o_parts, lse_parts, num_parts, rows, head_dim, num_q_heads, sink,
-                                   static_cast<uint16_t *>(o_out), lse_out, static_cast<hipStream_t>(stream));
+                                   static_cast<uint16_t *>(o_out), lse_out, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -42,9 +42,12 @@ struct Params {
 };
 
 hipError_t launch_attention(const Params &p, hipStream_t stream);
+// unit_rows > 0: rows come in units of unit_rows consecutive rows (the query
+// heads of one (query, KV head) pair), unit u's partials written on XCD
+// u mod 8; the merge then reads each unit on that XCD.  0: plain order.
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int32_t num_parts,
                         int64_t rows, int32_t head_dim, int32_t num_q_heads, const float *sink,
-                        uint16_t *o_out, float *lse_out, hipStream_t stream);
+                        uint16_t *o_out, float *lse_out, int32_t unit_rows, hipStream_t stream);
 hipError_t launch_gather(const Params &p, int32_t cap, int64_t *rows_out, int32_t *counts_out,
                          hipStream_t stream);
 

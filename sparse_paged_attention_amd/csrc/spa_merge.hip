@@ -26,11 +26,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ o_
                                                     int32_t S, int64_t rows, int32_t hq,
                                                     const float *__restrict__ sink,
                                                     uint16_t *__restrict__ o_out,
-                                                    float *__restrict__ lse_out) {
+                                                    float *__restrict__ lse_out, int32_t unit_rows) {
   constexpr int LPR = D / 4;          // lanes per row
   constexpr int RPB = 256 / LPR;      // rows per block
   const int c = threadIdx.x % LPR;    // this lane's float4 of the row
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  int64_t row;
+  if (unit_rows > 0) {
+    // Rows come in units of unit_rows (the heads of one query and KV head);
+    // block b takes a piece of a unit u with u = b (mod 8), so that it runs
+    // on the XCD whose L2 holds the partials the attention kernel wrote for
+    // u.
+    const int32_t bpu = (unit_rows + RPB - 1) / RPB;
+    const int64_t i = blockIdx.x >> 3;
+    const int64_t j = i / bpu;
+    const int32_t r = (int32_t)(i - j * bpu) * RPB + (int32_t)(threadIdx.x / LPR);
+    const int64_t u = (int64_t)(blockIdx.x & 7) + 8 * j;
+    if (u * unit_rows >= rows || r >= unit_rows) return;
+    row = u * unit_rows + r;
+  } else {
+    row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  }
   if (row >= rows) return;
   const float sk = sink ? sink[row % hq] : -INFINITY;
   float M = sk;
@@ -112,16 +127,23 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ o_
 
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int32_t num_parts,
                         int64_t rows, int32_t head_dim, int32_t num_q_heads, const float *sink,
-                        uint16_t *o_out, float *lse_out, hipStream_t stream) {
+                        uint16_t *o_out, float *lse_out, int32_t unit_rows, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const int64_t rpb = 256 / (head_dim / 4);
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+  int64_t blocks = (rows + rpb - 1) / rpb;
+  if (unit_rows > 0) {
+    if (rows % unit_rows != 0) return hipErrorInvalidValue;
+    const int64_t units = rows / unit_rows;
+    blocks = 8 * ((units + 7) / 8) * ((unit_rows + rpb - 1) / rpb);
+  }
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, o_parts, lse_parts,
-                       num_parts, rows, num_q_heads, sink, o_out, lse_out);
+                       num_parts, rows, num_q_heads, sink, o_out, lse_out, unit_rows);
   else
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, o_parts, lse_parts,
-                       num_parts, rows, num_q_heads, sink, o_out, lse_out);
+                       num_parts, rows, num_q_heads, sink, o_out, lse_out, unit_rows);
   return hipGetLastError();
 }
 
