@@ -29,29 +29,26 @@
 // consecutive workgroups, so the jobs of one unit share that XCD's L2.  This
 // affects speed only, never results.
 //
-// One tile stream per workgroup.  The workgroup's jobs form one stream of
-// 32-row tiles: per job a Q tile (its query's rows for the head block) and
-// then its KV tiles (selected compressed rows, then the window; an empty set
-// gets one fully masked tile).  A producer wave (the last wave) runs the
-// stream through two rings of 4 LDS slots, one for K and one for V (a Q tile
-// puts heads 0-31 in its K slot and 32-63 in its V slot), with direct
-// global->LDS loads (global_load_lds_dwordx4 / _dword: no VGPR staging), and
-// translates rows ahead of those loads in two stages that are direct loads
-// into small LDS rings as well.  Step t of the stream issues K of tile t+4,
-// V of tile t+3, the page-table entries of tile t+7 and the list entries of
-// tile t+10.  Every step issues the same number of loads (padding loads read
-// a static zero row into a scratch area), so one vmcnt immediate tracks
-// everything: the data of a step's loads is complete three steps later,
-// which is when the next stage (or the compute waves) reads it.  The per-job
-// metadata is computed once, up front, one job per producer lane.
-//
-// Compute waves.  Barrier t hands K of tile t+1 and V of tile t over (the
-// producer waits for them first); in step t the compute waves take the
-// scores of tile t+1 and the softmax and PV product of tile t, and the
-// producer refills the K slot of tile t and the V slot of tile t-1.  A Q
-// tile is copied into the Q fragments before the scores of its job's first
-// KV tile; after a job's last KV tile the epilogue writes its output and the
-// state is reset for the next job.
+// Job streams.  A workgroup runs NS streams (NS = 2 for 64-head bf16 jobs,
+// else 1); job k of the workgroup goes to stream k % NS.  A stream is a
+// sequence of 32-row tiles: per job a Q tile (its query's rows for the head
+// block) and then its KV tiles (selected compressed rows, then the window;
+// an empty set gets one fully masked tile).  Each stream has its compute
+// waves, a K load wave, a V load wave and a translation wave; the streams
+// share the workgroup's barriers, one per step.  Step t of a stream (after
+// barrier t): the compute waves take tile t (scores, softmax, PV product;
+// a Q tile is copied into the Q fragments); the load waves issue the K and
+// V sides of tile t+3 into rings of 4 LDS slots with direct global->LDS
+// loads (global_load_lds_dwordx4: no VGPR staging; a Q tile puts heads 0-31
+// in its K slot and 32-63 in its V slot); the translation wave forms the
+// pool row of every row of tile t+4 and loads the page-table entries of tile
+// t+7 and the list entries of tile t+10 into small LDS rings, with direct
+// loads as well.  Every helper wave issues the same number of loads each
+// step (padding loads read a static zero row into a scratch area), so one
+// vmcnt immediate tracks everything: before barrier t+1 each waits for its
+// loads of steps <= t-2.  The per-job metadata is computed once, up front,
+// one job per helper lane.  After a job's last KV tile the epilogue writes
+// its output and the state is reset for the next job.
 //
 // Softmax runs in the log2 domain (scores pre-multiplied by scale*log2 e,
 // sink by log2 e) with v_exp_f32; with one slice the running max starts at
@@ -90,7 +87,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 constexpr int kTile = 32;      // KV rows per tile
 constexpr int kRing = 4;       // LDS tile slots
 constexpr int kXRing = 8;      // translation ring slots (list, page-table and id entries)
-constexpr int kStages = 2;     // translation loads per step (page table, list)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // The running max used for the exponentials moves only when a tile's max
