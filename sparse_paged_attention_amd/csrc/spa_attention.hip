@@ -34,16 +34,16 @@
 // sequence of 32-row tiles: per job a Q tile (its query's rows for the head
 // block) and then its KV tiles (selected compressed rows, then the window;
 // an empty set gets one fully masked tile).  Each stream has its compute
-// waves, a K load wave, a V load wave and a translation wave; the streams
-// share the workgroup's barriers, one per step.  Step t of a stream (after
+// waves, a K load wave, a V load wave, a translation wave and a row wave;
+// the streams share the workgroup's barriers, one per step.  Step t of a stream (after
 // barrier t): the compute waves take tile t (scores, softmax, PV product;
 // a Q tile is copied into the Q fragments); the load waves issue the K and
 // V sides of tile t+3 into rings of 4 LDS slots with direct global->LDS
 // loads (global_load_lds_dwordx4: no VGPR staging; a Q tile puts heads 0-31
-// in its K slot and 32-63 in its V slot); the translation wave forms the
-// pool row of every row of tile t+4 and loads the page-table entries of tile
-// t+7 and the list entries of tile t+10 into small LDS rings, with direct
-// loads as well.  Every helper wave issues the same number of loads each
+// in its K slot and 32-63 in its V slot); the row wave forms the pool row
+// of every row of tile t+4; the translation wave loads the page-table
+// entries of tile t+7 and the list entries of tile t+10 into small LDS
+// rings, with direct loads as well.  Every helper wave issues the same number of loads each
 // step (padding loads read a static zero row into a scratch area), so one
 // vmcnt immediate tracks everything: before barrier t+1 each waits for its
 // loads of steps <= t-2.  The per-job metadata is computed once, up front,
@@ -215,7 +215,7 @@ template <int D, int NH, bool FP8>
 struct Cfg {
   static constexpr int NC = NH;                        // compute waves
   static constexpr int kThreads = NC * 64;             // compute threads
-  static constexpr int kBlock = kThreads + 192;        // + two load waves (K, V) and the translation wave
+  static constexpr int kBlock = kThreads + 256;        // + two load waves (K, V), the translation wave and the row wave
   static constexpr int kRowB = 2 * D;                  // bf16 row bytes
   static constexpr int kChunks = kRowB / 16;           // 16-byte chunks per row
   static constexpr int kTileB = kTile * kRowB;         // one K (or V) tile, bytes
@@ -251,7 +251,7 @@ struct Smem {
 };
 
 template <int D, int NH, int NS, bool FP8>
-__global__ __launch_bounds__(NS * (NH + 3) * 64) __attribute__((amdgpu_waves_per_eu(3)))  // <= 168 VGPRs
+__global__ __launch_bounds__(NS * (NH + 4) * 64) __attribute__((amdgpu_waves_per_eu(3)))  // <= 168 VGPRs
 void attn_fwd_kernel(const Params p) {
   using C = Cfg<D, NH, FP8>;
   static_assert(NS == 1 || NS == 2, "one or two streams per workgroup");
@@ -270,30 +270,33 @@ void attn_fwd_kernel(const Params p) {
   const int S = p.num_splits;
   // NS independent streams (job sequences) share the workgroup and its
   // barriers: waves [0, NS*NC) compute (stream wave / NC), then the K and
-  // V load waves of each stream, then each stream's translation wave.  A
-  // workgroup's waves 0-3 sit on four different SIMDs and every further
-  // four on the same four, so with NS = 2 and NC = 2 every SIMD runs one
-  // compute wave and one load wave: a SIMD's wave issues its loads into
-  // LDS at a bounded rate, which the load waves then share evenly.
+  // V load waves of each stream, then each stream's translation wave, then
+  // each stream's row wave.  A workgroup's waves 0-3 sit on four different
+  // SIMDs and every further four on the same four, so with NS = 2 and
+  // NC = 2 every SIMD runs one compute wave, one load wave and one of the
+  // translation and row waves: a SIMD's wave issues its loads into LDS at a
+  // bounded rate, which the load waves then share evenly.
   constexpr int NCW = NS * C::NC;
   const bool helper = wave >= NCW;
   const int hidx = wave - NCW;                 // helper index
-  const int strm = !helper ? wave / C::NC : hidx < 2 * NS ? hidx >> 1 : hidx - 2 * NS;
+  const int strm = !helper ? wave / C::NC : hidx < 2 * NS ? hidx >> 1 : hidx < 3 * NS ? hidx - 2 * NS : hidx - 3 * NS;
   Smem<D, NH, FP8> &sm = sm_all[strm];
   // stream strm's k-th job is the workgroup's job NS*k + strm
   auto jid = [&](int32_t k) { return job_id(p, x, y, Gx, NS * k + strm); };
 
   // =================================================================
-  // Load wave (K, V and Q tiles) and translation wave (page-table and
-  // list entries)
+  // Load waves (K, V and Q tiles), translation wave (page-table and list
+  // entries) and row wave (pool rows)
   // =================================================================
   if (helper) {
     // the K load wave issues the K side of every tile (K rows, Q heads
     // 0-31) and its descriptor, the V load wave the V side (V rows, Q heads
-    // 32-63), and the translation wave the list and page-table entries and
-    // the pool row of every tile row
+    // 32-63), the translation wave the list and page-table entries and the
+    // row wave the pool row of every tile row
     const bool loader = hidx < 2 * NS;
     const bool vload = loader && (hidx & 1) != 0;
+    const bool roww = hidx >= 3 * NS;        // the row wave: pool rows of every tile
+    const bool xlat = !loader && !roww;      // the translation wave: list and page-table entries
     const int64_t raw_np = in_sgpr(p.raw_pages), cmp_np = in_sgpr(p.cmp_pages);
     const int32_t raw_st = in_sgpr(p.raw_pt_stride), cmp_st = in_sgpr(p.cmp_pt_stride);
     const int32_t *const raw_pt = in_sgpr(p.raw_pt), *const cmp_pt = in_sgpr(p.cmp_pt);
@@ -317,7 +320,7 @@ void attn_fwd_kernel(const Params p) {
     // ones.
     constexpr int kSpec = 6;                 // tiles 1..kSpec of the stream at most
     int32_t nspec = 0;
-    if (!loader && p.topk > 0 && jid(0).valid) {   // (a stream may have no job at all)
+    if (xlat && p.topk > 0 && jid(0).valid) {   // (a stream may have no job at all)
       const JobId j0 = jid(0);
       const int cper = round_up((p.topk + S - 1) / S, kTile);
       const int cs0 = min(p.topk, j0.split * cper);
@@ -437,7 +440,7 @@ void attn_fwd_kernel(const Params p) {
     };
     const bool pow2 = p.page_shift >= 0;
     const int32_t P = p.page_size;
-    // ---------------- translation wave stages
+    // ---------------- translation and row wave stages
     // -- list stage: list entries of a compressed KV tile of a top-k layer
     // (pad = false: a tile with nothing to load issues no padding load;
     // only where the wave then waits for all of its loads)
@@ -511,7 +514,7 @@ void attn_fwd_kernel(const Params p) {
     };
 
     // ---------------- tile loads
-    // -- one side of a tile (K: load wave, V: translation wave).  The pool
+    // -- one side of a tile (K or V load wave).  The pool
     // rows each lane loads are read first, in one batch of LDS reads (a
     // load's asm orders every later LDS access behind it) ...
     struct Rows {
@@ -595,9 +598,9 @@ void attn_fwd_kernel(const Params p) {
     };
 
     // ---- the stream.  Step t (after barrier t): the load waves issue the K
-    // and V sides of tile t+3; the translation wave forms the pool rows of
-    // tile t+4 and issues the page entries of tile t+7 and the list entries
-    // of tile t+10.  Each wave issues a fixed number of loads per step and,
+    // and V sides of tile t+3; the row wave forms the pool rows of tile t+4
+    // and the translation wave issues the page entries of tile t+7 and the
+    // list entries of tile t+10.  Each wave issues a fixed number of loads per step and,
     // before barrier t+1, waits for its own loads of steps <= t-2: tile t+1
     // for the compute waves, and every stage's input two steps before it is
     // read.
@@ -605,12 +608,15 @@ void attn_fwd_kernel(const Params p) {
     // Priming, before barrier 0: the translation wave issues the lists of
     // tiles 0-6 (those not loaded early), then their page entries and the
     // lists of tiles 7-9 (each phase complete before the next), and forms
-    // the pool rows of tiles 0-3; after a barrier the load waves issue tiles
+    // the pool rows of tiles 0-3 (the row wave starts at tile 4); after a
+    // barrier the load waves issue tiles
     // 1 and 2 (tile 0, job 0's Q tile, was issued at the start).
-    Cur cv{0, 0, 0, job(0)};   // load waves: tiles; translation wave: rows, page entries, lists
+    Cur cv{0, 0, 0, job(0)};   // load waves: tiles; row wave: rows; translation wave: rows (priming), page entries, lists
     Cur cp = cv, cl = cv;
     if (loader) {
       advance(cv);
+    } else if (roww) {
+      for (int n = 0; n < 4; ++n) advance(cv);
     } else if (njobs == 0) {
       // a stream with no job: its stages pad
       for (int n = 0; n < 7; ++n) advance(cp);
@@ -730,14 +736,11 @@ void attn_fwd_kernel(const Params p) {
         if (t == 0) load_step(cv);
         load_step(cv);
         wait_vmcnt<2 * C::kLoadOps>();
-      } else {
-        // every LDS read of the step first, in one batch
-        const int32_t xv = sm.xid[cv.u % kXRing][lane & 31];
-        const int32_t pgv = sm.pg[cv.u % kXRing][lane & 31];
-        const int32_t le = list_entry(cp);
-        stage_rows(cv, xv, pgv);
+      } else if (roww) {
+        stage_rows(cv, sm.xid[cv.u % kXRing][lane & 31], sm.pg[cv.u % kXRing][lane & 31]);
         advance(cv);
-        stage_page(cp, le, true);
+      } else {
+        stage_page(cp, list_entry(cp), true);
         advance(cp);
         stage_list(cl, true);
         advance(cl);
