@@ -97,8 +97,16 @@ typedef struct spa_fwd_args {
                               tile: 32 or 64, or 0 = chosen by the library (64
                               when the KV group has more than 32 heads); a
                               tuning knob, the result does not depend on it    */
-  int32_t queries_per_block; /* queries one job serves: 0 or 1 (one query per
-                              job; other values are rejected)                   */
+  int32_t queries_per_block; /* queries one job serves, a tuning knob (the
+                              result does not depend on it): 1 = one query per
+                              job; 2 = query pairs (prefill only: two queries
+                              stream the union of their KV sets through shared
+                              tiles; needs bf16 caches, head_dim 128,
+                              num_splits 1, topk > 0 or ratio 0, and
+                              2 * (topk + window) <= 1280, else
+                              SPA_ERR_UNSUPPORTED); 0 = library choice (pairs
+                              for a prefill that fits them unless
+                              heads_per_block is 32, else one query)        */
 
   const void *q;          /* bf16 [Nq, Hq, D]                                    */
   const void *k_raw;      /* bf16 [raw_pages, P, Hkv, D]                         */

@@ -68,8 +68,10 @@ spa_status validate(const spa_fwd_args *a, bool decode, bool need_outputs) {
     return fail(SPA_ERR_SPLITS, "num_splits %d outside [1, %d]", a->num_splits, SPA_MAX_SPLITS);
   if (a->heads_per_block != 0 && a->heads_per_block != 32 && a->heads_per_block != 64)
     return fail(SPA_ERR_UNSUPPORTED, "heads_per_block %d not supported (0, 32 or 64)", a->heads_per_block);
-  if (a->queries_per_block != 0 && a->queries_per_block != 1)
-    return fail(SPA_ERR_UNSUPPORTED, "queries_per_block %d not supported (0 or 1)", a->queries_per_block);
+  if (a->queries_per_block < 0 || a->queries_per_block > 2)
+    return fail(SPA_ERR_UNSUPPORTED, "queries_per_block %d not supported (0, 1 or 2)", a->queries_per_block);
+  if (a->queries_per_block == 2 && decode)
+    return fail(SPA_ERR_UNSUPPORTED, "queries_per_block 2 is a prefill layout");
   {
     const int64_t group = a->num_q_heads / a->num_kv_heads;
     const int64_t jobs = (int64_t)a->num_queries * a->num_kv_heads * a->num_splits * ((group + 31) / 32);
@@ -201,7 +203,17 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
   }
   if (a->num_queries == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = spa::launch_attention(p, s);
+  // Prefill: query pairs share each KV tile when the call fits that kernel
+  // (the library's choice unless the caller asks for 32-head jobs or one
+  // query per job); the result does not depend on the choice.
+  const bool pairs_ok = !decode && spa::prefill_pairs_eligible(p);
+  if (a->queries_per_block == 2 && !pairs_ok)
+    return fail(SPA_ERR_UNSUPPORTED,
+                "queries_per_block 2 needs bf16 caches, head_dim 128, one split, a top-k list or no "
+                "compressed part, and 2 * (topk + window) <= %d", spa::kPairRowsMax);
+  const bool pairs = pairs_ok && (a->queries_per_block == 2 ||
+                                  (a->queries_per_block == 0 && a->heads_per_block != 32));
+  hipError_t e = pairs ? spa::launch_prefill_pairs(p, s) : spa::launch_attention(p, s);
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
   if (a->num_splits > 1) {
     e = spa::launch_merge(p.part_o, p.part_lse, a->num_splits, (int64_t)a->num_queries * a->num_q_heads,

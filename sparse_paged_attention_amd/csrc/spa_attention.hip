@@ -73,119 +73,17 @@
 #include <type_traits>
 
 #include "spa_device.h"
+#include "spa_kernel_util.h"
 
 namespace spa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-
 constexpr int kTile = 32;      // KV rows per tile
 constexpr int kRing = 4;       // LDS tile slots
 constexpr int kXRing = 8;      // translation ring slots (list, page-table and id entries)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-// The running max used for the exponentials moves only when a tile's max
-// exceeds it by more than kTau (log2 units), so P and the sums stay below
-// 2^kTau and the O accumulators are rescaled only on such jumps.  Any
-// reference value gives the same softmax; only the rounding differs.
-constexpr float kTau = 8.f;
 
 // Tile descriptor flags.
 enum : uint32_t { kTileQ = 1, kTileKV = 2, kTileCmp = 4, kTileLast = 8, kTileWiden = 16 };
-
-// A kernel argument held in scalar registers.  Without it, a select between
-// two argument fields (raw or compressed pool, K or V side) can become one
-// vector load from the argument block, and the wait for that load would also
-// drain every tile load in flight.
-template <typename T>
-__device__ __forceinline__ T in_sgpr(T v) {
-  asm volatile("" : "+s"(v));
-  return v;
-}
-
-// Source of the padding loads and of the loads for masked rows.
-__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[256] = {};
-
-// LDS byte offset of a generic pointer into shared memory: the LDS aperture
-// is 4 GiB aligned in the flat address space, so the low 32 bits are the
-// offset (this avoids a checked generic->local address-space cast).
-__device__ __forceinline__ uint32_t lds_offset(const void *p) { return (uint32_t)(uintptr_t)p; }
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved; only these loads use it here
-// One wave-wide direct global->LDS load: lane L's 16 (or 4) bytes from `src`
-// land at lds_dst + 16 L (or 4 L); lds_dst is wave-uniform and goes through
-// M0.  Written as inline asm so that the compiler does not guard every later
-// LDS read with a wait for all outstanding loads; completion is tracked
-// explicitly with wait_vmcnt<>.  The instructions have no destination
-// registers.
-__device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_offset(lds_dst));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void *src, void *lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_offset(lds_dst));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(src), "s"(lds)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier that waits only for this wave's LDS operations.  The
-// HIP __syncthreads() adds a workgroup release fence, which on gfx950 also
-// waits for every outstanding global load and would drain the LDS ring;
-// global->LDS loads are instead completed explicitly with wait_vmcnt<>.
-// The "memory" clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// max(v, v of lane ^ 32): v_permlane32_swap exchanges the upper half of its
-// first operand with the lower half of its second, so with both holding v
-// each lane ends up with its own value in one register and its partner's in
-// the other.  (Written as asm: the builtin is folded wrongly when both
-// operands are the same value.)
-__device__ __forceinline__ float max_lane_pair(float v) {
-  float a = v, b = v;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-  return fmaxf(a, b);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16_hi(float lo, float hi) {
-  // exact narrowing for values that are bf16 already (widened e4m3 codes)
-  return (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xFFFF0000u);
-}
-
-__device__ __forceinline__ int round_up(int x, int m) { return (x + m - 1) / m * m; }
-
-__device__ __forceinline__ uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-
-// LDS layout of a tile: row r (2D bytes) holds logical 16-byte chunk c at
-// physical chunk c ^ swz(r).  For D 128 (16 chunks) the permutation makes
-// both access patterns conflict-free: the K (and Q) reads, where 16 lanes
-// read one chunk of 16 consecutive rows, and the V transpose reads, where 16
-// lanes read 2 adjacent chunks of 4 consecutive rows.  For D 64 (8 chunks,
-// two rows per bank sweep) the K reads are conflict-free.
-template <int CH>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (CH == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
-  else return (r >> 1) & 7;
-}
 
 // ---------------------------------------------------------------- job lists
 // Job k of workgroup (XCD x, index y of Gx on that XCD): local index

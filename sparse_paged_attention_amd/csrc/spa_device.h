@@ -32,17 +32,15 @@ __device__ __forceinline__ void flag_error(const Params &p, int32_t bits) {
   if (p.err_flag) atomicOr(p.err_flag, bits);
 }
 
-__device__ __forceinline__ QueryKV query_kv(const Params &p, int32_t i) {
+// KV-set counts of a query at position t of sequence b (b in range), with
+// len = seq_lens[b] and cnt its list count (top-k layers).  `report` raises
+// the error bits; without it the counts are also computed for t >= len
+// (a caller that does not know len yet passes INT32_MAX).
+__device__ __forceinline__ QueryKV query_kv_of(const Params &p, int32_t b, int32_t t, int32_t len,
+                                               int32_t cnt, bool report) {
   QueryKV kv{0, 0, 0, 0, 0, 0};
-  const int32_t b = p.query_seq ? p.query_seq[i] : i;
-  if (b < 0 || b >= p.num_seqs) {
-    flag_error(p, kErrQuery);
-    return kv;
-  }
-  const int32_t len = p.seq_lens[b];
-  const int32_t t = p.query_pos ? p.query_pos[i] : len - 1;
   if (t < 0 || t >= len) {
-    flag_error(p, kErrQuery);
+    if (report) flag_error(p, kErrQuery);
     return kv;
   }
   kv.b = b;
@@ -51,9 +49,9 @@ __device__ __forceinline__ QueryKV query_kv(const Params &p, int32_t i) {
   kv.win_len = t - kv.win_lo + 1;
   kv.n_c = p.ratio > 0 ? (t + 1) / p.ratio : 0;
   if (p.ratio > 0 && p.topk > 0) {
-    int32_t c = p.cmp_cnt[i];
+    int32_t c = cnt;
     if (c < 0 || c > p.topk) {
-      flag_error(p, kErrCount);
+      if (report) flag_error(p, kErrCount);
       c = c < 0 ? 0 : p.topk;
     }
     kv.n_sel = c;
@@ -61,6 +59,17 @@ __device__ __forceinline__ QueryKV query_kv(const Params &p, int32_t i) {
     kv.n_sel = p.ratio > 0 ? kv.n_c : 0;
   }
   return kv;
+}
+
+__device__ __forceinline__ QueryKV query_kv(const Params &p, int32_t i) {
+  const int32_t b = p.query_seq ? p.query_seq[i] : i;
+  if (b < 0 || b >= p.num_seqs) {
+    flag_error(p, kErrQuery);
+    return QueryKV{0, 0, 0, 0, 0, 0};
+  }
+  const int32_t len = p.seq_lens[b];
+  const int32_t t = p.query_pos ? p.query_pos[i] : len - 1;
+  return query_kv_of(p, b, t, len, (p.ratio > 0 && p.topk > 0) ? p.cmp_cnt[i] : 0, true);
 }
 
 // A listed compressed id is usable only if it names a complete group.

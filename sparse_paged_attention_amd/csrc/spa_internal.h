@@ -42,6 +42,15 @@ struct Params {
 };
 
 hipError_t launch_attention(const Params &p, hipStream_t stream);
+
+// Prefill with query pairs sharing KV tiles (spa_prefill.hip): bf16 caches,
+// D 128, one slice, a top-k list (or no compressed part) and at most
+// kPairRowsMax rows in the union of a pair's KV sets, which holds whenever
+// 2 * (topk + window) <= kPairRowsMax.
+constexpr int kPairRowsMax = 1280;
+constexpr int kPairStages = 2;      // LDS stages of the tile pipeline
+bool prefill_pairs_eligible(const Params &p);
+hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream);
 // unit_rows > 0: rows come in units of unit_rows consecutive rows (the query
 // heads of one (query, KV head) pair), unit u's partials written on XCD
 // u mod 8; the merge then reads each unit on that XCD.  0: plain order.

@@ -130,6 +130,29 @@ def test_prefill_needs_positions(lib):
     assert lib.attn_fwd_prefill(ctypes.byref(a), None) == -9
 
 
+PAIR_FAULTS = [
+    ("fp8_cache", lambda a: (setattr(a, "cmp_dtype", _lib.SPA_FP8_E4M3_OCP), setattr(a, "k_cmp_scale", 0x30000000),
+                             setattr(a, "v_cmp_scale", 0x30001000))),
+    ("head_dim_64", lambda a: setattr(a, "head_dim", 64)),
+    ("rows_beyond_capacity", lambda a: setattr(a, "topk", 700)),
+    ("all_groups_layer", lambda a: setattr(a, "topk", 0)),
+]
+
+
+@pytest.mark.parametrize("name,mutate", PAIR_FAULTS, ids=[f[0] for f in PAIR_FAULTS])
+def test_prefill_pairs_rejected_when_ineligible(lib, name, mutate):
+    """queries_per_block 2 asks for the pair kernel: a call it cannot serve
+    is refused before any HIP call."""
+    a = _good_args()
+    a.query_seq = 0x20000000
+    a.query_pos = 0x20001000
+    a.queries_per_block = 2
+    mutate(a)
+    st = lib.attn_fwd_prefill(ctypes.byref(a), None)
+    assert st == -4, (name, st, lib.attn_last_error())
+    assert b"queries_per_block 2" in lib.attn_last_error()
+
+
 def test_workspace_rules(lib):
     a = _good_args()
     a.num_splits = 4
