@@ -30,7 +30,20 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the sources whose change invalidates counter-measured traffic
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
-                  for f in ("spa_attention.hip", "spa_device.h", "spa_internal.h", "spa_api.cpp")]
+                  for f in ("spa_attention.hip", "spa_prefill.hip", "spa_kernel_util.h", "spa_device.h",
+                            "spa_internal.h", "spa_api.cpp")]
+PAIR_ROWS_MAX = 1280           # rows a query pair's union can hold in the prefill pair kernel
+
+
+def attention_kernel(p, splits, hpb, qpb):
+    """Name of the attention kernel the library launches for this call: the
+    prefill pair kernel when the call fits it and the library's choice (or
+    the caller's) is query pairs, else the one-query-per-job kernel.  Mirrors
+    the selection in spa_api.cpp."""
+    pairs_ok = (p.mode == "prefill" and p.head_dim == 128 and not p.cmp_fp8 and splits == 1
+                and (p.ratio == 0 or p.topk > 0) and 2 * (p.topk + p.window) <= PAIR_ROWS_MAX)
+    pairs = pairs_ok and (qpb == 2 or (qpb == 0 and hpb != 32))
+    return "attn_prefill_pair_kernel" if pairs else "attn_fwd_kernel"
 
 
 def kernel_source_hash():
@@ -291,7 +304,7 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None   # filled in below from the committed counter runs, if they match
-    roof["kernel"] = "attn_fwd_kernel"
+    roof["kernel"] = attention_kernel(p, splits, hpb, qpb)
     roof["kernel_ms"] = kernel_ms
     roof["kernel_ms_how"] = ("graph replay of the step minus graph replay of the merge alone" if merge_ms > 0
                              else "graph replay of the step (one kernel)")

@@ -14,26 +14,31 @@
 // the pair, heads 32w .. 32w+31) masks the rows its own query does not
 // select.  A tile of K and V then feeds 128 (query, head) columns instead of
 // 64, and the workgroup holds only compute waves: every wave issues a
-// quarter of each tile's direct global->LDS loads and then runs its MFMAs,
-// so three workgroups (twelve compute waves) share a CU.
+// quarter of each tile's direct global->LDS loads and then runs its MFMAs;
+// two workgroups (eight compute waves) share a CU.
 //
 // Setup (per workgroup, before the tile loop):
-//   * both queries' KV sets (query_kv);
-//   * union mode, when both queries are in one sequence, their windows touch
-//     and their complete groups fit the bitmaps: each query's selected
-//     groups become a bitmap in LDS (a listed id that is not a complete
-//     group of that query is flagged and left out), the OR of the two is
-//     compacted into the ascending list of union groups, and the window rows
-//     are the positions from the lower window start to the higher query
-//     position;
-//   * otherwise (pair across sequences, far-apart positions, the last query
-//     of an odd count) concatenation mode: query 0's rows, then query 1's,
-//     each in canonical order and selected by its own query only;
-//   * every union row is translated through its page table once, to a
-//     64-bit pool row (row * Hkv + g) or -1 when masked (flagged), with a
-//     byte of flags: bit q = selected by query q, bit 7 = compressed row.
+//   * the loads that need nothing else are issued together: the Q fragments,
+//     both queries' metadata and both whole list rows; the KV sets are first
+//     computed without the check of the positions against seq_lens, whose
+//     loads are issued with the page-table slices below;
+//   * union mode, when both queries are in one sequence, their windows touch,
+//     their complete groups fit the bitmaps and the page-table columns they
+//     need fit the LDS slices: the page-table slices are loaded into LDS,
+//     each query's selected groups become a bitmap (a listed id that is not
+//     a complete group of that query is flagged and left out), the OR of the
+//     two is ranked word by word, and every union group and every window
+//     position (from the lower window start to the higher query position)
+//     is translated through the slices;
+//   * otherwise (pair across sequences, far-apart positions, a list that
+//     names a group twice) concatenation mode: query 0's rows, then query
+//     1's, each in canonical order and selected by its own query only, with
+//     the page-table entries read row by row;
+//   * the result is one list of 64-bit pool rows (row * Hkv + g, bit 62 for
+//     a compressed row, -1 when masked) padded to whole tiles, with a byte
+//     per row: bit q = selected by query q.
 // The tile loop then needs no translation: tile j is rows 32j .. 32j+31 of
-// that list, masked rows and rows past the end load a static zero row.
+// that list; masked rows load a static zero row.
 //
 // Pipeline: NST LDS stages of one K and one V tile, one barrier per step.
 // Step j waits for tile j (each wave for its own loads, then the barrier),
@@ -88,6 +93,7 @@ struct PairSmem {
   alignas(16) int64_t row[kUMax];
   uint8_t flg[kUMax];                      // bit q: selected by query q
   int32_t wsum[4];
+  int32_t dup;                             // a list names a group twice
 };
 static_assert(sizeof(PairSmem<2>::u) == 2 * 2 * kPTileB, "setup arrays fit the tile stages");
 static_assert(kBmWords == 4 * kThreads, "four bitmap words per thread in the rank scan");
@@ -194,10 +200,11 @@ void attn_prefill_pair_kernel(const Params p) {
   const int32_t ncol_c = p.ratio > 0 ? min((ncmax + P - 1) / P, p.cmp_pt_stride) : 0;
   const int32_t col_lo = wlo / P;
   const int32_t ncol_r = nwin > 0 ? max(0, min((wlo + nwin - 1) / P, p.raw_pt_stride - 1) - col_lo + 1) : 0;
-  const bool uni = bok0 && (!has1 || (bok1 && mb1 == mb0)) && touch && ncmax <= 32 * kBmWords &&
+  bool uni = bok0 && (!has1 || (bok1 && mb1 == mb0)) && touch && ncmax <= 32 * kBmWords &&
                    ncol_c + ncol_r <= kPtMax;
   int32_t U = 0;                                      // rows in the union list
 
+  QueryKV kv0{0, 0, 0, 0, 0, 0}, kv1{0, 0, 0, 0, 0, 0};
   if (uni) {
     const int32_t b = mb0;
     // -- page-table slices into LDS (direct loads): compressed columns
@@ -210,13 +217,13 @@ void attn_prefill_pair_kernel(const Params p) {
       dma4(src, &sm.u.s.pt[64 * c]);
     }
     for (int k = tid; k < 2 * kBmWords; k += kThreads) (&sm.u.s.bm[0][0])[k] = 0u;
+    if (tid == 0) sm.dup = 0;
     wait_vmcnt<0>();                                  // slices, lists, Q
     __syncthreads();                                  // slices in, bitmaps cleared
     // -- the KV sets checked against seq_lens (a query past its sequence
     // has an empty set; the error bits are raised once); they are subsets
     // of the provisional ones, so the slices cover them
-    const QueryKV kv0 = query_kv_of(p, mb0, mt0, len0, mc0, tid == 0);
-    QueryKV kv1{0, 0, 0, 0, 0, 0};
+    kv0 = query_kv_of(p, mb0, mt0, len0, mc0, tid == 0);
     if (bok1) kv1 = query_kv_of(p, mb1, mt1, len1, mc1, tid == 0);
     if (has1 && !bok1 && tid == 0) flag_error(p, kErrQuery);
     // -- selected groups: one bitmap per query
@@ -228,12 +235,20 @@ void attn_prefill_pair_kernel(const Params p) {
         const QueryKV &kv = q ? kv1 : kv0;
         if (e - q * topk < kv.n_sel) {
           const int32_t c = ids[it];
-          if (c >= 0 && c < kv.n_c) atomicOr(&sm.u.s.bm[q][c >> 5], 1u << (c & 31));
-          else flag_error(p, kErrCmpId);
+          if (c >= 0 && c < kv.n_c) {
+            if (atomicOr(&sm.u.s.bm[q][c >> 5], 1u << (c & 31)) & (1u << (c & 31))) sm.dup = 1;
+          } else {
+            flag_error(p, kErrCmpId);
+          }
         }
       }
     }
     __syncthreads();
+    // a list that names a group twice counts it twice, as the canonical
+    // order does: such a pair takes the concatenation below
+    uni = sm.dup == 0;
+  }
+  if (uni) {
     // -- rank of every word's first group in the ascending union: thread t
     // sums words 4t .. 4t+3, one scan over the threads
     const int32_t nw = (ncmax + 31) / 32;             // <= kBmWords = 4 * kThreads
@@ -302,9 +317,8 @@ void attn_prefill_pair_kernel(const Params p) {
   } else {
     // -- concatenation: query 0's canonical rows, then query 1's (the
     // metadata is read again: this path is for the odd cases)
-    const QueryKV kv0 = query_kv(p, i0);
-    QueryKV kv1{0, 0, 0, 0, 0, 0};
-    if (has1) kv1 = query_kv(p, i1);
+    kv0 = query_kv(p, i0);
+    kv1 = has1 ? query_kv(p, i1) : QueryKV{0, 0, 0, 0, 0, 0};
     const int32_t U0 = kv0.n_sel + kv0.win_len;
     const int32_t U1 = has1 ? kv1.n_sel + kv1.win_len : 0;
     U = min(U0 + U1, kUMax);

@@ -2,11 +2,12 @@
 sequence streaming the union of their KV sets through shared tiles).
 
 The cases cover both ways a pair's rows are built: the union (same
-sequence, touching windows: bitmaps of the selected groups, OR-compacted)
-and the concatenation (pairs across sequences, far-apart positions, an odd
-last query, groups beyond the bitmaps), plus partial and multiple head
-blocks, empty sets, duplicate queries, disjoint lists at the row capacity,
-and the device-side checks.  Every case is compared with the FP64 oracle
+sequence, touching windows: bitmaps of the selected groups, ranked and
+translated through page-table slices in LDS; also an odd last query) and
+the concatenation (pairs across sequences, far-apart positions, groups
+beyond the bitmaps, a list that names a group twice), plus partial and
+multiple head blocks, empty sets, duplicate queries, disjoint lists at the
+row capacity, and the device-side checks.  Every case is compared with the FP64 oracle
 and, where the one-query-per-job kernel also applies, with it too."""
 import numpy as np
 import pytest
@@ -146,3 +147,22 @@ def test_pairs_deterministic():
     O1, L1, _ = run_hip(p, 1, queries_per_block=2)
     O2, L2, _ = run_hip(p, 1, queries_per_block=2)
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_group_listed_twice_counts_twice():
+    """A list that names a group twice (outside the oracle's input contract,
+    which takes distinct ids) attends to that row twice in the canonical
+    order: the pair leaves the union, whose bitmap would merge the two, for
+    the concatenation, and agrees with the one-query kernel."""
+    p = _prefill("dup_ids", [1000], [(0, t) for t in range(900, 906)], 64, 1, 16, 64, 4, 30)
+    p.cmp_idx[2, 5] = p.cmp_idx[2, 4]
+    p.cmp_idx[3, 0] = p.cmp_idx[3, 7]
+    announce("group listed twice: pairs vs one query per job")
+    O2, L2, _ = run_hip(p, 1, queries_per_block=2)
+    O1, L1, _ = run_hip(p, 1, queries_per_block=1)
+    rep = accept(O2, L2, O1, L1)
+    assert rep.ok, rep
+    # and the duplicate matters: without it the result differs
+    q = _prefill("dup_ids", [1000], [(0, t) for t in range(900, 906)], 64, 1, 16, 64, 4, 30)
+    O0, _, _ = run_hip(q, 1, queries_per_block=2)
+    assert not np.allclose(O0[2], O2[2], atol=1e-3)
