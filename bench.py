@@ -39,11 +39,20 @@ def attention_kernel(p, splits, hpb, qpb):
     """Name of the attention kernel the library launches for this call: the
     prefill pair kernel when the call fits it and the library's choice (or
     the caller's) is query pairs, else the one-query-per-job kernel.  Mirrors
-    the selection in spa_api.cpp."""
+    the selection in spa_api.cpp (the decode-slice kernel for a decode the
+    library sizes itself)."""
     pairs_ok = (p.mode == "prefill" and p.head_dim == 128 and not p.cmp_fp8 and splits == 1
                 and (p.ratio == 0 or p.topk > 0) and 2 * (p.topk + p.window) <= PAIR_ROWS_MAX)
     pairs = pairs_ok and (qpb == 2 or (qpb == 0 and hpb != 32))
-    return "attn_prefill_pair_kernel" if pairs else "attn_fwd_kernel"
+    S = max(splits, 1)
+    cap = 0 if p.ratio == 0 else p.topk if p.topk > 0 else p.cmp_pt.shape[1] * p.page_size
+    slices_ok = (p.mode == "decode" and p.head_dim == 128 and not p.cmp_fp8 and hpb == 0 and qpb == 0
+                 and -(-cap // S) + -(-p.window // S) <= PAIR_ROWS_MAX)
+    if pairs:
+        return "attn_pair_kernel<2, false>"
+    if slices_ok:
+        return "attn_pair_kernel<2, true>"
+    return "attn_fwd_kernel"
 
 
 def kernel_source_hash():
@@ -165,7 +174,7 @@ def parse_args(argv=None):
 
 
 DEFAULTS = {   # (num_splits, heads_per_block, queries_per_block) per workload; 0 = library choice
-    "decode_csa": (4, 64, 1), "decode_hca": (4, 0, 1), "mixed_fp8": (8, 64, 1), "prefill_csa": (1, 0, 0),
+    "decode_csa": (4, 0, 0), "decode_hca": (4, 0, 0), "mixed_fp8": (8, 64, 1), "prefill_csa": (1, 0, 0),
     "tiny": (1, 0, 0),
 }
 

@@ -213,11 +213,19 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
                 "compressed part, and 2 * (topk + window) <= %d", spa::kPairRowsMax);
   const bool pairs = pairs_ok && (a->queries_per_block == 2 ||
                                   (a->queries_per_block == 0 && a->heads_per_block != 32));
-  hipError_t e = pairs ? spa::launch_prefill_pairs(p, s) : spa::launch_attention(p, s);
+  // Decode: one workgroup per query slice and 128 heads, when the call fits
+  // it and the caller leaves both block sizes to the library.
+  const bool slices = decode && a->heads_per_block == 0 && a->queries_per_block == 0 &&
+                      spa::decode_slices_eligible(p);
+  hipError_t e = pairs ? spa::launch_prefill_pairs(p, s)
+                 : slices ? spa::launch_decode_slices(p, s)
+                          : spa::launch_attention(p, s);
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
   if (a->num_splits > 1) {
+    // the job-stream kernel writes each (query, KV head) unit's partials on
+    // one XCD and the merge reads them there; the slice kernel in row order
     e = spa::launch_merge(p.part_o, p.part_lse, a->num_splits, (int64_t)a->num_queries * a->num_q_heads,
-                          a->head_dim, a->num_q_heads, a->sink, p.o, a->lse, p.group, s);
+                          a->head_dim, a->num_q_heads, a->sink, p.o, a->lse, slices ? 0 : p.group, s);
     if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
   }
   return ok();

@@ -48,9 +48,16 @@ hipError_t launch_attention(const Params &p, hipStream_t stream);
 // kPairRowsMax rows in the union of a pair's KV sets, which holds whenever
 // 2 * (topk + window) <= kPairRowsMax.
 constexpr int kPairRowsMax = 1280;
-constexpr int kPairStages = 2;      // LDS stages of the tile pipeline
+constexpr int kPairStages = 2;      // LDS stages of the tile pipeline (prefill pairs)
+constexpr int kDecodeStages = 2;    // the same for decode slices
 bool prefill_pairs_eligible(const Params &p);
 hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream);
+// Decode with one workgroup per (query, KV head, 128-head block, KV slice)
+// (spa_prefill.hip): bf16 caches, D 128, and a slice's rows within
+// kPairRowsMax.  With several slices it writes sink-free partials for the
+// merge (in plain row order).
+bool decode_slices_eligible(const Params &p);
+hipError_t launch_decode_slices(const Params &p, hipStream_t stream);
 // unit_rows > 0: rows come in units of unit_rows consecutive rows (the query
 // heads of one (query, KV head) pair), unit u's partials written on XCD
 // u mod 8; the merge then reads each unit on that XCD.  0: plain order.

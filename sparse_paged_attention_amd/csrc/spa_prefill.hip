@@ -122,36 +122,55 @@ __device__ __forceinline__ int32_t block_excl_scan(int32_t v, int32_t &total, in
   return before + x - v;
 }
 
-template <int NST>
+// DEC = false: a prefill query pair (two queries, 64 heads: wave = query *
+// 2 + head half).  DEC = true: one KV slice of a decode query (one query,
+// 128 heads: wave = head quarter), whose sink-free partial the LSE merge
+// combines when there are several slices.
+template <int NST, bool DEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_prefill_pair_kernel(const Params p) {
+void attn_pair_kernel(const Params p) {
+  static_assert(NST >= 2 && NST <= 4, "two to four LDS stages");
   __shared__ PairSmem<NST> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hi = lane >> 5;
-  const int qw = wave >> 1;                  // this wave's query within the pair
-  const int hw = wave & 1;                   // this wave's 32-head half of the block
+  const int qw = DEC ? 0 : wave >> 1;        // this wave's query within the pair
+  const int32_t S = DEC ? p.num_splits : 1;
 
-  // workgroup -> (pair, KV head, 64-head block); the last pairs (the longest
-  // KV sets in a causal prefill) are started first
-  const int32_t hblocks = (p.group + 63) / 64;
-  const int32_t per_pair = p.hkv * hblocks;
-  const int32_t npairs = (p.num_queries + 1) / 2;
-  const int32_t pr = npairs - 1 - (int32_t)(blockIdx.x / per_pair);
-  const int32_t rem = (int32_t)(blockIdx.x % per_pair);
-  const int32_t g = rem / hblocks;
-  const int32_t hb = rem - g * hblocks;
-  const int32_t i0 = 2 * pr, i1 = 2 * pr + 1;
-  const bool has1 = i1 < p.num_queries;
+  // workgroup -> item.  Pairs: (pair, KV head, 64-head block), the last pairs
+  // (the longest KV sets in a causal prefill) first.  Decode: (query, KV
+  // head, 128-head block, slice).
+  int32_t i0, i1, g, hb, split = 0;
+  if constexpr (DEC) {
+    const int32_t hblocks = (p.group + 127) / 128;
+    const int32_t per_q = p.hkv * hblocks * S;
+    i0 = (int32_t)(blockIdx.x / per_q);
+    const int32_t rem = (int32_t)(blockIdx.x % per_q);
+    split = rem % S;
+    g = rem / S / hblocks;
+    hb = rem / S - g * hblocks;
+    i1 = i0;
+  } else {
+    const int32_t hblocks = (p.group + 63) / 64;
+    const int32_t per_pair = p.hkv * hblocks;
+    const int32_t npairs = (p.num_queries + 1) / 2;
+    const int32_t pr = npairs - 1 - (int32_t)(blockIdx.x / per_pair);
+    const int32_t rem = (int32_t)(blockIdx.x % per_pair);
+    g = rem / hblocks;
+    hb = rem - g * hblocks;
+    i0 = 2 * pr;
+    i1 = 2 * pr + 1;
+  }
+  const bool has1 = !DEC && i1 < p.num_queries;
   const int32_t iq = qw == 0 ? i0 : i1;      // this wave's query
   const bool qvalid = qw == 0 || has1;
 
   // ---- phase A: the loads that need nothing else, issued together: the Q
-  // fragments and sink of this lane's head, both queries' metadata and both
-  // whole list rows (list capacity topk each; entries past a count are not
-  // used)
-  const int hl = hb * 64 + hw * 32 + (lane & 31);   // head within the KV group
+  // fragments and sink of this lane's head, the metadata and the list
+  // entries this item reads (for pairs both whole list rows, capacity topk
+  // each; entries past a count are not used)
+  const int hl = DEC ? hb * 128 + wave * 32 + (lane & 31) : hb * 64 + (wave & 1) * 32 + (lane & 31);
   const bool hvalid0 = qvalid && hl < p.group;       // before the query's own checks
   bf16x8 qf[kD / 16];
   {
@@ -160,232 +179,302 @@ void attn_prefill_pair_kernel(const Params p) {
     for (int kk = 0; kk < kD / 16; ++kk)
       qf[kk] = hvalid0 ? *(const bf16x8 *)(qrow + 16 * kk) : bf16x8{};
   }
-  const float sink = (hvalid0 && p.sink != nullptr) ? p.sink[g * p.group + hl] : -INFINITY;
+  // with several slices the partials are sink-free; the merge adds the sink
+  const float sink = (hvalid0 && p.sink != nullptr && S == 1) ? p.sink[g * p.group + hl] : -INFINITY;
   const int32_t topk = p.topk;                        // 0: no list
-  const int32_t mb0 = p.query_seq[i0], mt0 = p.query_pos[i0];
-  const int32_t mb1 = has1 ? p.query_seq[i1] : -1, mt1 = has1 ? p.query_pos[i1] : -1;
-  const int32_t mc0 = topk > 0 ? p.cmp_cnt[i0] : 0;
-  const int32_t mc1 = (topk > 0 && has1) ? p.cmp_cnt[i1] : 0;
-  int32_t ids[kRowIters];
-#pragma unroll
-  for (int it = 0; it < kRowIters; ++it) {
-    const int e = tid + it * kThreads;
-    const int q = e >= topk ? 1 : 0;
-    ids[it] = (topk > 0 && e < 2 * topk && (q == 0 || has1))
-                  ? p.cmp_idx[(int64_t)(q ? i1 : i0) * topk + (e - q * topk)] : -1;
-  }
-
-  // ---- the pair's KV sets, before the positions are checked against
-  // seq_lens (those loads are issued now and checked after the build)
-  const bool bok0 = mb0 >= 0 && mb0 < p.num_seqs;
-  const bool bok1 = has1 && mb1 >= 0 && mb1 < p.num_seqs;
-  const QueryKV pk0 = bok0 ? query_kv_of(p, mb0, mt0, INT32_MAX, mc0, false) : QueryKV{0, 0, 0, 0, 0, 0};
-  const QueryKV pk1 = bok1 ? query_kv_of(p, mb1, mt1, INT32_MAX, mc1, false) : QueryKV{0, 0, 0, 0, 0, 0};
-  const int32_t len0 = bok0 ? p.seq_lens[mb0] : 0;
-  const int32_t len1 = bok1 ? p.seq_lens[mb1] : 0;
   const int32_t P = p.page_size;
   const int64_t hkv = p.hkv;
-
-  // union mode: one sequence, touching windows, the groups within the
-  // bitmaps and the page-table columns within the LDS slices
-  const bool touch = pk0.win_len == 0 || pk1.win_len == 0 ||
-                     (pk1.win_lo <= pk0.t + 1 && pk0.win_lo <= pk1.t + 1);
-  const int32_t ncmax = max(pk0.n_c, pk1.n_c);
-  int32_t wlo = 0, nwin = 0;                          // union window: positions wlo .. wlo+nwin-1
-  if (pk0.win_len > 0 || pk1.win_len > 0) {
-    wlo = pk0.win_len == 0 ? pk1.win_lo : pk1.win_len == 0 ? pk0.win_lo : min(pk0.win_lo, pk1.win_lo);
-    const int32_t whi = pk0.win_len == 0 ? pk1.t : pk1.win_len == 0 ? pk0.t : max(pk0.t, pk1.t);
-    nwin = whi - wlo + 1;
-  }
-  const int32_t ncol_c = p.ratio > 0 ? min((ncmax + P - 1) / P, p.cmp_pt_stride) : 0;
-  const int32_t col_lo = wlo / P;
-  const int32_t ncol_r = nwin > 0 ? max(0, min((wlo + nwin - 1) / P, p.raw_pt_stride - 1) - col_lo + 1) : 0;
-  bool uni = bok0 && (!has1 || (bok1 && mb1 == mb0)) && touch && ncmax <= 32 * kBmWords &&
-                   ncol_c + ncol_r <= kPtMax;
-  int32_t U = 0;                                      // rows in the union list
-
-  QueryKV kv0{0, 0, 0, 0, 0, 0}, kv1{0, 0, 0, 0, 0, 0};
-  if (uni) {
-    const int32_t b = mb0;
-    // -- page-table slices into LDS (direct loads): compressed columns
-    // 0 .. ncol_c-1, then raw columns col_lo .. col_lo+ncol_r-1
-    for (int c = wave; 64 * c < ncol_c + ncol_r; c += kThreads / 64) {
-      const int k = 64 * c + lane;
-      const void *src = kZeroRow;
-      if (k < ncol_c) src = p.cmp_pt + (int64_t)b * p.cmp_pt_stride + k;
-      else if (k < ncol_c + ncol_r) src = p.raw_pt + (int64_t)b * p.raw_pt_stride + col_lo + (k - ncol_c);
-      dma4(src, &sm.u.s.pt[64 * c]);
-    }
-    for (int k = tid; k < 2 * kBmWords; k += kThreads) (&sm.u.s.bm[0][0])[k] = 0u;
-    if (tid == 0) sm.dup = 0;
-    wait_vmcnt<0>();                                  // slices, lists, Q
-    __syncthreads();                                  // slices in, bitmaps cleared
-    // -- the KV sets checked against seq_lens (a query past its sequence
-    // has an empty set; the error bits are raised once); they are subsets
-    // of the provisional ones, so the slices cover them
-    kv0 = query_kv_of(p, mb0, mt0, len0, mc0, tid == 0);
-    if (bok1) kv1 = query_kv_of(p, mb1, mt1, len1, mc1, tid == 0);
-    if (has1 && !bok1 && tid == 0) flag_error(p, kErrQuery);
-    // -- selected groups: one bitmap per query
+  int32_t U = 0;                                      // rows in the item's list
+  if constexpr (DEC) {
+    // ---- a decode slice.  Slice s holds the compressed entries in list
+    // slots [s*cper, (s+1)*cper) (cper = the list capacity, or the groups
+    // the page table can hold for an all-groups layer, over S) and the
+    // window entries [s*wper, (s+1)*wper) (wper = W over S), each cut at the
+    // query's own counts; any partition gives the same result
+    const int64_t cap = p.ratio == 0 ? 0 : topk > 0 ? topk : (int64_t)p.cmp_pt_stride * P;
+    const int32_t cper = (int32_t)((cap + S - 1) / S);
+    const int32_t wper = (p.window + S - 1) / S;
+    const int32_t c0 = split * cper;
+    int32_t ids[kRowIters];
 #pragma unroll
     for (int it = 0; it < kRowIters; ++it) {
       const int e = tid + it * kThreads;
-      if (topk > 0 && e < 2 * topk) {
-        const int q = e >= topk ? 1 : 0;
-        const QueryKV &kv = q ? kv1 : kv0;
-        if (e - q * topk < kv.n_sel) {
-          const int32_t c = ids[it];
-          if (c >= 0 && c < kv.n_c) {
-            if (atomicOr(&sm.u.s.bm[q][c >> 5], 1u << (c & 31)) & (1u << (c & 31))) sm.dup = 1;
-          } else {
-            flag_error(p, kErrCmpId);
-          }
-        }
-      }
+      ids[it] = (topk > 0 && e < cper && c0 + e < topk) ? p.cmp_idx[(int64_t)i0 * topk + c0 + e] : -1;
     }
-    __syncthreads();
-    // a list that names a group twice counts it twice, as the canonical
-    // order does: such a pair takes the concatenation below
-    uni = sm.dup == 0;
-  }
-  if (uni) {
-    // -- rank of every word's first group in the ascending union: thread t
-    // sums words 4t .. 4t+3, one scan over the threads
-    const int32_t nw = (ncmax + 31) / 32;             // <= kBmWords = 4 * kThreads
-    int32_t wc[4];
-    int32_t own = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = 4 * tid + u;
-      wc[u] = k < nw ? __popc(sm.u.s.bm[0][k] | sm.u.s.bm[1][k]) : 0;
-      own += wc[u];
-    }
-    int32_t ncu;                                      // groups in the union
-    int32_t pre = block_excl_scan(own, ncu, sm.wsum);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = 4 * tid + u;
-      if (k < nw) sm.u.s.wpre[k] = pre;
-      pre += wc[u];
-    }
-    const int32_t wlo2 = kv0.win_len == 0 ? kv1.win_lo : kv1.win_len == 0 ? kv0.win_lo : min(kv0.win_lo, kv1.win_lo);
-    const int32_t nwin2 = (kv0.win_len == 0 && kv1.win_len == 0) ? 0
-                          : (kv0.win_len == 0 ? kv1.t : kv1.win_len == 0 ? kv0.t : max(kv0.t, kv1.t)) - wlo2 + 1;
-    U = min(ncu + nwin2, kUMax);
-    __syncthreads();                                  // word ranks in
-    // -- translation from the slices: pool row (row * Hkv + g) with bit 62
-    // set for a compressed row, or -1; one thread per group id, then per
-    // window position; rows up to the next tile edge padded
+    const QueryKV kv = query_kv(p, i0);
+    if (topk == 0 && kv.n_sel > cap && split == 0 && tid == 0) flag_error(p, kErrPage);   // groups past the table
+    const int32_t cs = min(c0, kv.n_sel), ce = min(c0 + cper, kv.n_sel);
+    const int32_t ws = min(split * wper, kv.win_len), we = min(split * wper + wper, kv.win_len);
+    const int32_t Uc = ce - cs;
+    U = min(Uc + (we - ws), kUMax);
     const bool pow2 = p.page_shift >= 0;
-    auto pool_row = [&](int32_t x, bool cmp) -> int64_t {
-      const int32_t col = pow2 ? x >> p.page_shift : x / P;
-      const int32_t off = x - col * P;
-      int32_t page = -1;
-      if (cmp ? col < ncol_c : (col >= col_lo && col - col_lo < ncol_r)) page = sm.u.s.pt[cmp ? col : ncol_c + (col - col_lo)];
-      if (page >= 0 && (int64_t)page < (cmp ? p.cmp_pages : p.raw_pages))
-        return (((int64_t)page * P + off) * hkv + g) | (cmp ? kCmpBit : 0);
-      flag_error(p, kErrPage);
-      return -1;
-    };
-    for (int c = tid; c < 32 * nw; c += kThreads) {
-      const uint32_t b0 = sm.u.s.bm[0][c >> 5], b1 = sm.u.s.bm[1][c >> 5];
-      const uint32_t bit = 1u << (c & 31);
-      if ((b0 | b1) & bit) {
-        const int32_t r = sm.u.s.wpre[c >> 5] + __popc((b0 | b1) & (bit - 1u));
-        if (r < kUMax) {
-          const int64_t er = pool_row(c, true);
-          sm.row[r] = er;
-          sm.flg[r] = (uint8_t)(er >= 0 ? ((b0 & bit) ? 1u : 0u) | ((b1 & bit) ? 2u : 0u) : 0u);
-        }
-      }
-    }
-    for (int e = tid; e < (U + kPT - 1) / kPT * kPT - ncu; e += kThreads) {
-      const int r = ncu + e;
-      int64_t er = -1;
-      uint32_t sel = 0;
-      if (e < nwin2 && r < kUMax) {
-        const int32_t x = wlo2 + e;
-        sel = (kv0.win_len > 0 && x >= kv0.win_lo && x <= kv0.t ? 1u : 0u) |
-              (kv1.win_len > 0 && x >= kv1.win_lo && x <= kv1.t ? 2u : 0u);
-        if (sel != 0) er = pool_row(x, false);
-      }
-      if (r < kUMax) {
-        sm.row[r] = er;
-        sm.flg[r] = (uint8_t)(er >= 0 ? sel : 0u);
-      }
-    }
-  } else {
-    // -- concatenation: query 0's canonical rows, then query 1's (the
-    // metadata is read again: this path is for the odd cases)
-    kv0 = query_kv(p, i0);
-    kv1 = has1 ? query_kv(p, i1) : QueryKV{0, 0, 0, 0, 0, 0};
-    const int32_t U0 = kv0.n_sel + kv0.win_len;
-    const int32_t U1 = has1 ? kv1.n_sel + kv1.win_len : 0;
-    U = min(U0 + U1, kUMax);
-    int32_t xs[kRowIters];
+    int32_t xs[kRowIters], pg[kRowIters];
 #pragma unroll
     for (int it = 0; it < kRowIters; ++it) {
       const int r = tid + it * kThreads;
-      xs[it] = -1;
+      int32_t x = -1;
+      const int32_t *src = nullptr;
       if (r < U) {
-        const int q = r < U0 ? 0 : 1;
-        const QueryKV &kv = q ? kv1 : kv0;
-        const int32_t e = q ? r - U0 : r;
-        if (e < kv.n_sel) xs[it] = topk > 0 ? p.cmp_idx[(int64_t)(q ? i1 : i0) * topk + e] : e;
-        else xs[it] = kv.win_lo + (e - kv.n_sel);
-      }
-    }
-    int32_t pg[kRowIters];
-#pragma unroll
-    for (int it = 0; it < kRowIters; ++it) {
-      const int r = tid + it * kThreads;
-      pg[it] = -1;
-      if (r < U) {
-        const int q = r < U0 ? 0 : 1;
-        const QueryKV &kv = q ? kv1 : kv0;
-        const int32_t e = q ? r - U0 : r;
-        const bool cmp = e < kv.n_sel;
-        int32_t x = xs[it];
+        const bool cmp = r < Uc;
+        x = cmp ? (topk > 0 ? ids[it] : cs + r) : kv.win_lo + ws + (r - Uc);
         if (cmp && (x < 0 || x >= kv.n_c)) {
           flag_error(p, kErrCmpId);
           x = -1;
         }
         if (x >= 0) {
-          const int32_t col = x / P;
+          const int32_t col = pow2 ? x >> p.page_shift : x / P;
           if (col < (cmp ? p.cmp_pt_stride : p.raw_pt_stride))
-            pg[it] = (cmp ? p.cmp_pt + (int64_t)kv.b * p.cmp_pt_stride : p.raw_pt + (int64_t)kv.b * p.raw_pt_stride)[col];
+            src = cmp ? p.cmp_pt + (int64_t)kv.b * p.cmp_pt_stride + col : p.raw_pt + (int64_t)kv.b * p.raw_pt_stride + col;
           else {
             flag_error(p, kErrPage);
             x = -1;
           }
         }
-        xs[it] = x;
       }
+      xs[it] = x;
+      pg[it] = src != nullptr ? *src : -1;
     }
 #pragma unroll
     for (int it = 0; it < kRowIters; ++it) {
       const int r = tid + it * kThreads;
       if (r < (U + kPT - 1) / kPT * kPT) {
+        const bool cmp = r < Uc;
+        int64_t er = -1;
+        if (r < U && xs[it] >= 0) {
+          if (pg[it] >= 0 && (int64_t)pg[it] < (cmp ? p.cmp_pages : p.raw_pages)) {
+            const int32_t col = pow2 ? xs[it] >> p.page_shift : xs[it] / P;
+            er = (((int64_t)pg[it] * P + (xs[it] - col * P)) * hkv + g) | (cmp ? kCmpBit : 0);
+          } else {
+            flag_error(p, kErrPage);
+          }
+        }
+        sm.row[r] = er;
+        sm.flg[r] = (uint8_t)(er >= 0 ? 1u : 0u);
+      }
+    }
+  } else {
+    const int32_t mb0 = p.query_seq[i0], mt0 = p.query_pos[i0];
+    const int32_t mb1 = has1 ? p.query_seq[i1] : -1, mt1 = has1 ? p.query_pos[i1] : -1;
+    const int32_t mc0 = topk > 0 ? p.cmp_cnt[i0] : 0;
+    const int32_t mc1 = (topk > 0 && has1) ? p.cmp_cnt[i1] : 0;
+    int32_t ids[kRowIters];
+#pragma unroll
+    for (int it = 0; it < kRowIters; ++it) {
+      const int e = tid + it * kThreads;
+      const int q = e >= topk ? 1 : 0;
+      ids[it] = (topk > 0 && e < 2 * topk && (q == 0 || has1))
+                    ? p.cmp_idx[(int64_t)(q ? i1 : i0) * topk + (e - q * topk)] : -1;
+    }
+
+    // ---- the pair's KV sets, before the positions are checked against
+    // seq_lens (those loads are issued now and checked after the build)
+    const bool bok0 = mb0 >= 0 && mb0 < p.num_seqs;
+    const bool bok1 = has1 && mb1 >= 0 && mb1 < p.num_seqs;
+    const QueryKV pk0 = bok0 ? query_kv_of(p, mb0, mt0, INT32_MAX, mc0, false) : QueryKV{0, 0, 0, 0, 0, 0};
+    const QueryKV pk1 = bok1 ? query_kv_of(p, mb1, mt1, INT32_MAX, mc1, false) : QueryKV{0, 0, 0, 0, 0, 0};
+    const int32_t len0 = bok0 ? p.seq_lens[mb0] : 0;
+    const int32_t len1 = bok1 ? p.seq_lens[mb1] : 0;
+
+    // union mode: one sequence, touching windows, the groups within the
+    // bitmaps and the page-table columns within the LDS slices
+    const bool touch = pk0.win_len == 0 || pk1.win_len == 0 ||
+                       (pk1.win_lo <= pk0.t + 1 && pk0.win_lo <= pk1.t + 1);
+    const int32_t ncmax = max(pk0.n_c, pk1.n_c);
+    int32_t wlo = 0, nwin = 0;                          // union window: positions wlo .. wlo+nwin-1
+    if (pk0.win_len > 0 || pk1.win_len > 0) {
+      wlo = pk0.win_len == 0 ? pk1.win_lo : pk1.win_len == 0 ? pk0.win_lo : min(pk0.win_lo, pk1.win_lo);
+      const int32_t whi = pk0.win_len == 0 ? pk1.t : pk1.win_len == 0 ? pk0.t : max(pk0.t, pk1.t);
+      nwin = whi - wlo + 1;
+    }
+    const int32_t ncol_c = p.ratio > 0 ? min((ncmax + P - 1) / P, p.cmp_pt_stride) : 0;
+    const int32_t col_lo = wlo / P;
+    const int32_t ncol_r = nwin > 0 ? max(0, min((wlo + nwin - 1) / P, p.raw_pt_stride - 1) - col_lo + 1) : 0;
+    bool uni = bok0 && (!has1 || (bok1 && mb1 == mb0)) && touch && ncmax <= 32 * kBmWords &&
+                     ncol_c + ncol_r <= kPtMax;
+
+    QueryKV kv0{0, 0, 0, 0, 0, 0}, kv1{0, 0, 0, 0, 0, 0};
+    if (uni) {
+      const int32_t b = mb0;
+      // -- page-table slices into LDS (direct loads): compressed columns
+      // 0 .. ncol_c-1, then raw columns col_lo .. col_lo+ncol_r-1
+      for (int c = wave; 64 * c < ncol_c + ncol_r; c += kThreads / 64) {
+        const int k = 64 * c + lane;
+        const void *src = kZeroRow;
+        if (k < ncol_c) src = p.cmp_pt + (int64_t)b * p.cmp_pt_stride + k;
+        else if (k < ncol_c + ncol_r) src = p.raw_pt + (int64_t)b * p.raw_pt_stride + col_lo + (k - ncol_c);
+        dma4(src, &sm.u.s.pt[64 * c]);
+      }
+      for (int k = tid; k < 2 * kBmWords; k += kThreads) (&sm.u.s.bm[0][0])[k] = 0u;
+      if (tid == 0) sm.dup = 0;
+      wait_vmcnt<0>();                                  // slices, lists, Q
+      __syncthreads();                                  // slices in, bitmaps cleared
+      // -- the KV sets checked against seq_lens (a query past its sequence
+      // has an empty set; the error bits are raised once); they are subsets
+      // of the provisional ones, so the slices cover them
+      kv0 = query_kv_of(p, mb0, mt0, len0, mc0, tid == 0);
+      if (bok1) kv1 = query_kv_of(p, mb1, mt1, len1, mc1, tid == 0);
+      if (has1 && !bok1 && tid == 0) flag_error(p, kErrQuery);
+      // -- selected groups: one bitmap per query
+#pragma unroll
+      for (int it = 0; it < kRowIters; ++it) {
+        const int e = tid + it * kThreads;
+        if (topk > 0 && e < 2 * topk) {
+          const int q = e >= topk ? 1 : 0;
+          const QueryKV &kv = q ? kv1 : kv0;
+          if (e - q * topk < kv.n_sel) {
+            const int32_t c = ids[it];
+            if (c >= 0 && c < kv.n_c) {
+              if (atomicOr(&sm.u.s.bm[q][c >> 5], 1u << (c & 31)) & (1u << (c & 31))) sm.dup = 1;
+            } else {
+              flag_error(p, kErrCmpId);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // a list that names a group twice counts it twice, as the canonical
+      // order does: such a pair takes the concatenation below
+      uni = sm.dup == 0;
+    }
+    if (uni) {
+      // -- rank of every word's first group in the ascending union: thread t
+      // sums words 4t .. 4t+3, one scan over the threads
+      const int32_t nw = (ncmax + 31) / 32;             // <= kBmWords = 4 * kThreads
+      int32_t wc[4];
+      int32_t own = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = 4 * tid + u;
+        wc[u] = k < nw ? __popc(sm.u.s.bm[0][k] | sm.u.s.bm[1][k]) : 0;
+        own += wc[u];
+      }
+      int32_t ncu;                                      // groups in the union
+      int32_t pre = block_excl_scan(own, ncu, sm.wsum);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = 4 * tid + u;
+        if (k < nw) sm.u.s.wpre[k] = pre;
+        pre += wc[u];
+      }
+      const int32_t wlo2 = kv0.win_len == 0 ? kv1.win_lo : kv1.win_len == 0 ? kv0.win_lo : min(kv0.win_lo, kv1.win_lo);
+      const int32_t nwin2 = (kv0.win_len == 0 && kv1.win_len == 0) ? 0
+                            : (kv0.win_len == 0 ? kv1.t : kv1.win_len == 0 ? kv0.t : max(kv0.t, kv1.t)) - wlo2 + 1;
+      U = min(ncu + nwin2, kUMax);
+      __syncthreads();                                  // word ranks in
+      // -- translation from the slices: pool row (row * Hkv + g) with bit 62
+      // set for a compressed row, or -1; one thread per group id, then per
+      // window position; rows up to the next tile edge padded
+      const bool pow2 = p.page_shift >= 0;
+      auto pool_row = [&](int32_t x, bool cmp) -> int64_t {
+        const int32_t col = pow2 ? x >> p.page_shift : x / P;
+        const int32_t off = x - col * P;
+        int32_t page = -1;
+        if (cmp ? col < ncol_c : (col >= col_lo && col - col_lo < ncol_r)) page = sm.u.s.pt[cmp ? col : ncol_c + (col - col_lo)];
+        if (page >= 0 && (int64_t)page < (cmp ? p.cmp_pages : p.raw_pages))
+          return (((int64_t)page * P + off) * hkv + g) | (cmp ? kCmpBit : 0);
+        flag_error(p, kErrPage);
+        return -1;
+      };
+      for (int c = tid; c < 32 * nw; c += kThreads) {
+        const uint32_t b0 = sm.u.s.bm[0][c >> 5], b1 = sm.u.s.bm[1][c >> 5];
+        const uint32_t bit = 1u << (c & 31);
+        if ((b0 | b1) & bit) {
+          const int32_t r = sm.u.s.wpre[c >> 5] + __popc((b0 | b1) & (bit - 1u));
+          if (r < kUMax) {
+            const int64_t er = pool_row(c, true);
+            sm.row[r] = er;
+            sm.flg[r] = (uint8_t)(er >= 0 ? ((b0 & bit) ? 1u : 0u) | ((b1 & bit) ? 2u : 0u) : 0u);
+          }
+        }
+      }
+      for (int e = tid; e < (U + kPT - 1) / kPT * kPT - ncu; e += kThreads) {
+        const int r = ncu + e;
         int64_t er = -1;
         uint32_t sel = 0;
+        if (e < nwin2 && r < kUMax) {
+          const int32_t x = wlo2 + e;
+          sel = (kv0.win_len > 0 && x >= kv0.win_lo && x <= kv0.t ? 1u : 0u) |
+                (kv1.win_len > 0 && x >= kv1.win_lo && x <= kv1.t ? 2u : 0u);
+          if (sel != 0) er = pool_row(x, false);
+        }
+        if (r < kUMax) {
+          sm.row[r] = er;
+          sm.flg[r] = (uint8_t)(er >= 0 ? sel : 0u);
+        }
+      }
+    } else {
+      // -- concatenation: query 0's canonical rows, then query 1's (the
+      // metadata is read again: this path is for the odd cases)
+      kv0 = query_kv(p, i0);
+      kv1 = has1 ? query_kv(p, i1) : QueryKV{0, 0, 0, 0, 0, 0};
+      const int32_t U0 = kv0.n_sel + kv0.win_len;
+      const int32_t U1 = has1 ? kv1.n_sel + kv1.win_len : 0;
+      U = min(U0 + U1, kUMax);
+      int32_t xs[kRowIters];
+#pragma unroll
+      for (int it = 0; it < kRowIters; ++it) {
+        const int r = tid + it * kThreads;
+        xs[it] = -1;
+        if (r < U) {
+          const int q = r < U0 ? 0 : 1;
+          const QueryKV &kv = q ? kv1 : kv0;
+          const int32_t e = q ? r - U0 : r;
+          if (e < kv.n_sel) xs[it] = topk > 0 ? p.cmp_idx[(int64_t)(q ? i1 : i0) * topk + e] : e;
+          else xs[it] = kv.win_lo + (e - kv.n_sel);
+        }
+      }
+      int32_t pg[kRowIters];
+#pragma unroll
+      for (int it = 0; it < kRowIters; ++it) {
+        const int r = tid + it * kThreads;
+        pg[it] = -1;
         if (r < U) {
           const int q = r < U0 ? 0 : 1;
           const QueryKV &kv = q ? kv1 : kv0;
           const int32_t e = q ? r - U0 : r;
           const bool cmp = e < kv.n_sel;
-          if (xs[it] >= 0) {
-            if (pg[it] >= 0 && (int64_t)pg[it] < (cmp ? p.cmp_pages : p.raw_pages))
-              er = (((int64_t)pg[it] * P + (xs[it] % P)) * hkv + g) | (cmp ? kCmpBit : 0);
-            else
-              flag_error(p, kErrPage);
+          int32_t x = xs[it];
+          if (cmp && (x < 0 || x >= kv.n_c)) {
+            flag_error(p, kErrCmpId);
+            x = -1;
           }
-          sel = 1u << q;
+          if (x >= 0) {
+            const int32_t col = x / P;
+            if (col < (cmp ? p.cmp_pt_stride : p.raw_pt_stride))
+              pg[it] = (cmp ? p.cmp_pt + (int64_t)kv.b * p.cmp_pt_stride : p.raw_pt + (int64_t)kv.b * p.raw_pt_stride)[col];
+            else {
+              flag_error(p, kErrPage);
+              x = -1;
+            }
+          }
+          xs[it] = x;
         }
-        sm.row[r] = er;
-        sm.flg[r] = (uint8_t)(er >= 0 ? sel : 0u);
+      }
+#pragma unroll
+      for (int it = 0; it < kRowIters; ++it) {
+        const int r = tid + it * kThreads;
+        if (r < (U + kPT - 1) / kPT * kPT) {
+          int64_t er = -1;
+          uint32_t sel = 0;
+          if (r < U) {
+            const int q = r < U0 ? 0 : 1;
+            const QueryKV &kv = q ? kv1 : kv0;
+            const int32_t e = q ? r - U0 : r;
+            const bool cmp = e < kv.n_sel;
+            if (xs[it] >= 0) {
+              if (pg[it] >= 0 && (int64_t)pg[it] < (cmp ? p.cmp_pages : p.raw_pages))
+                er = (((int64_t)pg[it] * P + (xs[it] % P)) * hkv + g) | (cmp ? kCmpBit : 0);
+              else
+                flag_error(p, kErrPage);
+            }
+            sel = 1u << q;
+          }
+          sm.row[r] = er;
+          sm.flg[r] = (uint8_t)(er >= 0 ? sel : 0u);
+        }
       }
     }
-  }
+  }   // pairs
   wait_vmcnt<0>();                           // Q fragments, sink and every setup load are in
   __syncthreads();                           // rows and flags complete; bitmaps and slices dead
 
@@ -523,9 +612,11 @@ void attn_prefill_pair_kernel(const Params p) {
   for (int j = 0; j < ntiles; ++j) {
     // this wave's selection mask of tile j
     const uint32_t tm = (uint32_t)__ballot(lane < 32 && ((sm.flg[kPT * j + (lane & 31)] >> qw) & 1u));
-    // this wave's loads of tile j are complete (those of tile j+1 may still
-    // be in flight with three stages) ...
-    if (NST == 3 && j + 1 < ntiles) wait_vmcnt<4>();
+    // this wave's loads of tile j are complete (those of the next NST-2
+    // tiles may still be in flight; four loads per tile) ...
+    const int ahead = min(NST - 2, ntiles - 1 - j);
+    if (ahead >= 2) wait_vmcnt<8>();
+    else if (ahead == 1) wait_vmcnt<4>();
     else wait_vmcnt<0>();
     // ... and, after the barrier, every wave's: tile j is in LDS, and every
     // wave is done with tile j-1, whose stage the next load refills
@@ -544,6 +635,23 @@ void attn_prefill_pair_kernel(const Params p) {
   const float lse = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
   if (!hvalid) return;
   const int64_t h = (int64_t)g * p.group + hl;
+  if (DEC && S > 1) {
+    // a slice's sink-free partial: O_s = acc / l in fp32 and LSE_s (-inf
+    // for an empty slice, whose weight in the merge is then 0)
+    const int64_t prow = ((int64_t)split * p.num_queries + iq) * p.hq + h;
+    float *prow_o = p.part_o + prow * kD;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = 32 * db + 8 * i4 + 4 * hi;
+        *(float4 *)(prow_o + d0) = make_float4(acc[db][4 * i4] * inv, acc[db][4 * i4 + 1] * inv,
+                                               acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv);
+      }
+    }
+    if (hi == 0) p.part_lse[prow] = lse;
+    return;
+  }
   uint16_t *orow = p.o + ((int64_t)iq * p.hq + h) * kD;
 #pragma unroll
   for (int db = 0; db < kD / 32; ++db) {
@@ -573,7 +681,24 @@ hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream) {
   const int64_t npairs = (p.num_queries + 1) / 2;
   const int64_t grid = npairs * p.hkv * ((p.group + 63) / 64);
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(attn_prefill_pair_kernel<kPairStages>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_pair_kernel<kPairStages, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+bool decode_slices_eligible(const Params &p) {
+  if (p.head_dim != kD || p.cmp_fp8 || p.query_seq != nullptr || p.query_pos != nullptr || p.num_splits < 1)
+    return false;
+  const int64_t S = p.num_splits;
+  const int64_t cap = p.ratio == 0 ? 0 : p.topk > 0 ? p.topk : (int64_t)p.cmp_pt_stride * p.page_size;
+  return (cap + S - 1) / S + (p.window + S - 1) / S <= kUMax;
+}
+
+hipError_t launch_decode_slices(const Params &p, hipStream_t stream) {
+  if (p.num_queries == 0) return hipSuccess;
+  if (!decode_slices_eligible(p)) return hipErrorInvalidConfiguration;
+  const int64_t grid = (int64_t)p.num_queries * p.hkv * ((p.group + 127) / 128) * p.num_splits;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_pair_kernel<kDecodeStages, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
