@@ -30,7 +30,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the sources whose change invalidates counter-measured traffic
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
-                  for f in ("spa_attention.hip", "spa_prefill.hip", "spa_kernel_util.h", "spa_device.h",
+                  for f in ("spa_attention.hip", "spa_pair.hip", "spa_kernel_util.h", "spa_device.h",
                             "spa_internal.h", "spa_api.cpp")]
 PAIR_ROWS_MAX = 1280           # rows a query pair's union can hold in the prefill pair kernel
 
@@ -356,7 +356,7 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               f"multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch

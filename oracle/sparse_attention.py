@@ -20,7 +20,7 @@ Sources (the pages this follows; no code from them):
   tessera "Block AttnRes" PR (attn-with-stats + softmax_merge pair): the
   exact merge of partial (out, lse) pairs.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 * group c of ratio r is complete at token position t when r*(c+1) <= t+1, so
   n_c = floor((t+1)/r);
 * the window is the min(W, t+1) raw positions ending at t (the token itself

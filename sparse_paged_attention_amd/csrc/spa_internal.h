@@ -43,7 +43,7 @@ struct Params {
 
 hipError_t launch_attention(const Params &p, hipStream_t stream);
 
-// Prefill with query pairs sharing KV tiles (spa_prefill.hip): bf16 caches,
+// Prefill with query pairs sharing KV tiles (spa_pair.hip): bf16 caches,
 // D 128, one slice, a top-k list (or no compressed part) and at most
 // kPairRowsMax rows in the union of a pair's KV sets, which holds whenever
 // 2 * (topk + window) <= kPairRowsMax.
@@ -53,7 +53,7 @@ constexpr int kDecodeStages = 2;    // the same for decode slices
 bool prefill_pairs_eligible(const Params &p);
 hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream);
 // Decode with one workgroup per (query, KV head, 128-head block, KV slice)
-// (spa_prefill.hip): bf16 caches, D 128, and a slice's rows within
+// (spa_pair.hip): bf16 caches, D 128, and a slice's rows within
 // kPairRowsMax.  With several slices it writes sink-free partials for the
 // merge (in plain row order).
 bool decode_slices_eligible(const Params &p);

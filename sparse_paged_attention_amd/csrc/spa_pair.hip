@@ -1,23 +1,32 @@
-// Sparse paged attention prefill for gfx950: query pairs that share KV tiles.
+// Sparse paged attention for gfx950 with every wave of a workgroup a compute
+// wave: prefill query pairs that share KV tiles, and decode KV slices.
 //
 // Operation: the same as spa_attention.hip (RL-Kernel PR "Roadmap item 24:
 // joint compressed/window attention with sink", section "Reuse and
-// arithmetic"; KV-set and translation rules in spa_device.h), for prefill
-// calls with bf16 caches, D 128 and one KV slice.
+// arithmetic"; KV-set and translation rules in spa_device.h), for calls with
+// bf16 caches and D 128.
 //
-// Why pairs.  In a prefill the KV sets of neighbouring tokens of a sequence
-// overlap almost entirely: their windows differ by one row, and the
-// compressed groups two neighbours select are mostly the same (all of them,
-// while n_c is at most the top-k).  One workgroup serves two queries (a
-// pair) of one KV head and 64 of its query heads.  It streams the UNION of
-// the two KV sets once through LDS, and each of its four waves (query q of
-// the pair, heads 32w .. 32w+31) masks the rows its own query does not
-// select.  A tile of K and V then feeds 128 (query, head) columns instead of
-// 64, and the workgroup holds only compute waves: every wave issues a
-// quarter of each tile's direct global->LDS loads and then runs its MFMAs;
-// two workgroups (eight compute waves) share a CU.
+// Prefill query pairs (DEC = false).  In a prefill the KV sets of
+// neighbouring tokens of a sequence overlap almost entirely: their windows
+// differ by one row, and the compressed groups two neighbours select are
+// mostly the same (all of them, while n_c is at most the top-k).  One
+// workgroup serves two queries (a pair) of one KV head and 64 of its query
+// heads, with one KV slice.  It streams the UNION of the two KV sets once
+// through LDS, and each of its four waves (query q of the pair, heads
+// 32w .. 32w+31) masks the rows its own query does not select.  A tile of K
+// and V then feeds 128 (query, head) columns instead of 64.
 //
-// Setup (per workgroup, before the tile loop):
+// Decode slices (DEC = true).  One workgroup serves one KV slice of one
+// query, one KV head and 128 of its query heads (four waves of 32 heads).
+// A slice's list slots are cut by capacity, not by the query's own counts
+// (any partition of a set gives the same softmax), so they are loaded
+// together with the metadata; with several slices it writes a sink-free
+// partial (O_s, LSE_s) that the LSE merge kernel combines with the sink.
+//
+// Every wave issues a quarter of each tile's direct global->LDS loads and
+// then runs its MFMAs; two workgroups (eight waves) fit on a CU.
+//
+// Setup of a query pair (before the tile loop):
 //   * the loads that need nothing else are issued together: the Q fragments,
 //     both queries' metadata and both whole list rows; the KV sets are first
 //     computed without the check of the positions against seq_lens, whose
