@@ -46,12 +46,15 @@ def attention_kernel(p, splits, hpb, qpb):
     pairs = pairs_ok and (qpb == 2 or (qpb == 0 and hpb != 32))
     S = max(splits, 1)
     cap = 0 if p.ratio == 0 else p.topk if p.topk > 0 else p.cmp_pt.shape[1] * p.page_size
-    slices_ok = (p.mode == "decode" and p.head_dim == 128 and not p.cmp_fp8 and hpb == 0 and qpb == 0
-                 and -(-cap // S) + -(-p.window // S) <= PAIR_ROWS_MAX)
+    cper = -(-cap // S)
+    if p.cmp_fp8:
+        cper = -(-cper // 32) * 32          # e4m3 rows fill whole tiles
+    slices_ok = (p.mode == "decode" and p.head_dim == 128 and hpb == 0 and qpb == 0
+                 and cper + -(-p.window // S) <= PAIR_ROWS_MAX)
     if pairs:
-        return "attn_pair_kernel<2, false>"
+        return "attn_pair_kernel<2, false, false>"
     if slices_ok:
-        return "attn_pair_kernel<2, true>"
+        return "attn_pair_kernel<2, true, true>" if p.cmp_fp8 else "attn_pair_kernel<2, true, false>"
     return "attn_fwd_kernel"
 
 
@@ -174,7 +177,7 @@ def parse_args(argv=None):
 
 
 DEFAULTS = {   # (num_splits, heads_per_block, queries_per_block) per workload; 0 = library choice
-    "decode_csa": (4, 0, 0), "decode_hca": (4, 0, 0), "mixed_fp8": (8, 64, 1), "prefill_csa": (1, 0, 0),
+    "decode_csa": (4, 0, 0), "decode_hca": (4, 0, 0), "mixed_fp8": (8, 0, 0), "prefill_csa": (1, 0, 0),
     "tiny": (1, 0, 0),
 }
 

@@ -95,14 +95,14 @@ typedef struct spa_fwd_args {
   int32_t num_splits;     /* 1 = one pass; >1 = split-KV partials + LSE merge    */
   int32_t heads_per_block; /* query heads one job computes, sharing each KV
                               tile: 32 or 64, or 0 = chosen by the library: a
-                              decode with bf16 caches and head_dim 128 whose
-                              slice rows fit (ceil(topk / num_splits) +
-                              ceil(window / num_splits) <= 1280, topk read as
-                              cmp_pt_stride * page_size for an all-groups
-                              layer) takes 128 heads per job when
-                              queries_per_block is 0 too, otherwise 64 when
-                              the KV group has more than 32 heads; a tuning
-                              knob, the result does not depend on it       */
+                              decode with head_dim 128 whose slice rows fit
+                              (ceil(topk / num_splits), rounded up to 32 for
+                              e4m3 pages, + ceil(window / num_splits) <=
+                              1280, topk read as cmp_pt_stride * page_size
+                              for an all-groups layer) takes 128 heads per
+                              job when queries_per_block is 0 too, otherwise
+                              64 when the KV group has more than 32 heads; a
+                              tuning knob, the result does not depend on it */
   int32_t queries_per_block; /* queries one job serves, a tuning knob (the
                               result does not depend on it): 1 = one query per
                               job; 2 = query pairs (prefill only: two queries

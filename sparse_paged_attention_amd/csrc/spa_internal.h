@@ -53,8 +53,8 @@ constexpr int kDecodeStages = 2;    // the same for decode slices
 bool prefill_pairs_eligible(const Params &p);
 hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream);
 // Decode with one workgroup per (query, KV head, 128-head block, KV slice)
-// (spa_pair.hip): bf16 caches, D 128, and a slice's rows within
-// kPairRowsMax.  With several slices it writes sink-free partials for the
+// (spa_pair.hip): D 128, bf16 or e4m3 compressed pages, and a slice's rows
+// (compressed ones rounded up to whole tiles for e4m3) within kPairRowsMax.  With several slices it writes sink-free partials for the
 // merge (in plain row order).
 bool decode_slices_eligible(const Params &p);
 hipError_t launch_decode_slices(const Params &p, hipStream_t stream);

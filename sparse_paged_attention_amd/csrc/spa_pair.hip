@@ -84,7 +84,7 @@ constexpr int kBmWords = 1024;             // bitmap words per query: groups < 3
 constexpr int kPtMax = 4096;               // page-table entries the LDS slices hold
 constexpr int64_t kCmpBit = int64_t(1) << 62;   // row list: a compressed-pool row
 
-template <int NST>
+template <int NST, bool FP8>
 struct PairSmem {
   union {
     struct {
@@ -103,8 +103,14 @@ struct PairSmem {
   uint8_t flg[kUMax];                      // bit q: selected by query q
   int32_t wsum[4];
   int32_t dup;                             // a list names a group twice
+  // e4m3 compressed tiles (decode slices with FP8 pages): the staged codes
+  // of both sides, 32 rows of D bytes, and their fp32 row scales
+  alignas(16) uint8_t f8k[FP8 ? NST : 1][FP8 ? kPT * kD : 16];
+  alignas(16) uint8_t f8v[FP8 ? NST : 1][FP8 ? kPT * kD : 16];
+  alignas(16) float f8sk[FP8 ? NST : 1][64];
+  alignas(16) float f8sv[FP8 ? NST : 1][64];
 };
-static_assert(sizeof(PairSmem<2>::u) == 2 * 2 * kPTileB, "setup arrays fit the tile stages");
+static_assert(sizeof(PairSmem<2, false>::u) == 2 * 2 * kPTileB, "setup arrays fit the tile stages");
 static_assert(kBmWords == 4 * kThreads, "four bitmap words per thread in the rank scan");
 static_assert(kUMax % kPT == 0, "padding to a whole tile stays within the row list");
 
@@ -135,11 +141,19 @@ __device__ __forceinline__ int32_t block_excl_scan(int32_t v, int32_t &total, in
 // 2 + head half).  DEC = true: one KV slice of a decode query (one query,
 // 128 heads: wave = head quarter), whose sink-free partial the LSE merge
 // combines when there are several slices.
-template <int NST, bool DEC>
+//
+// FP8 (decode slices only): the compressed pool holds OCP e4m3 codes with an
+// fp32 scale per row.  The compressed rows of a slice fill whole tiles (the
+// window starts at the next tile), an e4m3 tile is loaded into a staging
+// area with its scales and widened to bf16 in LDS by all waves after its
+// barrier (every e4m3 value is a bf16 value, so this is exact), and the k
+// scale multiplies the fp32 scores, the v scale p before its bf16 rounding.
+template <int NST, bool DEC, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_pair_kernel(const Params p) {
   static_assert(NST >= 2 && NST <= 4, "two to four LDS stages");
-  __shared__ PairSmem<NST> sm;
+  static_assert(!FP8 || (DEC && NST == 2), "e4m3 tiles: decode slices with two stages");
+  __shared__ PairSmem<NST, FP8> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -194,6 +208,7 @@ void attn_pair_kernel(const Params p) {
   const int32_t P = p.page_size;
   const int64_t hkv = p.hkv;
   int32_t U = 0;                                      // rows in the item's list
+  int32_t wbase = 0;                                  // decode: first window row
   if constexpr (DEC) {
     // ---- a decode slice.  Slice s holds the compressed entries in list
     // slots [s*cper, (s+1)*cper) (cper = the list capacity, or the groups
@@ -215,7 +230,8 @@ void attn_pair_kernel(const Params p) {
     const int32_t cs = min(c0, kv.n_sel), ce = min(c0 + cper, kv.n_sel);
     const int32_t ws = min(split * wper, kv.win_len), we = min(split * wper + wper, kv.win_len);
     const int32_t Uc = ce - cs;
-    U = min(Uc + (we - ws), kUMax);
+    wbase = FP8 ? (Uc + kPT - 1) / kPT * kPT : Uc;   // first window row
+    U = min(wbase + (we - ws), kUMax);
     const bool pow2 = p.page_shift >= 0;
     int32_t xs[kRowIters], pg[kRowIters];
 #pragma unroll
@@ -223,9 +239,9 @@ void attn_pair_kernel(const Params p) {
       const int r = tid + it * kThreads;
       int32_t x = -1;
       const int32_t *src = nullptr;
-      if (r < U) {
+      if (r < U && (r < Uc || r >= wbase)) {
         const bool cmp = r < Uc;
-        x = cmp ? (topk > 0 ? ids[it] : cs + r) : kv.win_lo + ws + (r - Uc);
+        x = cmp ? (topk > 0 ? ids[it] : cs + r) : kv.win_lo + ws + (r - wbase);
         if (cmp && (x < 0 || x >= kv.n_c)) {
           flag_error(p, kErrCmpId);
           x = -1;
@@ -504,13 +520,35 @@ void attn_pair_kernel(const Params p) {
     csrc[n] = ((lane % kChunks) ^ swz<kChunks>(r)) * 16;
   }
   const int32_t ntiles = (U + kPT - 1) / kPT;
+  const int32_t nf8 = FP8 ? wbase / kPT : 0;         // tiles 0 .. nf8-1 hold e4m3 rows
   int64_t nrow[2];
+  // an e4m3 tile: wave w moves rows 8w .. 8w+7 of D bytes per side (one
+  // 1 KiB load each, lane L: row 8w + L / 8, bytes 16 (L % 8) ..), into the
+  // staging area; waves 0 and 1 also load the 32 k and v scales
   auto fetch_rows = [&](int j) {
+    if (FP8 && j < nf8) {
+      nrow[0] = sm.row[kPT * j + 8 * wave + lane / 8];
+      nrow[1] = sm.row[kPT * j + (lane & 31)];
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < 2; ++n) nrow[n] = j < ntiles ? sm.row[kPT * j + 8 * wave + 4 * n + lane / kChunks] : -1;
   };
   auto issue = [&](int j) {
     const int st = j % NST;
+    if (FP8 && j < nf8) {
+      const int64_t er = nrow[0];
+      const int64_t off = (er & ~kCmpBit) * kD + (lane % 8) * 16;
+      dma16(er >= 0 ? kcmp + off : kZeroRow + (lane % 8) * 16, sm.f8k[FP8 ? st : 0] + 1024 * wave);
+      dma16(er >= 0 ? vcmp + off : kZeroRow + (lane % 8) * 16, sm.f8v[FP8 ? st : 0] + 1024 * wave);
+      if (wave < 2) {
+        const int64_t es = nrow[1];
+        const float *scl = wave == 0 ? p.k_cmp_scale : p.v_cmp_scale;
+        dma4(lane < kPT && es >= 0 ? (const void *)(scl + (es & ~kCmpBit)) : (const void *)(kZeroRow + 4 * lane),
+             wave == 0 ? sm.f8sk[FP8 ? st : 0] : sm.f8sv[FP8 ? st : 0]);
+      }
+      return;
+    }
     const uint8_t *ks[2], *vs[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -538,7 +576,7 @@ void attn_pair_kernel(const Params p) {
   // S^T = K . Q^T, the online softmax of the scores (rows not selected by
   // this wave's query masked to -inf) and O^T += V^T . P^T.  Lane rows of
   // S^T: 8*(i/4) + 4*hi + i%4.
-  auto tile = [&](int st, uint32_t tm) {
+  auto tile = [&](int st, uint32_t tm, bool f8) {
     const uint8_t *Kt = sm.u.t.k[st];
     const uint8_t *Vt = sm.u.t.v[st];
     bf16x8 kf[kD / 16];
@@ -571,9 +609,22 @@ void attn_pair_kernel(const Params p) {
     for (int kk = 0; kk < kD / 16; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
 
     float sc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = s[i];
+    if (FP8 && f8) {
+      // the k scale of each row multiplies the fp32 score of its exact code
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 k4 = *(const float4 *)(&sm.f8sk[FP8 ? st : 0][8 * q4 + 4 * hi]);
+        sc[4 * q4 + 0] *= k4.x;
+        sc[4 * q4 + 1] *= k4.y;
+        sc[4 * q4 + 2] *= k4.z;
+        sc[4 * q4 + 3] *= k4.w;
+      }
+    }
     const uint32_t tmh = tm >> (4 * hi);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = ((tmh >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
+    for (int i = 0; i < 16; ++i) sc[i] = ((tmh >> (8 * (i >> 2) + (i & 3))) & 1u) ? sc[i] : -INFINITY;
     float smax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     smax = fmaxf(smax, fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])),
                              fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]))));
@@ -596,6 +647,17 @@ void attn_pair_kernel(const Params p) {
       psum += pr[i];
     }
     l += psum;
+    if (FP8 && f8) {
+      // the v scale of each row multiplies p before its bf16 rounding
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v4 = *(const float4 *)(&sm.f8sv[FP8 ? st : 0][8 * q4 + 4 * hi]);
+        pr[4 * q4 + 0] *= v4.x;
+        pr[4 * q4 + 1] *= v4.y;
+        pr[4 * q4 + 2] *= v4.z;
+        pr[4 * q4 + 3] *= v4.w;
+      }
+    }
     bf16x8 pb[2];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
@@ -630,11 +692,40 @@ void attn_pair_kernel(const Params p) {
     // ... and, after the barrier, every wave's: tile j is in LDS, and every
     // wave is done with tile j-1, whose stage the next load refills
     block_sync();
+    const bool f8 = FP8 && j < nf8;
+    if (FP8 && f8) {
+      // widen the staged e4m3 tile into the bf16 tile of its stage (exact),
+      // in the swizzled layout of a bf16 tile: 8 codes per thread and step
+      const int st = j % NST;
+#pragma unroll
+      for (int side = 0; side < 2; ++side) {
+        const uint8_t *src = side ? sm.f8v[FP8 ? st : 0] : sm.f8k[FP8 ? st : 0];
+        uint8_t *dst = side ? sm.u.t.v[st] : sm.u.t.k[st];
+#pragma unroll
+        for (int it = 0; it < kPT * kD / 8 / kThreads; ++it) {
+          const int idx = tid + it * kThreads;
+          const int r = idx / (kD / 8);
+          const int piece = idx - r * (kD / 8);
+          const uint2 w = *(const uint2 *)(src + r * kD + piece * 8);
+          const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+          const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+          const f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+          const f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+          uint4 o;
+          o.x = pack_bf16_hi(a0[0], a0[1]);
+          o.y = pack_bf16_hi(a1[0], a1[1]);
+          o.z = pack_bf16_hi(a2[0], a2[1]);
+          o.w = pack_bf16_hi(a3[0], a3[1]);
+          *(uint4 *)(dst + r * kRowB + ((piece ^ swz<kChunks>(r)) * 16)) = o;
+        }
+      }
+      block_sync();                          // the widened tile is in
+    }
     if (j + NST - 1 < ntiles) {
       issue(j + NST - 1);
       fetch_rows(j + NST);
     }
-    tile(j % NST, tm);
+    tile(j % NST, tm, f8);
   }
 
   // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) ln 2
@@ -690,16 +781,17 @@ hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream) {
   const int64_t npairs = (p.num_queries + 1) / 2;
   const int64_t grid = npairs * p.hkv * ((p.group + 63) / 64);
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_pair_kernel<kPairStages, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_pair_kernel<kPairStages, false, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 bool decode_slices_eligible(const Params &p) {
-  if (p.head_dim != kD || p.cmp_fp8 || p.query_seq != nullptr || p.query_pos != nullptr || p.num_splits < 1)
-    return false;
+  if (p.head_dim != kD || p.query_seq != nullptr || p.query_pos != nullptr || p.num_splits < 1) return false;
   const int64_t S = p.num_splits;
   const int64_t cap = p.ratio == 0 ? 0 : p.topk > 0 ? p.topk : (int64_t)p.cmp_pt_stride * p.page_size;
-  return (cap + S - 1) / S + (p.window + S - 1) / S <= kUMax;
+  int64_t cper = (cap + S - 1) / S;
+  if (p.cmp_fp8) cper = (cper + kPT - 1) / kPT * kPT;   // e4m3 rows fill whole tiles
+  return cper + (p.window + S - 1) / S <= kUMax;
 }
 
 hipError_t launch_decode_slices(const Params &p, hipStream_t stream) {
@@ -707,7 +799,10 @@ hipError_t launch_decode_slices(const Params &p, hipStream_t stream) {
   if (!decode_slices_eligible(p)) return hipErrorInvalidConfiguration;
   const int64_t grid = (int64_t)p.num_queries * p.hkv * ((p.group + 127) / 128) * p.num_splits;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_pair_kernel<kDecodeStages, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  if (p.cmp_fp8)
+    hipLaunchKernelGGL((attn_pair_kernel<2, true, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_pair_kernel<kDecodeStages, true, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

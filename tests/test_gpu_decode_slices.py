@@ -70,3 +70,22 @@ def test_window_only_and_empty():
             assert np.allclose(L, np.broadcast_to(q.sink, L.shape), atol=1e-6)
         else:
             assert np.all(L == -np.inf)
+
+
+@pytest.mark.parametrize("splits", [1, 4, 8])
+def test_mixed_fp8_slices(splits):
+    """The mixed FP8/BF16 workload: e4m3 compressed rows (per-row fp32
+    scales) widened in LDS, then the bf16 window; both decode kernels."""
+    p = synth.make_workload("mixed_fp8")
+    check_against_oracle(p, num_splits=splits, label=f"mixed_fp8 slices S{splits}")
+    check_against_oracle(p, num_splits=splits, heads_per_block=64, label=f"mixed_fp8 job streams S{splits}")
+
+
+def test_fp8_partial_compressed_tiles():
+    """e4m3 compressed rows that do not fill their last tile (the window
+    starts at the next tile), short lists, split counts that leave slices
+    with no compressed row, and 80 heads over two KV heads."""
+    rng = np.random.default_rng(11)
+    p = _decode("f8p", rng.integers(20, 900, size=7), 160, 2, 16, 45, 4, 37, cmp_fp8=True)
+    for s in (1, 3, 11):
+        check_against_oracle(p, num_splits=s, label=f"fp8 partial tiles S{s}")
