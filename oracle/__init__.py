@@ -13,6 +13,7 @@ per-head sink logit (which has no value row).  Everything runs in float64.
 Modules:
   formats    bf16 and OCP e4m3 decoding (exact, to float64)
   sparse_attention  KV-set metadata, gather, attention with sink, (O, LSE) merge
+  topk       top-k selection of compressed groups from per-token scores
   compare    the acceptance comparator
 
 Every function cites the passage it follows.  Pins live in
@@ -24,3 +25,4 @@ from .sparse_attention import (  # noqa: F401
     gather_plan, partial_split, physical_rows, query_f64, lse_merge_arrays,
 )
 from .compare import accept, AcceptReport  # noqa: F401
+from .topk import order_key, topk_select  # noqa: F401
