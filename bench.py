@@ -158,7 +158,8 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_csa",
-                    choices=["decode_csa", "decode_hca", "mixed_fp8", "prefill_csa", "tiny"])
+                    choices=["decode_csa", "decode_hca", "mixed_fp8", "prefill_csa", "tiny", "topk_decode",
+                             "topk_prefill"])
     ap.add_argument("--batch", type=int, default=0, help="decode batch override (0 = the workload's)")
     ap.add_argument("--splits", type=int, default=0, help="0 = the default for the workload")
     ap.add_argument("--heads-per-block", type=int, default=-1,
@@ -180,6 +181,37 @@ DEFAULTS = {   # (num_splits, heads_per_block, queries_per_block) per workload; 
     "decode_csa": (4, 0, 0), "decode_hca": (4, 0, 0), "mixed_fp8": (8, 0, 0), "prefill_csa": (1, 0, 0),
     "tiny": (1, 0, 0),
 }
+
+
+def graph_replay_ms(launch, n):
+    """Per-launch time of `n` calls of `launch(stream, k)` captured in one
+    HIP graph and replayed 5 times back to back (HIP events on the capture
+    stream); also the per-replay times."""
+    import numpy as np
+    import torch
+    cap_stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap_stream):
+        for k in range(3):
+            launch(cap_stream.cuda_stream, k)
+        cap_stream.synchronize()
+        with torch.cuda.graph(graph, stream=cap_stream):
+            cs = torch.cuda.current_stream()
+            for k in range(n):
+                launch(cs.cuda_stream, k)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        reps_g = 5
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(reps_g + 1)]
+        ge[0].record(cap_stream)
+        for r in range(reps_g):
+            graph.replay()
+            ge[r + 1].record(cap_stream)
+        torch.cuda.synchronize()
+    per = np.array([ge[r].elapsed_time(ge[r + 1]) / n for r in range(reps_g)])
+    return float(ge[0].elapsed_time(ge[reps_g]) / (n * reps_g)), per
+
 
 
 def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries_per_block=-1,
@@ -249,32 +281,7 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
     wall = time.perf_counter() - t_wall0
     eager_ms = e0.elapsed_time(e1) / steps
 
-    def replay_ms(launch, n):
-        """Per-launch time of `n` calls of `launch(stream, k)` captured in one
-        HIP graph and replayed 5 times back to back (HIP events on the
-        capture stream)."""
-        cap_stream = torch.cuda.Stream()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap_stream):
-            for k in range(3):
-                launch(cap_stream.cuda_stream, k)
-            cap_stream.synchronize()
-            with torch.cuda.graph(graph, stream=cap_stream):
-                cs = torch.cuda.current_stream()
-                for k in range(n):
-                    launch(cs.cuda_stream, k)
-            torch.cuda.synchronize()
-            graph.replay()
-            torch.cuda.synchronize()
-            reps_g = 5
-            ge = [torch.cuda.Event(enable_timing=True) for _ in range(reps_g + 1)]
-            ge[0].record(cap_stream)
-            for r in range(reps_g):
-                graph.replay()
-                ge[r + 1].record(cap_stream)
-            torch.cuda.synchronize()
-        per = np.array([ge[r].elapsed_time(ge[r + 1]) / n for r in range(reps_g)])
-        return float(ge[0].elapsed_time(ge[reps_g]) / (n * reps_g)), per
+    replay_ms = graph_replay_ms
 
     def fwd_launch(s, k):
         st = fn(prepared[k % reps], s)
@@ -356,6 +363,75 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
     return out
 
 
+TOPK_SHAPES = {   # rows, per-row counts (complete ratio-4 groups), k
+    "topk_decode": "32 rows of 1024 complete groups (decode CSA, context 4096), k 512",
+    "topk_prefill": "2560 rows, row t holding floor((t+1)/4) complete groups (prefill CSA), k 512",
+}
+
+
+def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0):
+    """Time attn_topk_select on scores over the complete groups of the
+    decode CSA or prefill CSA workload (seeded N(0,1) scores; the pages do
+    not define the indexer's scoring).  One step = one call."""
+    import numpy as np
+    import torch
+    from sparse_paged_attention_amd import api, _lib
+
+    _lib.load()
+    rng = np.random.default_rng(7)
+    k = 512
+    if workload == "topk_decode":
+        n_valid = np.full(32, 1024, dtype=np.int32)
+    else:
+        n_valid = np.array([(t + 1) // 4 for t in range(2560)], dtype=np.int32)
+    ld = int(n_valid.max())
+    scores_h = rng.standard_normal((len(n_valid), ld)).astype(np.float32)
+    rows = len(n_valid)
+    # replicas rotated through so the scores are not L2-resident
+    reps = max(1, int(64e6 // scores_h.nbytes))
+    sc = [torch.from_numpy(scores_h).cuda() for _ in range(reps)]
+    nv = torch.from_numpy(n_valid).cuda()
+    lib = _lib.load()
+    ids = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(rows, dtype=torch.int32, device="cuda")
+
+    def launch(stream, r):
+        _lib.check(lib.attn_topk_select(sc[r % reps].data_ptr(), ld, nv.data_ptr(), rows, k, ids.data_ptr(),
+                                        cnt.data_ptr(), stream))
+
+    for r in range(warmup):
+        api.topk_select(sc[r % reps], nv, k)
+    torch.cuda.synchronize()
+    ms, per = graph_replay_ms(launch, steps)
+    read_b = int(n_valid.sum()) * 4 + rows * 4
+    write_b = rows * k * 4 + rows * 4
+    achieved = (read_b + write_b) / (ms / 1e3) / 1e9
+    cpu = None
+    if cpu_budget > 0:
+        import oracle
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < cpu_budget:
+            i = done % rows
+            oracle.topk_select(scores_h[i:i + 1], n_valid[i:i + 1], k)
+            done += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} rows of the same scores, {dt:.1f} s, numpy"}
+    return {
+        "metric": "top-k selection rows/s (the step before the attention core)",
+        "value": rows / (ms / 1e3), "unit": "rows/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "shape": TOPK_SHAPES[workload], "rows": rows, "k": k, "replicas": reps},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "topk_kernel",
+                     "kernel_ms": ms, "kernel_ms_how": "graph replay of the step (one kernel)",
+                     "algorithmic_bytes_per_launch": read_b + write_b},
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -369,6 +445,10 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_mib > 0:
         print(json.dumps(copy_calibration(args.copy_mib, args.steps)), flush=True)
+        return
+    if args.workload.startswith("topk_"):
+        print(json.dumps(run_topk(args.workload, steps=args.steps, warmup=args.warmup, cpu_budget=args.cpu_budget)),
+              flush=True)
         return
     out = run(args.workload, steps=args.steps, warmup=args.warmup, splits=args.splits,
               heads_per_block=args.heads_per_block, queries_per_block=args.queries_per_block, rotate_mb=args.rotate_mb, batch=args.batch,

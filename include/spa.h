@@ -191,6 +191,26 @@ spa_status attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t 
 spa_status attn_build_gather(const spa_fwd_args *args, int32_t decode, int32_t cap,
                              int64_t *rows_out, int32_t *counts_out, void *stream);
 
+/* Top-k selection of compressed groups from per-token scores: the step
+   before the attention core, whose selected ids become the query's list
+   (cmp_idx / cmp_cnt).  ATOM PR "test: add block-level DeepSeek-V4
+   attention test", sections "What this test actually drives" (the indexer
+   scores, a radix top-k select, then the top-k -> paged offsets pack, which
+   attn_build_gather exports) and "Validation" (the top-k truncates only once
+   the complete groups outnumber it).  The scores themselves come from the
+   caller; the pages do not define the indexer's scoring.
+   For row i: the min(k, n_i) highest of scores[i * ld .. i * ld + n_i - 1],
+   n_i = n_valid[i] clamped to [0, ld], in descending score order, ties by
+   ascending id, -0.0 below +0.0, a NaN score below every number.
+   scores f32 [num_rows, ld] (device, row stride ld); n_valid i32 [num_rows];
+   ids_out i32 [num_rows, k]: ids in that order, -1 past the count;
+   cnt_out i32 [num_rows]: min(k, n_i).  1 <= k <= SPA_MAX_TOPK
+   (SPA_ERR_UNSUPPORTED otherwise), ld >= 1, num_rows >= 0 (SPA_ERR_SHAPE);
+   NULL pointers give SPA_ERR_NULL. */
+#define SPA_MAX_TOPK 2048
+spa_status attn_topk_select(const float *scores, int64_t ld, const int32_t *n_valid, int32_t num_rows,
+                            int32_t k, int32_t *ids_out, int32_t *cnt_out, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *attn_last_error(void);
 

@@ -24,7 +24,8 @@ SPA_MAX_SPLITS = 64
 
 # exported symbols, in include/spa.h order
 SYMBOLS = ("attn_workspace_size", "attn_fwd_decode", "attn_fwd_prefill", "attn_merge_lse",
-           "attn_build_gather", "attn_last_error", "attn_abi_version")
+           "attn_build_gather", "attn_topk_select", "attn_last_error", "attn_abi_version")
+SPA_MAX_TOPK = 2048
 
 
 class SpaFwdArgs(ctypes.Structure):
@@ -102,6 +103,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_build_gather.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_build_gather.restype = ctypes.c_int
+    lib.attn_topk_select.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_topk_select.restype = ctypes.c_int
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []

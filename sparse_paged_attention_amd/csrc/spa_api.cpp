@@ -279,6 +279,20 @@ spa_status attn_build_gather(const spa_fwd_args *args, int32_t decode, int32_t c
   return ok();
 }
 
+spa_status attn_topk_select(const float *scores, int64_t ld, const int32_t *n_valid, int32_t num_rows,
+                            int32_t k, int32_t *ids_out, int32_t *cnt_out, void *stream) {
+  static_assert(SPA_MAX_TOPK == spa::kTopkMax, "header and kernel agree on the top-k limit");
+  if (scores == nullptr || n_valid == nullptr || ids_out == nullptr || cnt_out == nullptr)
+    return fail(SPA_ERR_NULL, "scores, n_valid, ids_out and cnt_out must not be NULL");
+  if (num_rows < 0) return fail(SPA_ERR_SHAPE, "num_rows must be >= 0 (got %d)", num_rows);
+  if (ld < 1) return fail(SPA_ERR_SHAPE, "ld must be >= 1 (got %lld)", (long long)ld);
+  if (k < 1 || k > SPA_MAX_TOPK) return fail(SPA_ERR_UNSUPPORTED, "k %d outside [1, %d]", k, SPA_MAX_TOPK);
+  hipError_t e = spa::launch_topk(scores, ld, n_valid, num_rows, k, ids_out, cnt_out,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "top-k launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char *attn_last_error(void) { return g_last_error.c_str(); }
 
 int32_t attn_abi_version(void) { return 1; }

@@ -66,5 +66,10 @@ hipError_t launch_merge(const float *o_parts, const float *lse_parts, int32_t nu
                         uint16_t *o_out, float *lse_out, int32_t unit_rows, hipStream_t stream);
 hipError_t launch_gather(const Params &p, int32_t cap, int64_t *rows_out, int32_t *counts_out,
                          hipStream_t stream);
+// Top-k selection from per-token scores (spa_topk.hip); k <= kTopkMax, a
+// power of two.
+constexpr int kTopkMax = 2048;
+hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t rows, int32_t k,
+                       int32_t *ids_out, int32_t *cnt_out, hipStream_t stream);
 
 }  // namespace spa

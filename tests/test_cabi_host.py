@@ -185,3 +185,15 @@ def test_gather_validation(lib):
     assert lib.attn_build_gather(ctypes.byref(a), 1, -1, 0x10000000, 0x10000000, None) == -2
     a.head_dim = 32
     assert lib.attn_build_gather(ctypes.byref(a), 1, 16, 0x10000000, 0x10000000, None) == -4
+
+
+def test_topk_validation(lib):
+    """attn_topk_select refuses bad arguments before any HIP call."""
+    P = 0x10000000
+    assert lib.attn_topk_select(None, 8, P, 1, 4, P, P, None) == -1
+    assert lib.attn_topk_select(P, 8, P, 1, 4, None, P, None) == -1
+    assert lib.attn_topk_select(P, 8, P, -1, 4, P, P, None) == -2
+    assert lib.attn_topk_select(P, 0, P, 1, 4, P, P, None) == -2
+    assert lib.attn_topk_select(P, 8, P, 1, 0, P, P, None) == -4
+    assert lib.attn_topk_select(P, 8, P, 1, _lib.SPA_MAX_TOPK + 1, P, P, None) == -4
+    assert b"k " in lib.attn_last_error()
