@@ -14,6 +14,7 @@ Modules:
   formats    bf16 and OCP e4m3 decoding (exact, to float64)
   sparse_attention  KV-set metadata, gather, attention with sink, (O, LSE) merge
   topk       top-k selection of compressed groups from per-token scores
+  backward   gradients of q, the caches and the sink (float64)
   compare    the acceptance comparator
 
 Every function cites the passage it follows.  Pins live in
@@ -26,3 +27,4 @@ from .sparse_attention import (  # noqa: F401
 )
 from .compare import accept, AcceptReport  # noqa: F401
 from .topk import order_key, topk_select  # noqa: F401
+from .backward import Grads, attention_backward, backward_values  # noqa: F401
