@@ -211,6 +211,43 @@ spa_status attn_build_gather(const spa_fwd_args *args, int32_t decode, int32_t c
 spa_status attn_topk_select(const float *scores, int64_t ld, const int32_t *n_valid, int32_t num_rows,
                             int32_t k, int32_t *ids_out, int32_t *cnt_out, void *stream);
 
+/* Backward pass: gradients of q, of both KV caches and of the sink, from
+   the forward's saved O and LSE.  RL-Kernel PR "Roadmap item 24: joint
+   compressed/window attention with sink": section "Reuse and arithmetic"
+   keeps the fp32 LSE for the backward pass that follows the forward; the
+   pages give no formulas, so these are the derivative of the forward's
+   definition.  For one query head with KV rows j, s_j = scale <q, k_j>,
+   p_j = exp(s_j - LSE), dp_j = <dO, v_j>, Delta = <dO, O> and
+   ds_j = p_j (dp_j - Delta):
+     dq = scale sum_j ds_j k_j           (written)
+     dk_j += scale ds_j q, dv_j += p_j dO (accumulated into the row's cache slot)
+     d_sink[h] += -sum_i exp(sink_h - LSE_ih) Delta_ih
+   `args` describes the forward call exactly as it was made (decode when
+   query_seq and query_pos are NULL, else prefill); args->o (bf16) and
+   args->lse are that call's outputs and are read here; num_splits,
+   heads_per_block and queries_per_block are ignored.  Supported: bf16
+   caches, head_dim 128 (SPA_ERR_UNSUPPORTED otherwise).
+   grads->d_o bf16 [Nq, Hq, D], 16-byte aligned; grads->dq f32 [Nq, Hq, D];
+   dk_raw/dv_raw f32 with the raw cache's layout [raw_pages, page_size,
+   Hkv, D]; dk_cmp/dv_cmp f32 with the compressed cache's layout (required
+   when ratio > 0); d_sink f32 [Hq] or NULL (no sink gradient; must be NULL
+   when args->sink is).  The accumulated buffers are zeroed by the caller
+   before the first call; dk/dv are added with float atomics, so their
+   rounding order, and their last bits, vary from run to run.  With d_sink
+   the call needs a workspace of attn_bwd_workspace_size(args) bytes in
+   args->workspace (16-byte aligned; SPA_ERR_WORKSPACE otherwise).  Invalid
+   metadata is flagged and masked as in the forward. */
+typedef struct spa_bwd_grads {
+  const void *d_o;
+  float *dq;
+  float *dk_raw, *dv_raw;
+  float *dk_cmp, *dv_cmp;
+  float *d_sink;
+} spa_bwd_grads;
+
+size_t attn_bwd_workspace_size(const spa_fwd_args *args);
+spa_status attn_bwd(const spa_fwd_args *args, const spa_bwd_grads *grads, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *attn_last_error(void);
 

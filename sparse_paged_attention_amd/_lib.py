@@ -24,7 +24,8 @@ SPA_MAX_SPLITS = 64
 
 # exported symbols, in include/spa.h order
 SYMBOLS = ("attn_workspace_size", "attn_fwd_decode", "attn_fwd_prefill", "attn_merge_lse",
-           "attn_build_gather", "attn_topk_select", "attn_last_error", "attn_abi_version")
+           "attn_build_gather", "attn_topk_select", "attn_bwd_workspace_size", "attn_bwd", "attn_last_error",
+           "attn_abi_version")
 SPA_MAX_TOPK = 2048
 
 
@@ -73,6 +74,19 @@ class SpaFwdArgs(ctypes.Structure):
     ]
 
 
+class SpaBwdGrads(ctypes.Structure):
+    """Mirror of struct spa_bwd_grads."""
+    _fields_ = [
+        ("d_o", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p),
+        ("dk_raw", ctypes.c_void_p),
+        ("dv_raw", ctypes.c_void_p),
+        ("dk_cmp", ctypes.c_void_p),
+        ("dv_cmp", ctypes.c_void_p),
+        ("d_sink", ctypes.c_void_p),
+    ]
+
+
 class SpaError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -106,6 +120,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_topk_select.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_topk_select.restype = ctypes.c_int
+    lib.attn_bwd_workspace_size.argtypes = [P]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [P, ctypes.POINTER(SpaBwdGrads), ctypes.c_void_p]
+    lib.attn_bwd.restype = ctypes.c_int
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []

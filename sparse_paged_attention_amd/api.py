@@ -206,3 +206,42 @@ def topk_select(scores: torch.Tensor, n_valid: torch.Tensor, k: int) -> Tuple[to
     _lib.check(lib.attn_topk_select(_ptr(scores), scores.stride(0) if rows else max(scores.shape[1], 1), _ptr(nv),
                                     rows, k, _ptr(ids), _ptr(cnt), _stream()))
     return ids, cnt
+
+
+def backward(dp: DeviceProblem, o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor, *,
+             err_flag: Optional[torch.Tensor] = None, want_dsink: bool = True,
+             grads: Optional[dict] = None, stream: Optional[int] = None) -> dict:
+    """attn_bwd: gradients of the forward call described by ``dp`` from its
+    outputs (o bf16, lse f32) and the upstream gradient d_o (bf16 [Nq,Hq,D]).
+    Returns dict dq, dk_raw, dv_raw, dk_cmp, dv_cmp, d_sink (f32; the cache
+    gradients have the caches' shapes).  ``grads`` reuses buffers, which the
+    call accumulates into (dq is overwritten)."""
+    lib = _lib.load()
+    dev = dp.q.device
+    if grads is None:
+        grads = {
+            "dq": torch.empty(dp.q.shape, dtype=torch.float32, device=dev),
+            "dk_raw": torch.zeros(dp.k_raw.shape, dtype=torch.float32, device=dev),
+            "dv_raw": torch.zeros(dp.v_raw.shape, dtype=torch.float32, device=dev),
+            "dk_cmp": None if dp.k_cmp is None else torch.zeros(dp.k_cmp.shape, dtype=torch.float32, device=dev),
+            "dv_cmp": None if dp.v_cmp is None else torch.zeros(dp.v_cmp.shape, dtype=torch.float32, device=dev),
+            "d_sink": (torch.zeros(dp.num_q_heads, dtype=torch.float32, device=dev)
+                       if (want_dsink and dp.sink is not None) else None),
+        }
+    args = dp.args(1)
+    args.o = _ptr(o)
+    args.lse = _ptr(lse)
+    args.err_flag = _ptr(err_flag)
+    ws = None
+    if grads["d_sink"] is not None:
+        need = int(lib.attn_bwd_workspace_size(ctypes.byref(args)))
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        args.workspace = _ptr(ws)
+        args.workspace_bytes = ws.numel()
+    g = _lib.SpaBwdGrads()
+    g.d_o = _ptr(d_o)
+    for name in ("dq", "dk_raw", "dv_raw", "dk_cmp", "dv_cmp", "d_sink"):
+        setattr(g, name, _ptr(grads[name]))
+    _lib.check(lib.attn_bwd(ctypes.byref(args), ctypes.byref(g), _stream() if stream is None else stream))
+    grads["_workspace"] = ws        # kept alive until the caller synchronises
+    return grads

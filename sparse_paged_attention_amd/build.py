@@ -15,7 +15,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["spa_api.cpp", "spa_attention.hip", "spa_pair.hip", "spa_merge.hip", "spa_gather.hip", "spa_topk.hip"]
+SOURCES = ["spa_api.cpp", "spa_attention.hip", "spa_pair.hip", "spa_merge.hip", "spa_gather.hip", "spa_topk.hip",
+           "spa_backward.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for every HIP source file.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -293,6 +293,58 @@ spa_status attn_topk_select(const float *scores, int64_t ld, const int32_t *n_va
   return ok();
 }
 
+size_t attn_bwd_workspace_size(const spa_fwd_args *args) {
+  if (args == nullptr || args->num_queries < 0 || args->num_q_heads < 1) return 0;
+  return (size_t)args->num_queries * (size_t)args->num_q_heads * sizeof(float);
+}
+
+spa_status attn_bwd(const spa_fwd_args *args, const spa_bwd_grads *grads, void *stream) {
+  if (args == nullptr || grads == nullptr) return fail(SPA_ERR_NULL, "args/grads is NULL");
+  const bool decode = args->query_seq == nullptr && args->query_pos == nullptr;
+  // the forward's split, block and workspace choices do not apply
+  spa_fwd_args a = *args;
+  a.num_splits = 1;
+  a.heads_per_block = 0;
+  a.queries_per_block = 0;
+  spa_status st = validate(&a, decode, true);
+  if (st != SPA_OK) return st;
+  if (!std::isfinite(a.scale) || !(a.scale > 0.f)) return fail(SPA_ERR_SHAPE, "scale must be finite and > 0");
+  if (a.head_dim != 128) return fail(SPA_ERR_UNSUPPORTED, "the backward takes head_dim 128 (got %d)", a.head_dim);
+  if (a.ratio > 0 && a.cmp_dtype != SPA_BF16) return fail(SPA_ERR_UNSUPPORTED, "the backward takes bf16 caches");
+  if (a.lse == nullptr) return fail(SPA_ERR_NULL, "lse (the forward's) is NULL");
+  if (grads->d_o == nullptr || grads->dq == nullptr || grads->dk_raw == nullptr || grads->dv_raw == nullptr)
+    return fail(SPA_ERR_NULL, "d_o, dq, dk_raw and dv_raw must not be NULL");
+  if (a.ratio > 0 && (grads->dk_cmp == nullptr || grads->dv_cmp == nullptr))
+    return fail(SPA_ERR_NULL, "ratio > 0 needs dk_cmp and dv_cmp");
+  if (grads->d_sink != nullptr && a.sink == nullptr) return fail(SPA_ERR_NULL, "d_sink without a sink");
+  if (!aligned16(grads->d_o) || !aligned16(grads->dq)) return fail(SPA_ERR_ALIGN, "d_o and dq must be 16-byte aligned");
+  spa::Params p = make_params(&a, decode);
+  spa::BwdParams b{};
+  b.d_o = static_cast<const uint16_t *>(grads->d_o);
+  b.o = static_cast<const uint16_t *>(a.o);
+  b.lse = a.lse;
+  b.dq = grads->dq;
+  b.dk_raw = grads->dk_raw;
+  b.dv_raw = grads->dv_raw;
+  b.dk_cmp = a.ratio > 0 ? grads->dk_cmp : nullptr;
+  b.dv_cmp = a.ratio > 0 ? grads->dv_cmp : nullptr;
+  b.dsink = grads->d_sink;
+  b.scale = a.scale;
+  if (grads->d_sink != nullptr) {
+    const size_t need = attn_bwd_workspace_size(&a);
+    if (need > 0 && (a.workspace == nullptr || a.workspace_bytes < need))
+      return fail(SPA_ERR_WORKSPACE, "the sink gradient needs a workspace of %zu bytes", need);
+    if (need > 0 && !aligned16(a.workspace)) return fail(SPA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    b.dsink_part = static_cast<float *>(a.workspace);
+  }
+  if (a.num_queries == 0) return ok();
+  if ((int64_t)a.num_queries * a.num_kv_heads * ((a.num_q_heads / a.num_kv_heads + 63) / 64) > 0x7FFFFFFFLL)
+    return fail(SPA_ERR_SHAPE, "the job count exceeds the launch grid");
+  hipError_t e = spa::launch_backward(p, b, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char *attn_last_error(void) { return g_last_error.c_str(); }
 
 int32_t attn_abi_version(void) { return 1; }

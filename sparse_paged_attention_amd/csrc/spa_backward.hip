@@ -1,0 +1,367 @@
+// Backward of sparse paged attention with a sink, for gfx950 (bf16 caches,
+// D 128).
+//
+// The forward keeps its log-sum-exp for a backward pass (RL-Kernel PR
+// "Roadmap item 24: joint compressed/window attention with sink", section
+// "Reuse and arithmetic").  The pages give no formulas for it; these are
+// the derivative of the forward definition.  For one query head with KV set
+// rows j, scores s_j = scale <q, k_j>, p_j = exp(s_j - LSE) and upstream
+// gradient dO:
+//   dp_j = <dO, v_j>,  Delta = <dO, O>,  ds_j = p_j (dp_j - Delta)
+//   dq = scale sum_j ds_j k_j,  dk_j += scale ds_j q,  dv_j += p_j dO
+//   dsink += -exp(sink - LSE) Delta
+// O and LSE are the forward's outputs; P is recomputed from LSE, so there
+// is no running max.
+//
+// One workgroup of two waves per (query, KV head, block of 64 query heads);
+// wave w owns 32 query heads.  The query's rows are translated through the
+// page tables (the forward's device functions) into an LDS list, chunk by
+// chunk, and streamed as 32-row K and V tiles through two LDS stages with
+// direct global->LDS loads.  Per tile and wave, on v_mfma_f32_32x32x16_bf16:
+//   S^T = K.Q^T and dP^T = V.dO^T (a lane per head): P, dS per head column;
+//   S = Q.K^T and dP = dO.V^T (a lane per KV row): P, dS per row column;
+//   dQ^T += K^T.dS^T      (K^T by transposing LDS reads, as the forward's V^T)
+//   dV = P.dO, dK = dS.Q  (dO and Q of the wave's heads are LDS tiles too,
+//                          read transposed the same way)
+// Computing the scores in both orientations costs two extra MFMA products per
+// tile but puts each of P and dS in the register layout its consumer needs,
+// with no LDS round trip.  dK and dV rows are added to the fp32 gradient
+// caches with float atomics: a lane per head dimension, so each atomic
+// instruction covers 128 contiguous bytes of two rows.  dQ is written once
+// (fp32).  The sink gradient is written per (query, head) and summed over
+// the queries by sink_reduce_kernel, in a fixed order.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "spa_device.h"
+#include "spa_kernel_util.h"
+
+namespace spa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kRowB = 2 * kD;              // bf16 row bytes
+constexpr int kChunks = kRowB / 16;        // 16-byte chunks per row
+constexpr int kPT = 32;                    // KV rows per tile
+constexpr int kTileB = kPT * kRowB;
+constexpr int kBThreads = 128;             // two waves of 32 query heads
+constexpr int kBRows = 1024;               // rows translated per chunk
+constexpr int kBIters = kBRows / kBThreads;
+constexpr int kBStages = 2;
+constexpr int64_t kCmpBit = int64_t(1) << 62;
+
+struct BwdSmem {
+  alignas(16) uint8_t k[kBStages][kTileB];
+  alignas(16) uint8_t v[kBStages][kTileB];
+  alignas(16) uint8_t q[2][kTileB];        // wave w: its 32 heads as tile rows
+  alignas(16) uint8_t dO[2][kTileB];
+  alignas(16) int64_t row[kBRows];         // row * Hkv + g (bit 62: compressed), -1: masked
+  alignas(16) float lse2[64];              // LSE * log2(e); +inf: no softmax (no rows, not a head)
+  alignas(16) float delta[64];
+};
+
+// A K^T, V^T, Q^T or dO^T fragment of a tile in LDS (transposing reads):
+// as the A operand, lane L holds column d = 32 db + L % 32 and the tile rows
+// of k-chunk k2 in the order the S^T accumulator lists its rows.
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t *T, int lane, int db, int k2) {
+  const int G = lane >> 4;
+  const int L = lane & 15;
+  i16x4 f[2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = 16 * k2 + 8 * rr + 4 * (G >> 1) + (L >> 2);
+    const int d = 32 * db + 16 * (G & 1) + 4 * (L & 3);
+    const int off = row * kRowB + (((d >> 3) ^ swz<kChunks>(row)) * 16) + (L & 1) * 8;
+    f[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(T + off));
+  }
+  const i16x8 cat = {f[0][0], f[0][1], f[0][2], f[0][3], f[1][0], f[1][1], f[1][2], f[1][3]};
+  return __builtin_bit_cast(bf16x8, cat);
+}
+
+// Row fragment (natural layout): lane L holds row L % 32, chunk 2 kk + L / 32.
+__device__ __forceinline__ bf16x8 row_frag(const uint8_t *T, int lane, int kk) {
+  const int r = lane & 31;
+  const int c = 2 * kk + (lane >> 5);
+  return *(const bf16x8 *)(T + r * kRowB + ((c ^ swz<kChunks>(r)) * 16));
+}
+
+__global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams b) {
+  __shared__ BwdSmem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hi = lane >> 5;
+  const int hblocks = (p.group + 63) / 64;
+  // heaviest jobs (the last queries of a prefill) first
+  const int64_t job = (int64_t)gridDim.x - 1 - blockIdx.x;
+  const int hb = (int)(job % hblocks);
+  const int64_t u = job / hblocks;
+  const int g = (int)(u % p.hkv);
+  const int i = (int)(u / p.hkv);
+  const QueryKV kv = query_kv(p, i);
+  const int32_t U = kv.n_sel + kv.win_len;
+
+  // ---- Q and dO of the wave's heads: LDS tiles (rows = heads) and the
+  // natural B fragments in registers
+  const int h0 = hb * 64 + wave * 32;                 // first head of the wave, within the group
+  const int64_t qbase = (int64_t)i * p.hq + (int64_t)g * p.group;
+  {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int idx = n * 64 + lane;
+      const int r = idx >> 4, c = idx & 15;
+      const bool ok = h0 + r < p.group;
+      const int64_t off = (qbase + h0 + r) * kD + c * 8;
+      const uint4 qv = ok ? *(const uint4 *)(p.q + off) : uint4{0, 0, 0, 0};
+      const uint4 ov = ok ? *(const uint4 *)(b.d_o + off) : uint4{0, 0, 0, 0};
+      const int dst = r * kRowB + ((c ^ swz<kChunks>(r)) * 16);
+      *(uint4 *)(sm.q[wave] + dst) = qv;
+      *(uint4 *)(sm.dO[wave] + dst) = ov;
+    }
+  }
+  const int hl = h0 + (lane & 31);                    // this lane's head (head-column layouts)
+  const bool hvalid = hl < p.group;
+  bf16x8 qf[kD / 16], dof[kD / 16];
+  {
+    const int64_t off = (qbase + hl) * kD + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < kD / 16; ++kk) {
+      qf[kk] = hvalid ? *(const bf16x8 *)(p.q + off + 16 * kk) : bf16x8{};
+      dof[kk] = hvalid ? *(const bf16x8 *)(b.d_o + off + 16 * kk) : bf16x8{};
+    }
+  }
+  // Delta = <dO, O> of the lane's head (each half of the wave sums 64 of
+  // the D products) and the head's LSE
+  {
+    float dsum = 0.f;
+    if (hvalid) {
+      const int64_t off = (qbase + hl) * kD + 64 * hi;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint4 ov = *(const uint4 *)(b.o + off + 8 * c);
+        const uint4 gv = *(const uint4 *)(b.d_o + off + 8 * c);
+        const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          dsum = __builtin_fmaf(__builtin_bit_cast(float, ow[w] << 16), __builtin_bit_cast(float, gw[w] << 16), dsum);
+          dsum = __builtin_fmaf(__builtin_bit_cast(float, ow[w] & 0xFFFF0000u),
+                                __builtin_bit_cast(float, gw[w] & 0xFFFF0000u), dsum);
+        }
+      }
+    }
+    dsum += __shfl_xor(dsum, 32);
+    if (hi == 0) {
+      const float lse = hvalid ? b.lse[qbase + hl] : INFINITY;
+      const bool live = hvalid && lse != -INFINITY;
+      sm.lse2[wave * 32 + (lane & 31)] = live ? lse * kLog2e : INFINITY;
+      sm.delta[wave * 32 + (lane & 31)] = live ? dsum : 0.f;
+      if (hvalid && b.dsink_part != nullptr) {
+        const float part = (live && p.sink != nullptr) ? -__expf(p.sink[g * p.group + hl] - lse) * dsum : 0.f;
+        b.dsink_part[qbase + hl] = part;
+      }
+    }
+  }
+  __syncthreads();
+  const float my_lse2 = sm.lse2[wave * 32 + (lane & 31)];
+  const float my_delta = sm.delta[wave * 32 + (lane & 31)];
+
+  f32x16 dqa[kD / 32];
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db) dqa[db] = f32x16{};
+
+  const uint8_t *const kraw = in_sgpr(p.k_raw), *const vraw = in_sgpr(p.v_raw);
+  const uint8_t *const kcmp = in_sgpr(p.k_cmp), *const vcmp = in_sgpr(p.v_cmp);
+  float *const dk_raw = in_sgpr(b.dk_raw), *const dv_raw = in_sgpr(b.dv_raw);
+  float *const dk_cmp = in_sgpr(b.dk_cmp), *const dv_cmp = in_sgpr(b.dv_cmp);
+  const float sl2 = p.scale_log2;
+  const float scale = b.scale;
+  // tile loads: wave w moves rows 16w .. 16w+15 of both sides (four 1 KiB
+  // direct loads per side, four rows each); lane L's chunk in load n is
+  // logical chunk (L % 16) ^ swz(row), row = 16w + 4n + L / 16
+  int32_t csrc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int r = 16 * wave + 4 * n + lane / kChunks;
+    csrc[n] = ((lane % kChunks) ^ swz<kChunks>(r)) * 16;
+  }
+
+  for (int32_t c0 = 0; c0 < U; c0 += kBRows) {
+    const int32_t n = min(kBRows, U - c0);
+    const int32_t ntiles = (n + kPT - 1) / kPT;
+    // ---- translate the chunk's rows: list entries, then page tables
+    int32_t xs[kBIters];
+#pragma unroll
+    for (int it = 0; it < kBIters; ++it) {
+      const int32_t e = c0 + tid + it * kBThreads;
+      xs[it] = e < c0 + n ? entry_logical(p, kv, i, e) : -1;
+    }
+#pragma unroll
+    for (int it = 0; it < kBIters; ++it) {
+      const int32_t r = tid + it * kBThreads;
+      if (r < ntiles * kPT) {
+        const int32_t e = c0 + r;
+        int64_t er = -1;
+        if (r < n) {
+          const bool cmp = e < kv.n_sel;
+          const int64_t pr = logical_row(p, kv, cmp, xs[it]);
+          if (pr >= 0) er = (pr * p.hkv + g) | (cmp ? kCmpBit : 0);
+        }
+        sm.row[r] = er;
+      }
+    }
+    __syncthreads();
+
+    auto issue = [&](int j) {
+      const int st = j % kBStages;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int64_t er = sm.row[kPT * j + 16 * wave + 4 * q4 + lane / kChunks];
+        const bool cmp = (er & kCmpBit) != 0;
+        const int64_t off = (er & ~kCmpBit) * kRowB + csrc[q4];
+        dma16(er >= 0 ? (cmp ? kcmp : kraw) + off : kZeroRow + csrc[q4], sm.k[st] + (16 * wave + 4 * q4) * kRowB);
+        dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + csrc[q4], sm.v[st] + (16 * wave + 4 * q4) * kRowB);
+      }
+    };
+
+    issue(0);
+    for (int j = 0; j < ntiles; ++j) {
+      // tile j is in (this wave's loads, then everyone's), and every wave is
+      // done with tile j-1, whose stage the next loads refill; the wait also
+      // covers the previous tile's atomics
+      wait_vmcnt<0>();
+      block_sync();
+      if (j + 1 < ntiles) issue(j + 1);
+      const int st = j % kBStages;
+      const uint8_t *Kt = sm.k[st];
+      const uint8_t *Vt = sm.v[st];
+      const int64_t lrow = sm.row[kPT * j + (lane & 31)];
+      const uint32_t tm = (uint32_t)__ballot(lane < 32 && lrow >= 0);
+      const bool lvalid = lrow >= 0;
+
+      // scores and dP in both orientations
+      f32x16 s_rh = f32x16{}, s_hr = f32x16{}, dp_rh = f32x16{}, dp_hr = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < kD / 16; ++kk) {
+        const bf16x8 kf = row_frag(Kt, lane, kk);
+        s_rh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s_rh, 0, 0, 0);
+        s_hr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kf, s_hr, 0, 0, 0);
+      }
+#pragma unroll
+      for (int kk = 0; kk < kD / 16; ++kk) {
+        const bf16x8 vf = row_frag(Vt, lane, kk);
+        dp_rh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[kk], dp_rh, 0, 0, 0);
+        dp_hr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dof[kk], vf, dp_hr, 0, 0, 0);
+      }
+      // head-column layout: value r is row 8(r/4) + 4hi + r%4 of the tile
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * hi + (r & 3);
+        const float pr = ((tm >> row) & 1u) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s_rh[r], sl2, -my_lse2)) : 0.f;
+        dsb[r >> 3][r & 7] = (__bf16)(pr * (dp_rh[r] - my_delta));
+      }
+      // row-column layout: value r is head 8(r/4) + 4hi + r%4 of the wave
+      bf16x8 pb[2], dsh[2];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 l4 = *(const float4 *)(&sm.lse2[wave * 32 + 8 * q4 + 4 * hi]);
+        const float4 d4 = *(const float4 *)(&sm.delta[wave * 32 + 8 * q4 + 4 * hi]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          const float pr = lvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s_hr[r], sl2, -lv[e])) : 0.f;
+          pb[r >> 3][r & 7] = (__bf16)pr;
+          dsh[r >> 3][r & 7] = (__bf16)(pr * (dp_hr[r] - dv[e]));
+        }
+      }
+      // dQ^T += K^T . dS^T
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Kt, lane, db, k2), dsb[k2], dqa[db], 0, 0, 0);
+      // dV = P . dO and dK = scale dS . Q for the tile's rows, added to the
+      // gradient caches: value r is row 8(r/4) + 4hi + r%4, lane column d
+      int64_t er[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) er[r] = sm.row[kPT * j + 8 * (r >> 2) + 4 * hi + (r & 3)];
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) {
+        f32x16 av = f32x16{}, ak = f32x16{};
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          av = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[k2], tr_frag(sm.dO[wave], lane, db, k2), av, 0, 0, 0);
+          ak = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsh[k2], tr_frag(sm.q[wave], lane, db, k2), ak, 0, 0, 0);
+        }
+        const int d = 32 * db + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (er[r] >= 0) {
+            const bool cmp = (er[r] & kCmpBit) != 0;
+            const int64_t off = (er[r] & ~kCmpBit) * kD + d;
+            unsafeAtomicAdd((cmp ? dv_cmp : dv_raw) + off, av[r]);
+            unsafeAtomicAdd((cmp ? dk_cmp : dk_raw) + off, ak[r] * scale);
+          }
+        }
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();                         // the row list is rewritten by the next chunk
+  }
+
+  // ---- dQ = scale dQ^T^T: lane column = head, value r = d 32db + 8(r/4) + 4hi + r%4
+  if (hvalid) {
+    float *dq = b.dq + (qbase + hl) * kD;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v = {dqa[db][4 * q4] * scale, dqa[db][4 * q4 + 1] * scale, dqa[db][4 * q4 + 2] * scale,
+                          dqa[db][4 * q4 + 3] * scale};
+        *(float4 *)(dq + 32 * db + 8 * q4 + 4 * hi) = v;
+      }
+  }
+}
+
+// dsink[h] += sum over queries of part[i, h], one workgroup per head, in a
+// fixed order (strided partial sums, then a tree).
+__global__ __launch_bounds__(256) void sink_reduce_kernel(const float *part, int32_t nq, int32_t hq, float *dsink) {
+  __shared__ float red[256];
+  const int h = blockIdx.x;
+  float s = 0.f;
+  for (int32_t i = threadIdx.x; i < nq; i += 256) s += part[(int64_t)i * hq + h];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dsink[h] += red[0];
+}
+
+}  // namespace
+
+bool backward_eligible(const Params &p) { return p.head_dim == kD && !p.cmp_fp8; }
+
+hipError_t launch_backward(const Params &p, const BwdParams &b, hipStream_t stream) {
+  if (!backward_eligible(p)) return hipErrorInvalidValue;
+  if (p.num_queries == 0) return hipSuccess;
+  const int64_t blocks = (int64_t)p.num_queries * p.hkv * ((p.group + 63) / 64);
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)blocks), dim3(kBThreads), 0, stream, p, b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (b.dsink != nullptr && b.dsink_part != nullptr) {
+    hipLaunchKernelGGL(sink_reduce_kernel, dim3((unsigned)p.hq), dim3(256), 0, stream, b.dsink_part, p.num_queries,
+                       p.hq, b.dsink);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace spa

@@ -66,10 +66,23 @@ hipError_t launch_merge(const float *o_parts, const float *lse_parts, int32_t nu
                         uint16_t *o_out, float *lse_out, int32_t unit_rows, hipStream_t stream);
 hipError_t launch_gather(const Params &p, int32_t cap, int64_t *rows_out, int32_t *counts_out,
                          hipStream_t stream);
-// Top-k selection from per-token scores (spa_topk.hip); k <= kTopkMax, a
-// power of two.
+// Top-k selection from per-token scores (spa_topk.hip); 1 <= k <= kTopkMax.
 constexpr int kTopkMax = 2048;
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t rows, int32_t k,
                        int32_t *ids_out, int32_t *cnt_out, hipStream_t stream);
+
+// Backward (spa_backward.hip): bf16 caches, D 128.  dq is written; the
+// gradient caches and dsink are accumulated into.
+struct BwdParams {
+  const uint16_t *d_o, *o;            // bf16 [Nq, Hq, D]
+  const float *lse;                   // [Nq, Hq], natural log
+  float *dq;                          // [Nq, Hq, D]
+  float *dk_raw, *dv_raw, *dk_cmp, *dv_cmp;   // the caches' layouts
+  float *dsink_part;                  // [Nq, Hq] scratch, or null (no sink gradient)
+  float *dsink;                       // [Hq], or null
+  float scale;
+};
+bool backward_eligible(const Params &p);
+hipError_t launch_backward(const Params &p, const BwdParams &b, hipStream_t stream);
 
 }  // namespace spa

@@ -197,3 +197,60 @@ def test_topk_validation(lib):
     assert lib.attn_topk_select(P, 8, P, 1, 0, P, P, None) == -4
     assert lib.attn_topk_select(P, 8, P, 1, _lib.SPA_MAX_TOPK + 1, P, P, None) == -4
     assert b"k " in lib.attn_last_error()
+
+
+def test_bwd_grads_layout_matches_header(tmp_path):
+    fields = [f[0] for f in _lib.SpaBwdGrads._fields_]
+    src = tmp_path / "bwd_layout.c"
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(spa_bwd_grads, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "spa.h"\nint main(void){\n'
+                   + body + '\n  printf("SIZE %zu\\n", sizeof(spa_bwd_grads));\n  return 0;\n}\n')
+    exe = tmp_path / "bwd_layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = dict(line.split() for line in out if line)
+    for f in fields:
+        assert int(got[f]) == getattr(_lib.SpaBwdGrads, f).offset, f
+    assert int(got["SIZE"]) == ctypes.sizeof(_lib.SpaBwdGrads)
+
+
+def _good_grads():
+    g = _lib.SpaBwdGrads()
+    for i, f in enumerate(["d_o", "dq", "dk_raw", "dv_raw", "dk_cmp", "dv_cmp", "d_sink"]):
+        setattr(g, f, 0x40000000 + 0x1000 * i)
+    return g
+
+
+BWD_FAULTS = [
+    ("null_grads", None, None, -1),
+    ("null_dq", None, lambda g: setattr(g, "dq", None), -1),
+    ("null_dk_cmp_with_ratio", None, lambda g: setattr(g, "dk_cmp", None), -1),
+    ("null_lse", lambda a: setattr(a, "lse", None), None, -1),
+    ("null_o", lambda a: setattr(a, "o", None), None, -1),
+    ("d_sink_without_sink", lambda a: setattr(a, "sink", None), None, -1),
+    ("head_dim_64", lambda a: setattr(a, "head_dim", 64), None, -4),
+    ("fp8_cache", lambda a: (setattr(a, "cmp_dtype", _lib.SPA_FP8_E4M3_OCP), setattr(a, "k_cmp_scale", 0x30000000),
+                             setattr(a, "v_cmp_scale", 0x30001000)), None, -4),
+    ("misaligned_d_o", None, lambda g: setattr(g, "d_o", g.d_o + 2), -5),
+    ("no_workspace_for_dsink", None, None, -6),
+    ("scale_negative", lambda a: setattr(a, "scale", -1.0), None, -2),
+    ("positions_half_given", lambda a: setattr(a, "query_pos", 0x20000000), None, -9),
+]
+
+
+@pytest.mark.parametrize("name,mut_a,mut_g,code", BWD_FAULTS, ids=[f[0] for f in BWD_FAULTS])
+def test_backward_validation(lib, name, mut_a, mut_g, code):
+    """attn_bwd refuses bad arguments before any HIP call."""
+    a = _good_args()
+    g = _good_grads()
+    if name != "no_workspace_for_dsink":
+        a.workspace = 0x50000000
+        a.workspace_bytes = lib.attn_bwd_workspace_size(ctypes.byref(a))
+    if mut_a:
+        mut_a(a)
+    if mut_g:
+        mut_g(g)
+    st = lib.attn_bwd(ctypes.byref(a), None if name == "null_grads" else ctypes.byref(g), None)
+    assert st == code, (name, st, lib.attn_last_error())
+    assert lib.attn_last_error().decode()
+    assert lib.attn_bwd_workspace_size(None) == 0
