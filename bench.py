@@ -159,7 +159,7 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_csa",
                     choices=["decode_csa", "decode_hca", "mixed_fp8", "prefill_csa", "tiny", "topk_decode",
-                             "topk_prefill"])
+                             "topk_prefill", "bwd_prefill_csa"])
     ap.add_argument("--batch", type=int, default=0, help="decode batch override (0 = the workload's)")
     ap.add_argument("--splits", type=int, default=0, help="0 = the default for the workload")
     ap.add_argument("--heads-per-block", type=int, default=-1,
@@ -432,6 +432,98 @@ def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0):
     }
 
 
+def run_backward(workload, *, steps=20, warmup=3, cpu_budget=0.0, rotate_mb=640.0):
+    """Time attn_bwd on the prefill CSA workload: one step = one backward call
+    (the attention kernel's gradients plus the fixed-order sink reduction)
+    from the forward's own O and LSE, with a seeded N(0,1) bf16 upstream
+    gradient.  The gradient caches accumulate across steps (zeroing them is
+    the caller's and is not timed)."""
+    import ctypes
+    import dataclasses
+
+    import numpy as np
+    import torch
+    from sparse_paged_attention_amd import api, synth, _lib
+
+    lib = _lib.load()
+    p = synth.make_workload(workload.replace("bwd_", ""))
+    base = api.DeviceProblem.from_problem(p)
+    cap = p.window + p.topk + 1
+    _, counts = api.build_gather(base, cap)
+    counts = counts.cpu().numpy()
+    _, fwd_flops, kv_entries = algorithmic_work(p, counts)
+    alg_flops = fwd_flops // 4 * 10          # S, dP, dQ, dK, dV: 2 Hq D flops each per (query, entry)
+    nq, Hq, D = p.num_queries, p.num_q_heads, p.head_dim
+    rng = np.random.default_rng(5)
+    dO_bits = synth.f32_to_bf16_bits(rng.standard_normal(p.q.shape).astype(np.float32))
+    per_rep = nq * Hq * D * (2 * 3 + 4) + nq * Hq * 8   # q, dO, O (bf16), dq (f32), lse, sink parts
+    reps = max(1, math.ceil(rotate_mb * 1e6 / per_rep))
+    sets = []
+    g = {
+        "dk_raw": torch.zeros(base.k_raw.shape, dtype=torch.float32, device="cuda"),
+        "dv_raw": torch.zeros(base.v_raw.shape, dtype=torch.float32, device="cuda"),
+        "dk_cmp": torch.zeros(base.k_cmp.shape, dtype=torch.float32, device="cuda"),
+        "dv_cmp": torch.zeros(base.v_cmp.shape, dtype=torch.float32, device="cuda"),
+        "d_sink": torch.zeros(Hq, dtype=torch.float32, device="cuda"),
+    }
+    for r in range(reps):
+        dp = dataclasses.replace(base, q=base.q.clone())
+        o, lse = api.forward(dp)
+        d_o = torch.from_numpy(dO_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        args = dp.args(1)
+        args.o, args.lse = o.data_ptr(), lse.data_ptr()
+        ws = torch.empty(int(lib.attn_bwd_workspace_size(ctypes.byref(args))), dtype=torch.uint8, device="cuda")
+        args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+        dq = torch.empty(p.q.shape, dtype=torch.float32, device="cuda")
+        gr = _lib.SpaBwdGrads()
+        gr.d_o, gr.dq = d_o.data_ptr(), dq.data_ptr()
+        for name in ("dk_raw", "dv_raw", "dk_cmp", "dv_cmp", "d_sink"):
+            setattr(gr, name, g[name].data_ptr())
+        sets.append((args, gr, (dp, o, lse, d_o, ws, dq)))
+    torch.cuda.synchronize()
+
+    def launch(stream, k):
+        a, gr, _ = sets[k % reps]
+        _lib.check(lib.attn_bwd(ctypes.byref(a), ctypes.byref(gr), stream))
+
+    for k in range(warmup):
+        launch(torch.cuda.current_stream().cuda_stream, k)
+    torch.cuda.synchronize()
+    ms, per = graph_replay_ms(launch, steps)
+    achieved = alg_flops / (ms / 1e3) / 1e12
+    cpu = None
+    if cpu_budget > 0:
+        import oracle
+        from oracle.backward import attention_backward
+        t0 = time.perf_counter()
+        done = 0
+        stride = 37                       # a spread of positions, short and long sets
+        while time.perf_counter() - t0 < cpu_budget:
+            i = (done * stride) % nq
+            sub = dataclasses.replace(p, q=p.q[[i]], query_seq=p.query_seq[[i]], query_pos=p.query_pos[[i]],
+                                      cmp_idx=p.cmp_idx[[i]], cmp_cnt=p.cmp_cnt[[i]])
+            attention_backward(sub, dO_bits[[i]])
+            done += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} query tokens of the workload (every 37th position), {dt:.1f} s, numpy fp64"}
+    return {
+        "metric": "backward tokens/s (dq, dk, dv, dsink from O and LSE)",
+        "value": nq / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "queries": nq, "q_heads": Hq, "kv_heads": p.num_kv_heads, "head_dim": D,
+                   "window": p.window, "ratio": p.ratio, "topk": p.topk, "kv_entries": kv_entries,
+                   "replicas": reps},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "attn_bwd_kernel",
+                     "kernel_ms": ms, "kernel_ms_how": "graph replay of the step (backward kernel + sink reduction)",
+                     "algorithmic_flops_per_launch": alg_flops},
+        "cpu_baseline": cpu,
+        "timing": {"graph_replay_ms_per_step_min": float(per.min()), "graph_replay_ms_per_step_max": float(per.max())},
+    }
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -445,6 +537,10 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_mib > 0:
         print(json.dumps(copy_calibration(args.copy_mib, args.steps)), flush=True)
+        return
+    if args.workload.startswith("bwd_"):
+        print(json.dumps(run_backward(args.workload, steps=min(args.steps, 50), warmup=min(args.warmup, 5),
+                                      cpu_budget=args.cpu_budget)), flush=True)
         return
     if args.workload.startswith("topk_"):
         print(json.dumps(run_topk(args.workload, steps=args.steps, warmup=args.warmup, cpu_budget=args.cpu_budget)),

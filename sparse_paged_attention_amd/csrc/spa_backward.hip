@@ -21,13 +21,15 @@
 //   S^T = K.Q^T and dP^T = V.dO^T (a lane per head): P, dS per head column;
 //   S = Q.K^T and dP = dO.V^T (a lane per KV row): P, dS per row column;
 //   dQ^T += K^T.dS^T      (K^T by transposing LDS reads, as the forward's V^T)
-//   dV = P.dO, dK = dS.Q  (dO and Q of the wave's heads are LDS tiles too,
-//                          read transposed the same way)
+//   dV = P.dO, dK = dS.Q  over all 64 heads, for half the head dimensions
+//                          per wave (P and dS swapped through LDS; dO and Q
+//                          are LDS tiles too, read transposed the same way)
 // Computing the scores in both orientations costs two extra MFMA products per
 // tile but puts each of P and dS in the register layout its consumer needs,
 // with no LDS round trip.  dK and dV rows are added to the fp32 gradient
-// caches with float atomics: a lane per head dimension, so each atomic
-// instruction covers 128 contiguous bytes of two rows.  dQ is written once
+// caches with float atomics, once per workgroup and element: a lane per head
+// dimension, so each atomic instruction covers 128 contiguous bytes of two
+// rows.  dQ is written once
 // (fp32).  The sink gradient is written per (query, head) and summed over
 // the queries by sink_reduce_kernel, in a fixed order.
 
@@ -47,7 +49,7 @@ constexpr int kChunks = kRowB / 16;        // 16-byte chunks per row
 constexpr int kPT = 32;                    // KV rows per tile
 constexpr int kTileB = kPT * kRowB;
 constexpr int kBThreads = 128;             // two waves of 32 query heads
-constexpr int kBRows = 1024;               // rows translated per chunk
+constexpr int kBRows = 512;                // rows translated per chunk
 constexpr int kBIters = kBRows / kBThreads;
 constexpr int kBStages = 2;
 constexpr int64_t kCmpBit = int64_t(1) << 62;
@@ -58,6 +60,8 @@ struct BwdSmem {
   alignas(16) uint8_t q[2][kTileB];        // wave w: its 32 heads as tile rows
   alignas(16) uint8_t dO[2][kTileB];
   alignas(16) int64_t row[kBRows];         // row * Hkv + g (bit 62: compressed), -1: masked
+  alignas(16) bf16x8 xp[2][2][64];         // P and dS of each wave's heads, A-fragment order
+  alignas(16) bf16x8 xd[2][2][64];
   alignas(16) float lse2[64];              // LSE * log2(e); +inf: no softmax (no rows, not a head)
   alignas(16) float delta[64];
 };
@@ -285,18 +289,31 @@ __global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
           dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Kt, lane, db, k2), dsb[k2], dqa[db], 0, 0, 0);
-      // dV = P . dO and dK = scale dS . Q for the tile's rows, added to the
-      // gradient caches: value r is row 8(r/4) + 4hi + r%4, lane column d
+      // dV = P . dO and dK = scale dS . Q for the tile's rows over all 64
+      // heads: the waves swap their P and dS fragments through LDS, and wave
+      // w takes head dimensions 64w .. 64w+63, so each gradient element is
+      // added once per workgroup.  Value r is row 8(r/4) + 4hi + r%4, lane
+      // column d.
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        sm.xp[wave][k2][lane] = pb[k2];
+        sm.xd[wave][k2][lane] = dsh[k2];
+      }
       int64_t er[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) er[r] = sm.row[kPT * j + 8 * (r >> 2) + 4 * hi + (r & 3)];
+      block_sync();
 #pragma unroll
-      for (int db = 0; db < kD / 32; ++db) {
+      for (int dbi = 0; dbi < 2; ++dbi) {
+        const int db = 2 * wave + dbi;
         f32x16 av = f32x16{}, ak = f32x16{};
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          av = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[k2], tr_frag(sm.dO[wave], lane, db, k2), av, 0, 0, 0);
-          ak = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsh[k2], tr_frag(sm.q[wave], lane, db, k2), ak, 0, 0, 0);
+        for (int kc = 0; kc < 4; ++kc) {
+          const int w2 = kc >> 1, k2 = kc & 1;
+          av = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sm.xp[w2][k2][lane], tr_frag(sm.dO[w2], lane, db, k2), av, 0,
+                                                       0, 0);
+          ak = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sm.xd[w2][k2][lane], tr_frag(sm.q[w2], lane, db, k2), ak, 0,
+                                                       0, 0);
         }
         const int d = 32 * db + (lane & 31);
 #pragma unroll
