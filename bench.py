@@ -32,6 +32,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
                   for f in ("spa_attention.hip", "spa_pair.hip", "spa_kernel_util.h", "spa_device.h",
                             "spa_internal.h", "spa_api.cpp")]
+# sources of the top-k and backward kernels (their traffic entries carry these hashes)
+TOPK_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
+                for f in ("spa_topk.hip", "spa_internal.h", "spa_api.cpp")]
+BWD_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
+               for f in ("spa_backward.hip", "spa_kernel_util.h", "spa_device.h", "spa_internal.h", "spa_api.cpp")]
 PAIR_ROWS_MAX = 1280           # rows a query pair's union can hold in the prefill pair kernel
 
 
@@ -58,16 +63,16 @@ def attention_kernel(p, splits, hpb, qpb):
     return "attn_fwd_kernel"
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=None):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES if files is None else files):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, cfg):
+def measured_traffic(workload, cfg, files=None, keys=("batch", "num_splits", "heads_per_block", "queries_per_block")):
     """HBM bytes per attention launch from the committed counter runs
     (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or
     None when none matches this workload, launch configuration and kernel
@@ -78,10 +83,9 @@ def measured_traffic(workload, cfg):
     except (OSError, ValueError):
         return None
     e = data.get(workload)
-    if not e or e.get("kernel_source") != kernel_source_hash():
+    if not e or e.get("kernel_source") != kernel_source_hash(files):
         return None
-    if any(e.get("config", {}).get(k) != cfg.get(k) for k in ("batch", "num_splits", "heads_per_block",
-                                                                "queries_per_block")):
+    if any(e.get("config", {}).get(k) != cfg.get(k) for k in keys):
         return None
     return e.get("bytes_per_launch")
 
@@ -181,6 +185,22 @@ DEFAULTS = {   # (num_splits, heads_per_block, queries_per_block) per workload; 
     "decode_csa": (4, 0, 0), "decode_hca": (4, 0, 0), "mixed_fp8": (8, 0, 0), "prefill_csa": (1, 0, 0),
     "tiny": (1, 0, 0),
 }
+
+
+def eager_ms(launch, n):
+    """Per-launch time of `n` host launches of `launch(stream, k)` (HIP
+    events on the current stream); also the per-launch mean as an array."""
+    import numpy as np
+    import torch
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for k in range(n):
+        launch(s.cuda_stream, k)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    return ms, np.array([ms])
 
 
 def graph_replay_ms(launch, n):
@@ -369,7 +389,7 @@ TOPK_SHAPES = {   # rows, per-row counts (complete ratio-4 groups), k
 }
 
 
-def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0):
+def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0, eager_only=False):
     """Time attn_topk_select on scores over the complete groups of the
     decode CSA or prefill CSA workload (seeded N(0,1) scores; the pages do
     not define the indexer's scoring).  One step = one call."""
@@ -402,7 +422,7 @@ def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0):
     for r in range(warmup):
         api.topk_select(sc[r % reps], nv, k)
     torch.cuda.synchronize()
-    ms, per = graph_replay_ms(launch, steps)
+    ms, per = eager_ms(launch, steps) if eager_only else graph_replay_ms(launch, steps)
     read_b = int(n_valid.sum()) * 4 + rows * 4
     write_b = rows * k * 4 + rows * 4
     achieved = (read_b + write_b) / (ms / 1e3) / 1e9
@@ -426,13 +446,14 @@ def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0):
         "config": {"workload": workload, "shape": TOPK_SHAPES[workload], "rows": rows, "k": k, "replicas": reps},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "topk_kernel",
-                     "kernel_ms": ms, "kernel_ms_how": "graph replay of the step (one kernel)",
+                     "kernel_ms": ms, "kernel_ms_how": ("host-launched calls" if eager_only
+                                                        else "graph replay of the step (one kernel)"),
                      "algorithmic_bytes_per_launch": read_b + write_b},
         "cpu_baseline": cpu,
-    }
+    } | {"_traffic": measured_traffic(workload, {"rows": rows, "k": k}, TOPK_SOURCES, ("rows", "k"))}
 
 
-def run_backward(workload, *, steps=20, warmup=3, cpu_budget=0.0, rotate_mb=640.0):
+def run_backward(workload, *, steps=20, warmup=3, cpu_budget=0.0, rotate_mb=640.0, eager_only=False):
     """Time attn_bwd on the prefill CSA workload: one step = one backward call
     (the attention kernel's gradients plus the fixed-order sink reduction)
     from the forward's own O and LSE, with a seeded N(0,1) bf16 upstream
@@ -489,7 +510,7 @@ def run_backward(workload, *, steps=20, warmup=3, cpu_budget=0.0, rotate_mb=640.
     for k in range(warmup):
         launch(torch.cuda.current_stream().cuda_stream, k)
     torch.cuda.synchronize()
-    ms, per = graph_replay_ms(launch, steps)
+    ms, per = eager_ms(launch, steps) if eager_only else graph_replay_ms(launch, steps)
     achieved = alg_flops / (ms / 1e3) / 1e12
     cpu = None
     if cpu_budget > 0:
@@ -517,11 +538,12 @@ def run_backward(workload, *, steps=20, warmup=3, cpu_budget=0.0, rotate_mb=640.
                    "replicas": reps},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "attn_bwd_kernel",
-                     "kernel_ms": ms, "kernel_ms_how": "graph replay of the step (backward kernel + sink reduction)",
+                     "kernel_ms": ms, "kernel_ms_how": ("host-launched calls" if eager_only else
+                                                        "graph replay of the step (backward kernel + sink reduction)"),
                      "algorithmic_flops_per_launch": alg_flops},
         "cpu_baseline": cpu,
         "timing": {"graph_replay_ms_per_step_min": float(per.min()), "graph_replay_ms_per_step_max": float(per.max())},
-    }
+    } | {"_traffic": measured_traffic(workload, {"queries": nq}, BWD_SOURCES, ("queries",))}
 
 
 def main():
@@ -539,12 +561,16 @@ def main():
         print(json.dumps(copy_calibration(args.copy_mib, args.steps)), flush=True)
         return
     if args.workload.startswith("bwd_"):
-        print(json.dumps(run_backward(args.workload, steps=min(args.steps, 50), warmup=min(args.warmup, 5),
-                                      cpu_budget=args.cpu_budget)), flush=True)
+        out = run_backward(args.workload, steps=min(args.steps, 50), warmup=min(args.warmup, 5),
+                           cpu_budget=args.cpu_budget, eager_only=args.eager_only)
+        out["roofline"]["traffic"] = out.pop("_traffic")
+        print(json.dumps(out), flush=True)
         return
     if args.workload.startswith("topk_"):
-        print(json.dumps(run_topk(args.workload, steps=args.steps, warmup=args.warmup, cpu_budget=args.cpu_budget)),
-              flush=True)
+        out = run_topk(args.workload, steps=args.steps, warmup=args.warmup, cpu_budget=args.cpu_budget,
+                       eager_only=args.eager_only)
+        out["roofline"]["traffic"] = out.pop("_traffic")
+        print(json.dumps(out), flush=True)
         return
     out = run(args.workload, steps=args.steps, warmup=args.warmup, splits=args.splits,
               heads_per_block=args.heads_per_block, queries_per_block=args.queries_per_block, rotate_mb=args.rotate_mb, batch=args.batch,
