@@ -30,7 +30,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the sources whose change invalidates counter-measured traffic
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
-                  for f in ("spa_attention.hip", "spa_pair.hip", "spa_kernel_util.h", "spa_device.h",
+                  for f in ("spa_attention.hip", "spa_pair.hip", "spa_latent.hip", "spa_kernel_util.h", "spa_device.h",
                             "spa_internal.h", "spa_api.cpp")]
 # sources of the top-k and backward kernels (their traffic entries carry these hashes)
 TOPK_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
@@ -46,6 +46,8 @@ def attention_kernel(p, splits, hpb, qpb):
     the caller's) is query pairs, else the one-query-per-job kernel.  Mirrors
     the selection in spa_api.cpp (the decode-slice kernel for a decode the
     library sizes itself)."""
+    if p.head_dim == 512:
+        return "attn_latent_kernel"
     pairs_ok = (p.mode == "prefill" and p.head_dim == 128 and not p.cmp_fp8 and splits == 1
                 and (p.ratio == 0 or p.topk > 0) and 2 * (p.topk + p.window) <= PAIR_ROWS_MAX)
     pairs = pairs_ok and (qpb == 2 or (qpb == 0 and hpb != 32))
@@ -114,12 +116,14 @@ def algorithmic_work(p, counts):
     """Bytes and FLOPs the method must move / compute for one call.
 
     Per query: Q and O (bf16), LSE (fp32), every KV entry of its set once
-    (K and V rows, plus the fp32 per-token scales for e4m3 rows) and the list
+    (K and V rows, one row for a shared latent cache, plus the fp32 per-token
+    scales for e4m3 rows) and the list
     indices; FLOPs = 4 * Hq * D * |KV set|.  Page-table reads, split
     partials and masked work are overhead and not counted."""
     Hq, Hkv, D = p.num_q_heads, p.num_kv_heads, p.head_dim
-    raw_entry = Hkv * 2 * D * 2
-    cmp_entry = Hkv * 2 * D * (1 if p.cmp_fp8 else 2) + (Hkv * 2 * 4 if p.cmp_fp8 else 0)
+    sides = 1 if p.v_raw is p.k_raw else 2       # a shared latent row is K and V
+    raw_entry = Hkv * sides * D * 2
+    cmp_entry = Hkv * sides * D * (1 if p.cmp_fp8 else 2) + (Hkv * 2 * 4 if p.cmp_fp8 else 0)
     win_len = counts[:, 1].astype("int64")
     n_sel = counts[:, 3].astype("int64")
     nq = counts.shape[0]
@@ -162,8 +166,8 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_csa",
-                    choices=["decode_csa", "decode_hca", "mixed_fp8", "prefill_csa", "tiny", "topk_decode",
-                             "topk_prefill", "bwd_prefill_csa"])
+                    choices=["decode_csa", "decode_hca", "mixed_fp8", "prefill_csa", "tiny", "decode_latent",
+                             "topk_decode", "topk_prefill", "bwd_prefill_csa"])
     ap.add_argument("--batch", type=int, default=0, help="decode batch override (0 = the workload's)")
     ap.add_argument("--splits", type=int, default=0, help="0 = the default for the workload")
     ap.add_argument("--heads-per-block", type=int, default=-1,
@@ -183,7 +187,7 @@ def parse_args(argv=None):
 
 DEFAULTS = {   # (num_splits, heads_per_block, queries_per_block) per workload; 0 = library choice
     "decode_csa": (4, 0, 0), "decode_hca": (4, 0, 0), "mixed_fp8": (8, 0, 0), "prefill_csa": (1, 0, 0),
-    "tiny": (1, 0, 0),
+    "tiny": (1, 0, 0), "decode_latent": (4, 0, 0),
 }
 
 
@@ -260,13 +264,19 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
 
     # replicas: the KV rows read per step plus Q/O, rotated so the set is HBM-cold
     reps = max(1, math.ceil(rotate_mb * 1e6 / max(alg_bytes, 1)))
-    pool_bytes = sum(t.numel() * t.element_size() for t in (base.k_raw, base.v_raw, base.k_cmp, base.v_cmp)
-                     if t is not None)
+    pools = {id(t): t for t in (base.k_raw, base.v_raw, base.k_cmp, base.v_cmp) if t is not None}
+    pool_bytes = sum(t.numel() * t.element_size() for t in pools.values())
     reps = min(reps, max(1, int(48e9 // max(pool_bytes, 1))))
     replicas = []
+
+    def clone_problem():
+        # one clone per distinct tensor, so a shared latent cache stays shared
+        memo = {}
+        return api.DeviceProblem(**{k: (memo.setdefault(id(v), v.clone()) if isinstance(v, torch.Tensor) else v)
+                                    for k, v in base.__dict__.items()})
+
     for r in range(reps):
-        dp = base if r == 0 else api.DeviceProblem(
-            **{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in base.__dict__.items()})
+        dp = base if r == 0 else clone_problem()
         a = dp.args(splits, hpb, qpb)
         o = torch.empty((p.num_queries, p.num_q_heads, p.head_dim), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((p.num_queries, p.num_q_heads), dtype=torch.float32, device=dev)

@@ -71,14 +71,19 @@ class DeviceProblem:
             return dev(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
 
         has_cmp = p.ratio > 0
+        # a shared latent cache (value arrays that are the key arrays) stays
+        # one device buffer, so the library sees K == V
+        k_raw = bits16(p.k_raw)
+        k_cmp = (dev(p.k_cmp) if p.cmp_fp8 else bits16(p.k_cmp)) if has_cmp else None
         return cls(
             mode=p.mode, num_seqs=p.num_seqs, num_queries=p.num_queries,
             num_q_heads=p.num_q_heads, num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
             page_size=p.page_size, window=p.window, ratio=p.ratio, topk=p.topk,
             scale=float(np.float32(p.scale)), cmp_fp8=bool(p.cmp_fp8), num_splits=p.num_splits,
-            q=bits16(p.q), k_raw=bits16(p.k_raw), v_raw=bits16(p.v_raw),
-            k_cmp=(dev(p.k_cmp) if p.cmp_fp8 else bits16(p.k_cmp)) if has_cmp else None,
-            v_cmp=(dev(p.v_cmp) if p.cmp_fp8 else bits16(p.v_cmp)) if has_cmp else None,
+            q=bits16(p.q), k_raw=k_raw, v_raw=k_raw if p.v_raw is p.k_raw else bits16(p.v_raw),
+            k_cmp=k_cmp,
+            v_cmp=(k_cmp if p.v_cmp is p.k_cmp else (dev(p.v_cmp) if p.cmp_fp8 else bits16(p.v_cmp))) if has_cmp
+            else None,
             k_cmp_scale=dev(p.k_cmp_scale) if (has_cmp and p.cmp_fp8) else None,
             v_cmp_scale=dev(p.v_cmp_scale) if (has_cmp and p.cmp_fp8) else None,
             raw_pt=dev(p.raw_pt), cmp_pt=dev(p.cmp_pt) if has_cmp else None,

@@ -59,8 +59,17 @@ spa_status validate(const spa_fwd_args *a, bool decode, bool need_outputs) {
   if (a->raw_pages < 1) return fail(SPA_ERR_SHAPE, "raw_pages must be >= 1");
   if (a->ratio > 0 && (a->cmp_pt_stride < 1 || a->cmp_pages < 1))
     return fail(SPA_ERR_SHAPE, "ratio > 0 needs cmp_pt_stride >= 1 and cmp_pages >= 1");
-  if (a->head_dim != 64 && a->head_dim != 128)
-    return fail(SPA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", a->head_dim);
+  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 512)
+    return fail(SPA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128 or 512)", a->head_dim);
+  if (a->head_dim == 512) {
+    // the 512-wide path is the shared latent cache: one row is K and V
+    if (a->k_raw != a->v_raw || (a->ratio > 0 && a->k_cmp != a->v_cmp))
+      return fail(SPA_ERR_UNSUPPORTED, "head_dim 512 needs a shared latent cache (k_raw == v_raw, k_cmp == v_cmp)");
+    if (a->ratio > 0 && a->cmp_dtype != SPA_BF16)
+      return fail(SPA_ERR_UNSUPPORTED, "head_dim 512 takes bf16 caches");
+    if (a->heads_per_block != 0 || a->queries_per_block != 0)
+      return fail(SPA_ERR_UNSUPPORTED, "head_dim 512 takes heads_per_block 0 and queries_per_block 0");
+  }
   if (a->raw_dtype != SPA_BF16) return fail(SPA_ERR_DTYPE, "raw_dtype must be SPA_BF16 (got %d)", a->raw_dtype);
   if (a->cmp_dtype != SPA_BF16 && a->cmp_dtype != SPA_FP8_E4M3_OCP)
     return fail(SPA_ERR_DTYPE, "cmp_dtype %d unknown", a->cmp_dtype);
@@ -206,7 +215,7 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
   // Prefill: query pairs share each KV tile when the call fits that kernel
   // (the library's choice unless the caller asks for 32-head jobs or one
   // query per job); the result does not depend on the choice.
-  const bool pairs_ok = !decode && spa::prefill_pairs_eligible(p);
+  const bool pairs_ok = !decode && a->head_dim != 512 && spa::prefill_pairs_eligible(p);
   if (a->queries_per_block == 2 && !pairs_ok)
     return fail(SPA_ERR_UNSUPPORTED,
                 "queries_per_block 2 needs bf16 caches, head_dim 128, one split, a top-k list or no "
@@ -217,7 +226,9 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
   // it and the caller leaves both block sizes to the library.
   const bool slices = decode && a->heads_per_block == 0 && a->queries_per_block == 0 &&
                       spa::decode_slices_eligible(p);
-  hipError_t e = pairs ? spa::launch_prefill_pairs(p, s)
+  const bool latent = a->head_dim == 512;
+  hipError_t e = latent   ? spa::launch_latent(p, s)
+                 : pairs  ? spa::launch_prefill_pairs(p, s)
                  : slices ? spa::launch_decode_slices(p, s)
                           : spa::launch_attention(p, s);
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
@@ -225,7 +236,7 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
     // the job-stream kernel writes each (query, KV head) unit's partials on
     // one XCD and the merge reads them there; the slice kernel in row order
     e = spa::launch_merge(p.part_o, p.part_lse, a->num_splits, (int64_t)a->num_queries * a->num_q_heads,
-                          a->head_dim, a->num_q_heads, a->sink, p.o, a->lse, slices ? 0 : p.group, s);
+                          a->head_dim, a->num_q_heads, a->sink, p.o, a->lse, (slices || latent) ? 0 : p.group, s);
     if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
   }
   return ok();
@@ -237,7 +248,7 @@ extern "C" {
 
 size_t attn_workspace_size(const spa_fwd_args *args) {
   if (args == nullptr || args->num_splits < 1 || args->num_queries < 0 || args->num_q_heads < 1) return 0;
-  if (args->head_dim != 64 && args->head_dim != 128) return 0;
+  if (args->head_dim != 64 && args->head_dim != 128 && args->head_dim != 512) return 0;
   return workspace_bytes_for(args);
 }
 
@@ -254,8 +265,8 @@ spa_status attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t 
     return fail(SPA_ERR_SPLITS, "num_parts %d outside [1, %d]", num_parts, SPA_MAX_SPLITS);
   if (rows < 0) return fail(SPA_ERR_SHAPE, "rows must be >= 0");
   if (num_q_heads < 1) return fail(SPA_ERR_SHAPE, "num_q_heads must be >= 1");
-  if (head_dim != 64 && head_dim != 128)
-    return fail(SPA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 512)
+    return fail(SPA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128 or 512)", head_dim);
   if ((rows + 7) / 8 > 0x7FFFFFFFLL) return fail(SPA_ERR_SHAPE, "rows exceed the launch grid");
   if (!aligned16(o_parts)) return fail(SPA_ERR_ALIGN, "o_parts must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(o_out) & 7u) != 0) return fail(SPA_ERR_ALIGN, "o_out must be 8-byte aligned");

@@ -58,6 +58,10 @@ hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream);
 // merge (in plain row order).
 bool decode_slices_eligible(const Params &p);
 hipError_t launch_decode_slices(const Params &p, hipStream_t stream);
+// 512-wide heads over a shared latent cache (spa_latent.hip): bf16, k_raw ==
+// v_raw and k_cmp == v_cmp; one workgroup per (query, KV head, 64-head block,
+// KV slice); with several slices it writes sink-free partials (plain order).
+hipError_t launch_latent(const Params &p, hipStream_t stream);
 // unit_rows > 0: rows come in units of unit_rows consecutive rows (the query
 // heads of one (query, KV head) pair), unit u's partials written on XCD
 // u mod 8; the merge then reads each unit on that XCD.  0: plain order.

@@ -8,7 +8,8 @@
 // part with O = 0.  The order of the sums is fixed (s ascending), so the
 // result is bitwise deterministic.
 //
-// HBM-bound: D/4 lanes per row, one float4 of O each; up to 8 parts are
+// HBM-bound: D/4 lanes per row, one float4 of O each (at D 512 a row spans
+// two waves); up to 8 parts are
 // loaded (LSE and O together) in one round trip, more in chunks of 8.
 
 #include <hip/hip_runtime.h>
@@ -141,8 +142,11 @@ hipError_t launch_merge(const float *o_parts, const float *lse_parts, int32_t nu
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, o_parts, lse_parts,
                        num_parts, rows, num_q_heads, sink, o_out, lse_out, unit_rows);
-  else
+  else if (head_dim == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, o_parts, lse_parts,
+                       num_parts, rows, num_q_heads, sink, o_out, lse_out, unit_rows);
+  else
+    hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(256), 0, stream, o_parts, lse_parts,
                        num_parts, rows, num_q_heads, sink, o_out, lse_out, unit_rows);
   return hipGetLastError();
 }

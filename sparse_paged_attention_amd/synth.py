@@ -193,7 +193,7 @@ def _scatter(pool, pages, logical, page_size):
 def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head_dim,
                  page_size, window, ratio, topk, *, seed, cmp_fp8=False, num_splits=1,
                  query_positions=None, selection="random", with_sink=True,
-                 scale=None, spare_pages=3, keep_logical=True):
+                 scale=None, spare_pages=3, keep_logical=True, shared_kv=False):
     """Generic builder used by every named workload and by parametrised tests.
 
     ``query_positions``: prefill only, a list of (seq, pos) pairs.  Decode
@@ -201,7 +201,11 @@ def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head
     ``selection``: "random" (distinct random groups, random order), "score"
     (top-k of a seeded random score, ties to the lower index), or "all"
     (list of every complete group in ascending order).
+    ``shared_kv``: one latent cache per pool serves as K and V (the value
+    arrays are the key arrays, the same objects); bf16 only.
     """
+    if shared_kv and cmp_fp8:
+        raise ValueError("a shared latent cache is bf16")
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     B = len(seq_lens)
     Hq, Hkv, D, P = num_q_heads, num_kv_heads, head_dim, page_size
@@ -267,6 +271,9 @@ def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head
         kc_log.append(kc)
         vc_log.append(vc)
 
+    if shared_kv:
+        v_raw, v_log, v_cmp, vc_log = k_raw, k_log, k_cmp, kc_log
+
     # per-query compressed index lists
     cap = max(topk, 1)
     cmp_idx = np.full((Nq, cap), -1, dtype=np.int32)
@@ -309,11 +316,12 @@ def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head
     return p
 
 
-WORKLOADS = ("tiny", "decode_csa", "prefill_csa", "decode_hca", "mixed_fp8")
+WORKLOADS = ("tiny", "decode_csa", "prefill_csa", "decode_hca", "mixed_fp8", "decode_latent")
 
 
 def make_workload(name: str, *, batch: Optional[int] = None, keep_logical: bool = False) -> Problem:
-    """The five named workloads.  ``batch`` overrides the decode batch size
+    """The named workloads (the five measured configurations and the 512-wide
+    shared-latent decode).  ``batch`` overrides the decode batch size
     (one GPU's share of a larger batch, or a bounded CPU sample)."""
     if name == "tiny":
         return make_problem("tiny", "prefill", [64], 4, 1, 64, 16, 16, 4, 8, seed=0,
@@ -337,4 +345,10 @@ def make_workload(name: str, *, batch: Optional[int] = None, keep_logical: bool 
         lens = rng.integers(1024, 16384, size=b, endpoint=True).astype(np.int32)
         return make_problem("mixed_fp8", "decode", lens, 128, 1, 128, 64, 128, 4, 512,
                             seed=4, cmp_fp8=True, selection="random", keep_logical=keep_logical)
+    if name == "decode_latent":
+        # the 512-wide shared latent cache (K = V) in 256-token pages, with
+        # the CSA layer's window and top-k of decode_csa and 64 query heads
+        b = batch or 32
+        return make_problem("decode_latent", "decode", [4096] * b, 64, 1, 512, 256, 128, 4, 512,
+                            seed=5, selection="random", num_splits=8, shared_kv=True, keep_logical=keep_logical)
     raise ValueError(f"unknown workload {name!r}")

@@ -103,6 +103,12 @@ FAULTS = [
     ("queries_per_block_3", lambda a: setattr(a, "queries_per_block", 3), -4),
     ("queries_per_block_2", lambda a: setattr(a, "queries_per_block", 2), -4),
     ("heads_per_block_128", lambda a: (setattr(a, "num_q_heads", 128), setattr(a, "heads_per_block", 128)), -4),
+    ("d512_separate_kv", lambda a: setattr(a, "head_dim", 512), -4),
+    ("d512_fp8", lambda a: (setattr(a, "head_dim", 512), setattr(a, "v_raw", a.k_raw), setattr(a, "v_cmp", a.k_cmp),
+                            setattr(a, "cmp_dtype", _lib.SPA_FP8_E4M3_OCP), setattr(a, "k_cmp_scale", 0x30000000),
+                            setattr(a, "v_cmp_scale", 0x30001000)), -4),
+    ("d512_heads_per_block", lambda a: (setattr(a, "head_dim", 512), setattr(a, "v_raw", a.k_raw),
+                                        setattr(a, "v_cmp", a.k_cmp), setattr(a, "heads_per_block", 64)), -4),
     ("splits_zero", lambda a: setattr(a, "num_splits", 0), -7),
     ("splits_too_many", lambda a: setattr(a, "num_splits", 65), -7),
     ("decode_with_positions", lambda a: setattr(a, "query_pos", 0x20000000), -9),

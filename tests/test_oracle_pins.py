@@ -115,6 +115,26 @@ def test_dense_reduction_window_only(Hq, Hkv):
     np.testing.assert_allclose(LSE, Lref, rtol=0, atol=1e-12)
 
 
+def test_dense_reduction_shared_latent_d512():
+    """A 512-wide shared latent cache (one array is K and V) in 256-token
+    pages: window-only attention over all positions is dense causal
+    attention with v = k."""
+    L = 300
+    p = synth.make_problem("latent", "prefill", [L], 4, 1, 512, 256, L + 1, 0, 0, seed=7,
+                           query_positions=[(0, t) for t in (0, 1, 100, 255, 256, 299)], with_sink=False,
+                           shared_kv=True)
+    assert p.v_raw is p.k_raw
+    O, LSE = oracle.attention(p)
+    k = _bf(p.k_raw_logical[0])
+    Oref, Lref = _textbook_causal(_bf(p.q[[5]]), k, k, float(p.scale))   # t = 299: the last row
+    np.testing.assert_allclose(O[5], Oref[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(LSE[5], Lref[0], rtol=0, atol=1e-12)
+    for i, t in enumerate((0, 1, 100, 255, 256)):
+        Oi, Li = _textbook_causal(_bf(p.q[[i]]), k[:t + 1], k[:t + 1], float(p.scale))
+        np.testing.assert_allclose(O[i], Oi[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(LSE[i], Li[0], rtol=0, atol=1e-12)
+
+
 def test_dense_reduction_ratio1_compressed_equals_raw():
     """r = 1, compressed cache holding the raw rows, every group selected,
     no window: again dense causal attention."""
