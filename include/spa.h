@@ -63,7 +63,7 @@ typedef enum spa_status {
   SPA_ERR_SHAPE = -2,       /* a count or dimension is out of range / inconsistent */
   SPA_ERR_DTYPE = -3,       /* unknown dtype code, or raw KV not bf16              */
   SPA_ERR_UNSUPPORTED = -4, /* valid request this library does not implement
-                               (head_dim other than 64/128, ...)                  */
+                               (head_dim other than 64/128/512, ...)              */
   SPA_ERR_ALIGN = -5,       /* a pointer lacks the alignment its call requires     */
   SPA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than attn_workspace_size  */
   SPA_ERR_SPLITS = -7,      /* num_splits outside [1, SPA_MAX_SPLITS]              */
@@ -83,7 +83,14 @@ typedef struct spa_fwd_args {
   int32_t num_queries;    /* Nq; decode: must equal B                            */
   int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads                      */
   int32_t num_kv_heads;   /* Hkv                                                 */
-  int32_t head_dim;       /* D in {64, 128}                                      */
+  int32_t head_dim;       /* D in {64, 128, 512}.  512 is the shared latent
+                              cache of the DeepSeek-V4 layout (RL-Kernel PR
+                              "Roadmap item 24", review of the joint-attention
+                              contract and the packed-page gather: one bf16
+                              `_kv` buffer is K and V, heads 512 wide): it
+                              needs v_raw == k_raw, v_cmp == k_cmp, bf16
+                              caches and heads_per_block = queries_per_block
+                              = 0 (SPA_ERR_UNSUPPORTED otherwise)            */
   int32_t page_size;      /* P >= 1 tokens (rows) per page, same for both caches */
   int32_t window;         /* W >= 0 raw tokens ending at the query token         */
   int32_t ratio;          /* r >= 0 tokens per compressed group; 0 = no groups   */
@@ -174,7 +181,7 @@ spa_status attn_fwd_prefill(const spa_fwd_args *args, void *stream);
    gets O = 0, LSE = -inf.  o_parts f32 [num_parts, rows, head_dim],
    lse_parts f32 [num_parts, rows] (device); sink f32 [num_q_heads] or NULL;
    o_out bf16 [rows, head_dim]; lse_out f32 [rows] or NULL.
-   head_dim in {64, 128}; 1 <= num_parts <= SPA_MAX_SPLITS; o_parts 16-byte
+   head_dim in {64, 128, 512}; 1 <= num_parts <= SPA_MAX_SPLITS; o_parts 16-byte
    and o_out 8-byte aligned (else SPA_ERR_ALIGN). */
 spa_status attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t num_parts,
                           int64_t rows, int32_t head_dim, int32_t num_q_heads,
