@@ -14,7 +14,7 @@
 //
 // One workgroup of eight waves per (query, KV head, block of 64 query heads,
 // KV slice): wave w takes head group w / 4 (32 heads, the MFMA's N) and head
-// dimensions 128 (w % 4) .. +127.  Per 32-row tile (1 KiB rows, two LDS
+// dimensions 128 (w % 4) .. +127.  Per 32-row tile (1 KiB rows, three LDS
 // stages filled by direct global->LDS loads, one 1 KiB load per row):
 //   * each wave forms the partial S^T = K.Q^T over its 128 dimensions
 //     (v_mfma_f32_32x32x16_bf16) and stores it in LDS;
@@ -46,7 +46,7 @@ constexpr int kPT = 32;                    // rows per tile
 constexpr int kTileB = kPT * kRowB;
 constexpr int kLThreads = 512;             // eight waves
 constexpr int kLRows = 512;                // rows translated per chunk (one per thread)
-constexpr int kLStages = 2;
+constexpr int kLStages = 3;               // two tiles in flight while one is computed
 constexpr int64_t kCmpBit = int64_t(1) << 62;
 
 struct LatentSmem {
@@ -131,10 +131,15 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
     }
     __syncthreads();
     issue(0);
+    if (ntiles > 1) issue(1);
     for (int j = 0; j < ntiles; ++j) {
-      wait_vmcnt<0>();
-      block_sync();                          // tile j in; every wave done with tile j-1
-      if (j + 1 < ntiles) issue(j + 1);
+      // this wave's loads of tile j are complete (tile j+1's four may still
+      // be in flight), then everyone's; every wave is done with tile j-1,
+      // whose stage tile j+2 refills
+      if (j + 1 < ntiles) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+      block_sync();
+      if (j + 2 < ntiles) issue(j + 2);
       const uint8_t *T = sm.kv[j % kLStages];
       const uint32_t tm = (uint32_t)__ballot(lane < 32 && sm.row[kPT * j + (lane & 31)] >= 0);
       // partial scores over this wave's 128 dimensions
