@@ -18,10 +18,11 @@
 // stages filled by direct global->LDS loads, one 1 KiB load per row):
 //   * each wave forms the partial S^T = K.Q^T over its 128 dimensions
 //     (v_mfma_f32_32x32x16_bf16) and stores it in LDS;
-//   * after a barrier, each wave sums its group's four partials in a fixed
-//     order, so the four waves of a group hold the same scores, and runs the
-//     online softmax (log2 domain, sink folded into (m, l), lazy rescale)
-//     identically;
+//   * after a barrier, wave (g, q) sums float4 q of its group's four
+//     partials in a fixed order and publishes it; after another barrier the
+//     four waves of a group read the same sums (half the LDS reads of each
+//     wave summing everything) and run identical online softmaxes (log2
+//     domain, sink folded into (m, l), lazy rescale);
 //   * O^T += V^T.P^T for the wave's 128 dimensions, V^T read from the same
 //     tile by transposing LDS reads.
 // A 1 KiB row is four 256-byte quarters, each laid out (and swizzled) like a
@@ -51,7 +52,8 @@ constexpr int64_t kCmpBit = int64_t(1) << 62;
 
 struct LatentSmem {
   alignas(16) uint8_t kv[kLStages][kTileB];
-  alignas(16) float4 xs[2][4][4][64];      // [head group][quarter][float4 of S^T][lane]
+  alignas(16) float4 xs[2][4][4][64];      // partial S^T: [head group][quarter][float4][lane]
+  alignas(16) float4 xf[2][4][64];         // summed S^T: [head group][float4][lane]
   alignas(16) int64_t row[kLRows];         // row * Hkv + g (bit 62: compressed), -1: masked
 };
 
@@ -175,19 +177,26 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
       for (int c = 0; c < 4; ++c)
         sm.xs[hg][dq][c][lane] = make_float4(s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3]);
       block_sync();
-      // the group's full scores, summed in quarter order by all four waves
-      float sc[16];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float4 t = sm.xs[hg][0][c][lane];
+      // the group's full scores: wave (g, q) sums float4 q of the four
+      // partials (quarter order) and publishes it; then every wave of the
+      // group reads all four sums, so the four hold the same scores
+      {
+        float4 t = sm.xs[hg][0][dq][lane];
 #pragma unroll
         for (int q = 1; q < 4; ++q) {
-          const float4 x = sm.xs[hg][q][c][lane];
+          const float4 x = sm.xs[hg][q][dq][lane];
           t.x += x.x;
           t.y += x.y;
           t.z += x.z;
           t.w += x.w;
         }
+        sm.xf[hg][dq][lane] = t;
+      }
+      block_sync();
+      float sc[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 t = sm.xf[hg][c][lane];
         sc[4 * c] = t.x;
         sc[4 * c + 1] = t.y;
         sc[4 * c + 2] = t.z;

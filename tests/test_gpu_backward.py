@@ -202,3 +202,10 @@ def test_backward_short_lists_and_bad_ids_flagged():
     api.backward(dq, o, lse, d_o, err_flag=err)
     torch.cuda.synchronize()
     assert int(err.item()) & 2                   # the compressed-id bit
+
+
+def test_backward_full_prefill_csa():
+    """The workload bench.py times (prefill CSA, 2560 queries), every
+    element against the oracle under the same bound."""
+    p = synth.make_workload("prefill_csa")
+    assert _check(p, "prefill_csa full", seed=5) == 0

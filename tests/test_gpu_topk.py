@@ -86,3 +86,16 @@ def test_topk_then_attention():
     Oref, Lref = oracle.attention(p)
     rep = accept(O, L, Oref, Lref)
     assert rep.ok, rep
+
+
+@pytest.mark.parametrize("shape", ["topk_decode", "topk_prefill"])
+def test_topk_bench_shapes(shape):
+    """The two shapes bench.py times, with its seed and launch: 32 rows of
+    1024 groups, and 2560 prefill rows of floor((t+1)/4) groups, k 512."""
+    rng = np.random.default_rng(7)
+    if shape == "topk_decode":
+        n_valid = np.full(32, 1024, dtype=np.int32)
+    else:
+        n_valid = np.array([(t + 1) // 4 for t in range(2560)], dtype=np.int32)
+    scores = rng.standard_normal((len(n_valid), int(n_valid.max()))).astype(np.float32)
+    _check(scores, n_valid, 512, shape)
