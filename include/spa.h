@@ -231,8 +231,13 @@ spa_status attn_topk_select(const float *scores, int64_t ld, const int32_t *n_va
      d_sink[h] += -sum_i exp(sink_h - LSE_ih) Delta_ih
    `args` describes the forward call exactly as it was made (decode when
    query_seq and query_pos are NULL, else prefill); args->o (bf16) and
-   args->lse are that call's outputs and are read here; num_splits,
-   heads_per_block and queries_per_block are ignored.  Supported: bf16
+   args->lse are that call's outputs and are read here; num_splits and
+   heads_per_block are ignored.  queries_per_block: 0 lets the library
+   choose; 1 takes one query per workgroup; 2 takes prefill query pairs,
+   which stream the union of two neighbouring queries' KV sets so that a row
+   both read is added once (a prefill call with a top-k list or no
+   compressed part and 2 * (topk + window) <= 1280; SPA_ERR_UNSUPPORTED
+   otherwise).  The library's choice is pairs wherever they fit.  Supported: bf16
    caches, head_dim 128 (SPA_ERR_UNSUPPORTED otherwise).
    grads->d_o bf16 [Nq, Hq, D], 16-byte aligned; grads->dq f32 [Nq, Hq, D];
    dk_raw/dv_raw f32 with the raw cache's layout [raw_pages, page_size,

@@ -215,7 +215,7 @@ def topk_select(scores: torch.Tensor, n_valid: torch.Tensor, k: int) -> Tuple[to
 
 def backward(dp: DeviceProblem, o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor, *,
              err_flag: Optional[torch.Tensor] = None, want_dsink: bool = True,
-             grads: Optional[dict] = None, stream: Optional[int] = None) -> dict:
+             grads: Optional[dict] = None, stream: Optional[int] = None, queries_per_block: int = 0) -> dict:
     """attn_bwd: gradients of the forward call described by ``dp`` from its
     outputs (o bf16, lse f32) and the upstream gradient d_o (bf16 [Nq,Hq,D]).
     Returns dict dq, dk_raw, dv_raw, dk_cmp, dv_cmp, d_sink (f32; the cache
@@ -233,7 +233,7 @@ def backward(dp: DeviceProblem, o: torch.Tensor, lse: torch.Tensor, d_o: torch.T
             "d_sink": (torch.zeros(dp.num_q_heads, dtype=torch.float32, device=dev)
                        if (want_dsink and dp.sink is not None) else None),
         }
-    args = dp.args(1)
+    args = dp.args(1, 0, queries_per_block)
     args.o = _ptr(o)
     args.lse = _ptr(lse)
     args.err_flag = _ptr(err_flag)

@@ -312,7 +312,9 @@ size_t attn_bwd_workspace_size(const spa_fwd_args *args) {
 spa_status attn_bwd(const spa_fwd_args *args, const spa_bwd_grads *grads, void *stream) {
   if (args == nullptr || grads == nullptr) return fail(SPA_ERR_NULL, "args/grads is NULL");
   const bool decode = args->query_seq == nullptr && args->query_pos == nullptr;
-  // the forward's split, block and workspace choices do not apply
+  // the forward's split and head-block choices do not apply;
+  // queries_per_block picks one query or a query pair per workgroup
+  const int32_t qpb = args->queries_per_block;
   spa_fwd_args a = *args;
   a.num_splits = 1;
   a.heads_per_block = 0;
@@ -329,7 +331,13 @@ spa_status attn_bwd(const spa_fwd_args *args, const spa_bwd_grads *grads, void *
     return fail(SPA_ERR_NULL, "ratio > 0 needs dk_cmp and dv_cmp");
   if (grads->d_sink != nullptr && a.sink == nullptr) return fail(SPA_ERR_NULL, "d_sink without a sink");
   if (!aligned16(grads->d_o) || !aligned16(grads->dq)) return fail(SPA_ERR_ALIGN, "d_o and dq must be 16-byte aligned");
+  if (qpb < 0 || qpb > 2) return fail(SPA_ERR_UNSUPPORTED, "queries_per_block %d not supported (0, 1 or 2)", qpb);
   spa::Params p = make_params(&a, decode);
+  const bool pairs_ok = !decode && spa::backward_pairs_eligible(p);
+  if (qpb == 2 && !pairs_ok)
+    return fail(SPA_ERR_UNSUPPORTED, "queries_per_block 2 needs a prefill call with a top-k list or no compressed part "
+                "and 2 * (topk + window) <= %d", spa::kPairRowsMax);
+  const bool pairs = pairs_ok && qpb != 1;
   spa::BwdParams b{};
   b.d_o = static_cast<const uint16_t *>(grads->d_o);
   b.o = static_cast<const uint16_t *>(a.o);
@@ -351,7 +359,7 @@ spa_status attn_bwd(const spa_fwd_args *args, const spa_bwd_grads *grads, void *
   if (a.num_queries == 0) return ok();
   if ((int64_t)a.num_queries * a.num_kv_heads * ((a.num_q_heads / a.num_kv_heads + 63) / 64) > 0x7FFFFFFFLL)
     return fail(SPA_ERR_SHAPE, "the job count exceeds the launch grid");
-  hipError_t e = spa::launch_backward(p, b, static_cast<hipStream_t>(stream));
+  hipError_t e = spa::launch_backward(p, b, pairs, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }

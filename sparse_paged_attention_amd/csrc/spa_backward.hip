@@ -13,23 +13,30 @@
 // O and LSE are the forward's outputs; P is recomputed from LSE, so there
 // is no running max.
 //
-// One workgroup of two waves per (query, KV head, block of 64 query heads);
-// wave w owns 32 query heads.  The query's rows are translated through the
-// page tables (the forward's device functions) into an LDS list, chunk by
-// chunk, and streamed as 32-row K and V tiles through two LDS stages with
-// direct global->LDS loads.  Per tile and wave, on v_mfma_f32_32x32x16_bf16:
+// One workgroup per (query, KV head, block of 64 query heads) with two
+// waves of 32 query heads, or, for a prefill call whose lists are short
+// enough, per (query pair, KV head, 64-head block) with four waves (query x
+// head half).  A pair streams the union of its two KV sets (per-query
+// bitmaps of the listed groups, then the window positions from the lower
+// window start to the higher query position), each row flagged with the
+// queries that read it; pairs across sequences, or lists that name a group
+// twice, stream the two lists one after the other.  Rows are translated
+// through the page tables (the forward's device functions) into an LDS list
+// and streamed as 32-row K and V tiles through two LDS stages with direct
+// global->LDS loads.  Per tile and wave, on v_mfma_f32_32x32x16_bf16:
 //   S^T = K.Q^T and dP^T = V.dO^T (a lane per head): P, dS per head column;
 //   S = Q.K^T and dP = dO.V^T (a lane per KV row): P, dS per row column;
 //   dQ^T += K^T.dS^T      (K^T by transposing LDS reads, as the forward's V^T)
-//   dV = P.dO, dK = dS.Q  over all 64 heads, for half the head dimensions
-//                          per wave (P and dS swapped through LDS; dO and Q
-//                          are LDS tiles too, read transposed the same way)
+//   dV = P.dO, dK = dS.Q  over every wave's heads (both queries of a pair),
+//                          for a share of the head dimensions per wave (P
+//                          and dS swapped through LDS; dO and Q are LDS
+//                          tiles too, read transposed the same way)
 // Computing the scores in both orientations costs two extra MFMA products per
 // tile but puts each of P and dS in the register layout its consumer needs,
 // with no LDS round trip.  dK and dV rows are added to the fp32 gradient
-// caches with float atomics, once per workgroup and element: a lane per head
-// dimension, so each atomic instruction covers 128 contiguous bytes of two
-// rows.  dQ is written once
+// caches with float atomics, once per workgroup and element (so a row both
+// queries of a pair read is added once): a lane per head dimension, so each
+// atomic instruction covers 128 contiguous bytes of two rows.  dQ is written once
 // (fp32).  The sink gradient is written per (query, head) and summed over
 // the queries by sink_reduce_kernel, in a fixed order.
 
@@ -48,23 +55,36 @@ constexpr int kRowB = 2 * kD;              // bf16 row bytes
 constexpr int kChunks = kRowB / 16;        // 16-byte chunks per row
 constexpr int kPT = 32;                    // KV rows per tile
 constexpr int kTileB = kPT * kRowB;
-constexpr int kBThreads = 128;             // two waves of 32 query heads
-constexpr int kBRows = 512;                // rows translated per chunk
-constexpr int kBIters = kBRows / kBThreads;
+constexpr int kBRows = 512;                // rows translated per chunk (one query per workgroup)
+constexpr int kPairRows = kPairRowsMax;    // rows of a query pair's list (one chunk)
+constexpr int kBmWords = 1024;             // bitmap words per query: groups < 32768
 constexpr int kBStages = 2;
 constexpr int64_t kCmpBit = int64_t(1) << 62;
 
+// NQ queries per workgroup (1, or 2 for a prefill query pair); 2 NQ waves,
+// wave w = query (w / 2) x head half (w % 2).
+template <int NQ>
 struct BwdSmem {
-  alignas(16) uint8_t k[kBStages][kTileB];
-  alignas(16) uint8_t v[kBStages][kTileB];
-  alignas(16) uint8_t q[2][kTileB];        // wave w: its 32 heads as tile rows
-  alignas(16) uint8_t dO[2][kTileB];
-  alignas(16) int64_t row[kBRows];         // row * Hkv + g (bit 62: compressed), -1: masked
-  alignas(16) bf16x8 xp[2][2][64];         // P and dS of each wave's heads, A-fragment order
-  alignas(16) bf16x8 xd[2][2][64];
-  alignas(16) float lse2[64];              // LSE * log2(e); +inf: no softmax (no rows, not a head)
-  alignas(16) float delta[64];
+  static constexpr int kRows = NQ == 1 ? kBRows : kPairRows;
+  union {
+    struct {
+      alignas(16) uint8_t k[kBStages][kTileB];
+      alignas(16) uint8_t v[kBStages][kTileB];
+    } t;
+    uint32_t bm[2][kBmWords];              // query pair setup: each query's selected groups
+  } u;
+  alignas(16) uint8_t q[2 * NQ][kTileB];   // wave w: its query's 32 heads as tile rows
+  alignas(16) uint8_t dO[2 * NQ][kTileB];
+  alignas(16) int64_t row[kRows];          // row * Hkv + g (bit 62: compressed), -1: masked
+  uint8_t flg[NQ == 1 ? 1 : kRows];        // query pair: bit q = in query q's set
+  alignas(16) bf16x8 xp[2 * NQ][2][64];    // P and dS of each wave's heads, A-fragment order
+  alignas(16) bf16x8 xd[2 * NQ][2][64];
+  alignas(16) float lse2[NQ * 64];         // LSE * log2(e); +inf: no softmax (no rows, not a head)
+  alignas(16) float delta[NQ * 64];
+  int32_t wsum[2 * NQ];
+  int32_t dup;                             // a pair's list names a group twice
 };
+static_assert(sizeof(BwdSmem<2>::u) >= 2 * kBmWords * 4, "bitmaps fit the tile stages");
 
 // A K^T, V^T, Q^T or dO^T fragment of a tile in LDS (transposing reads):
 // as the A operand, lane L holds column d = 32 db + L % 32 and the tile rows
@@ -91,11 +111,129 @@ __device__ __forceinline__ bf16x8 row_frag(const uint8_t *T, int lane, int kk) {
   return *(const bf16x8 *)(T + r * kRowB + ((c ^ swz<kChunks>(r)) * 16));
 }
 
-__global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams b) {
-  __shared__ BwdSmem sm;
+// The row list of a query pair (queries i0, i1 of the same prefill call):
+// the union of their KV sets when both sit in one sequence (compressed
+// groups in ascending id order from per-query bitmaps, then the window
+// positions from the lower window start to the higher query position),
+// else their two canonical lists one after the other.  Each row carries
+// bit q for membership in query q's set.  Returns the number of rows; the
+// list is padded with masked rows to a whole tile.
+template <int NT, class Smem>
+__device__ int32_t pair_rows(const Params &p, Smem &sm, int32_t i0, int32_t i1, bool has1, const QueryKV &kv0,
+                             const QueryKV &kv1, int32_t g) {
+  const int tid = threadIdx.x;
+  constexpr int kIters = Smem::kRows / NT;
+  const int32_t U0 = kv0.n_sel + kv0.win_len, U1 = has1 ? kv1.n_sel + kv1.win_len : 0;
+  const int32_t wlo = min(kv0.win_len > 0 ? kv0.win_lo : INT32_MAX, kv1.win_len > 0 ? kv1.win_lo : INT32_MAX);
+  const int32_t whi = max(kv0.win_len > 0 ? kv0.t : -1, kv1.win_len > 0 ? kv1.t : -1);
+  const int32_t wrange = whi >= wlo ? whi - wlo + 1 : 0;
+  bool uni = has1 && U0 > 0 && U1 > 0 && kv0.b == kv1.b && kv0.n_c <= 32 * kBmWords && kv1.n_c <= 32 * kBmWords &&
+             kv0.n_sel + kv1.n_sel + wrange <= Smem::kRows;
+  int32_t U = 0, ncu = 0;
+  if (uni) {
+    // ---- bitmaps of the two lists (a repeated id falls back to the
+    // concatenation, which counts it twice as the single-query path does)
+    for (int w = tid; w < 2 * kBmWords; w += NT) sm.u.bm[w / kBmWords][w % kBmWords] = 0u;
+    if (tid == 0) sm.dup = 0;
+    __syncthreads();
+    for (int32_t e = tid; e < kv0.n_sel + kv1.n_sel; e += NT) {
+      const int q = e < kv0.n_sel ? 0 : 1;
+      const QueryKV &kv = q ? kv1 : kv0;
+      const int32_t c = check_cmp_id(p, kv, p.cmp_idx[(int64_t)(q ? i1 : i0) * p.topk + (q ? e - kv0.n_sel : e)]);
+      if (c >= 0) {
+        const uint32_t bit = 1u << (c & 31);
+        if (atomicOr(&sm.u.bm[q][c >> 5], bit) & bit) sm.dup = 1;
+      }
+    }
+    __syncthreads();
+    uni = sm.dup == 0;
+    if (uni) {
+      // ---- ranks: four bitmap words per thread, in id order
+      constexpr int kWpt = kBmWords / NT;
+      uint32_t wd[kWpt];
+      int32_t own = 0;
+#pragma unroll
+      for (int k = 0; k < kWpt; ++k) {
+        wd[k] = sm.u.bm[0][tid * kWpt + k] | sm.u.bm[1][tid * kWpt + k];
+        own += __popc(wd[k]);
+      }
+      int32_t pre = block_excl_scan<NT>(own, ncu, sm.wsum);
+#pragma unroll
+      for (int k = 0; k < kWpt; ++k) {
+        const int w = tid * kWpt + k;
+        uint32_t bits = wd[k];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          bits &= bits - 1;
+          const int32_t c = 32 * w + b;
+          sm.row[pre] = c;
+          sm.flg[pre] = (uint8_t)(((sm.u.bm[0][w] >> b) & 1u) | (((sm.u.bm[1][w] >> b) & 1u) << 1));
+          ++pre;
+        }
+      }
+      U = ncu + wrange;
+      __syncthreads();                       // every logical id and flag is in; the bitmaps are dead
+      // ---- window positions and the translation of every row
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int32_t r = tid + it * NT;
+        if (r < (U + kPT - 1) / kPT * kPT) {
+          int64_t er = -1;
+          uint8_t f = 0;
+          if (r < ncu) {
+            f = sm.flg[r];
+            const int64_t pr = logical_row(p, kv0, true, (int32_t)sm.row[r]);
+            if (pr >= 0) er = (pr * p.hkv + g) | kCmpBit;
+          } else if (r < U) {
+            const int32_t x = wlo + (r - ncu);
+            f = (uint8_t)((kv0.win_len > 0 && x >= kv0.win_lo && x <= kv0.t ? 1u : 0u) |
+                          (kv1.win_len > 0 && x >= kv1.win_lo && x <= kv1.t ? 2u : 0u));
+            const int64_t pr = f ? logical_row(p, kv0, false, x) : -1;
+            if (pr >= 0) er = pr * p.hkv + g;
+          }
+          sm.row[r] = er;
+          sm.flg[r] = er >= 0 ? f : 0;
+        }
+      }
+    }
+  }
+  if (!uni) {
+    // ---- concatenation: query 0's canonical rows, then query 1's
+    U = U0 + U1;
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int32_t r = tid + it * NT;
+      if (r < (U + kPT - 1) / kPT * kPT) {
+        int64_t er = -1;
+        uint8_t f = 0;
+        if (r < U) {
+          const int q = r < U0 ? 0 : 1;
+          const QueryKV &kv = q ? kv1 : kv0;
+          const int32_t e = q ? r - U0 : r;
+          const bool cmp = e < kv.n_sel;
+          const int64_t pr = logical_row(p, kv, cmp, entry_logical(p, kv, q ? i1 : i0, e));
+          if (pr >= 0) er = (pr * p.hkv + g) | (cmp ? kCmpBit : 0);
+          f = (uint8_t)(1u << q);
+        }
+        sm.row[r] = er;
+        sm.flg[r] = er >= 0 ? f : 0;
+      }
+    }
+  }
+  return U;
+}
+
+template <int NQ>
+__global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams b) {
+  constexpr int NT = 128 * NQ;
+  constexpr int NW = 2 * NQ;                 // waves
+  constexpr int kRowsPerWave = kPT / NW;     // tile rows each wave loads
+  __shared__ BwdSmem<NQ> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int qw = wave >> 1;                  // the wave's query (0 with one query per workgroup)
+  const int hw = wave & 1;                   // the wave's head half
   const int hi = lane >> 5;
   const int hblocks = (p.group + 63) / 64;
   // heaviest jobs (the last queries of a prefill) first
@@ -103,30 +241,32 @@ __global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams
   const int hb = (int)(job % hblocks);
   const int64_t u = job / hblocks;
   const int g = (int)(u % p.hkv);
-  const int i = (int)(u / p.hkv);
-  const QueryKV kv = query_kv(p, i);
-  const int32_t U = kv.n_sel + kv.win_len;
+  const int32_t i0 = (int32_t)(u / p.hkv) * NQ;
+  const int32_t i1 = i0 + 1;
+  const bool has1 = NQ == 2 && i1 < p.num_queries;
+  const QueryKV kv0 = query_kv(p, i0);
+  const QueryKV kv1 = has1 ? query_kv(p, i1) : QueryKV{0, 0, 0, 0, 0, 0};
+  const int32_t iq = qw ? i1 : i0;
+  const bool qvalid = qw == 0 || has1;
 
   // ---- Q and dO of the wave's heads: LDS tiles (rows = heads) and the
   // natural B fragments in registers
-  const int h0 = hb * 64 + wave * 32;                 // first head of the wave, within the group
-  const int64_t qbase = (int64_t)i * p.hq + (int64_t)g * p.group;
-  {
+  const int h0 = hb * 64 + hw * 32;                   // first head of the wave, within the group
+  const int64_t qbase = (int64_t)iq * p.hq + (int64_t)g * p.group;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int idx = n * 64 + lane;
-      const int r = idx >> 4, c = idx & 15;
-      const bool ok = h0 + r < p.group;
-      const int64_t off = (qbase + h0 + r) * kD + c * 8;
-      const uint4 qv = ok ? *(const uint4 *)(p.q + off) : uint4{0, 0, 0, 0};
-      const uint4 ov = ok ? *(const uint4 *)(b.d_o + off) : uint4{0, 0, 0, 0};
-      const int dst = r * kRowB + ((c ^ swz<kChunks>(r)) * 16);
-      *(uint4 *)(sm.q[wave] + dst) = qv;
-      *(uint4 *)(sm.dO[wave] + dst) = ov;
-    }
+  for (int n = 0; n < 8; ++n) {
+    const int idx = n * 64 + lane;
+    const int r = idx >> 4, c = idx & 15;
+    const bool ok = qvalid && h0 + r < p.group;
+    const int64_t off = (qbase + h0 + r) * kD + c * 8;
+    const uint4 qv = ok ? *(const uint4 *)(p.q + off) : uint4{0, 0, 0, 0};
+    const uint4 ov = ok ? *(const uint4 *)(b.d_o + off) : uint4{0, 0, 0, 0};
+    const int dst = r * kRowB + ((c ^ swz<kChunks>(r)) * 16);
+    *(uint4 *)(sm.q[wave] + dst) = qv;
+    *(uint4 *)(sm.dO[wave] + dst) = ov;
   }
   const int hl = h0 + (lane & 31);                    // this lane's head (head-column layouts)
-  const bool hvalid = hl < p.group;
+  const bool hvalid = qvalid && hl < p.group;
   bf16x8 qf[kD / 16], dof[kD / 16];
   {
     const int64_t off = (qbase + hl) * kD + 8 * hi;
@@ -138,6 +278,7 @@ __global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams
   }
   // Delta = <dO, O> of the lane's head (each half of the wave sums 64 of
   // the D products) and the head's LSE
+  const int hslot = qw * 64 + hw * 32 + (lane & 31);  // the head's slot in lse2 / delta
   {
     float dsum = 0.f;
     if (hvalid) {
@@ -160,8 +301,8 @@ __global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams
     if (hi == 0) {
       const float lse = hvalid ? b.lse[qbase + hl] : INFINITY;
       const bool live = hvalid && lse != -INFINITY;
-      sm.lse2[wave * 32 + (lane & 31)] = live ? lse * kLog2e : INFINITY;
-      sm.delta[wave * 32 + (lane & 31)] = live ? dsum : 0.f;
+      sm.lse2[hslot] = live ? lse * kLog2e : INFINITY;
+      sm.delta[hslot] = live ? dsum : 0.f;
       if (hvalid && b.dsink_part != nullptr) {
         const float part = (live && p.sink != nullptr) ? -__expf(p.sink[g * p.group + hl] - lse) * dsum : 0.f;
         b.dsink_part[qbase + hl] = part;
@@ -169,8 +310,8 @@ __global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams
     }
   }
   __syncthreads();
-  const float my_lse2 = sm.lse2[wave * 32 + (lane & 31)];
-  const float my_delta = sm.delta[wave * 32 + (lane & 31)];
+  const float my_lse2 = sm.lse2[hslot];
+  const float my_delta = sm.delta[hslot];
 
   f32x16 dqa[kD / 32];
 #pragma unroll
@@ -182,52 +323,72 @@ __global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams
   float *const dk_cmp = in_sgpr(b.dk_cmp), *const dv_cmp = in_sgpr(b.dv_cmp);
   const float sl2 = p.scale_log2;
   const float scale = b.scale;
-  // tile loads: wave w moves rows 16w .. 16w+15 of both sides (four 1 KiB
-  // direct loads per side, four rows each); lane L's chunk in load n is
-  // logical chunk (L % 16) ^ swz(row), row = 16w + 4n + L / 16
-  int32_t csrc[4];
+  // tile loads: wave w moves rows kRowsPerWave w .. (four per direct load);
+  // lane L's chunk in load n is logical chunk (L % 16) ^ swz(row), row =
+  // kRowsPerWave w + 4n + L / 16
+  int32_t csrc[kRowsPerWave / 4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int r = 16 * wave + 4 * n + lane / kChunks;
+  for (int n = 0; n < kRowsPerWave / 4; ++n) {
+    const int r = kRowsPerWave * wave + 4 * n + lane / kChunks;
     csrc[n] = ((lane % kChunks) ^ swz<kChunks>(r)) * 16;
   }
 
-  for (int32_t c0 = 0; c0 < U; c0 += kBRows) {
-    const int32_t n = min(kBRows, U - c0);
-    const int32_t ntiles = (n + kPT - 1) / kPT;
-    // ---- translate the chunk's rows: list entries, then page tables
-    int32_t xs[kBIters];
+  // the list: one query's rows in chunks, or a query pair's rows at once
+  const int32_t Utot = NQ == 1 ? kv0.n_sel + kv0.win_len : 0;
+  int32_t c0 = 0;
+  bool more = true;
+  while (more) {
+    int32_t n;
+    if constexpr (NQ == 1) {
+      n = min(kBRows, Utot - c0);
+      more = c0 + n < Utot;
+      if (n <= 0) break;
+      constexpr int kIters = kBRows / NT;
+      int32_t xs[kIters];
 #pragma unroll
-    for (int it = 0; it < kBIters; ++it) {
-      const int32_t e = c0 + tid + it * kBThreads;
-      xs[it] = e < c0 + n ? entry_logical(p, kv, i, e) : -1;
-    }
-#pragma unroll
-    for (int it = 0; it < kBIters; ++it) {
-      const int32_t r = tid + it * kBThreads;
-      if (r < ntiles * kPT) {
-        const int32_t e = c0 + r;
-        int64_t er = -1;
-        if (r < n) {
-          const bool cmp = e < kv.n_sel;
-          const int64_t pr = logical_row(p, kv, cmp, xs[it]);
-          if (pr >= 0) er = (pr * p.hkv + g) | (cmp ? kCmpBit : 0);
-        }
-        sm.row[r] = er;
+      for (int it = 0; it < kIters; ++it) {
+        const int32_t e = c0 + tid + it * NT;
+        xs[it] = e < c0 + n ? entry_logical(p, kv0, i0, e) : -1;
       }
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int32_t r = tid + it * NT;
+        if (r < (n + kPT - 1) / kPT * kPT) {
+          const int32_t e = c0 + r;
+          int64_t er = -1;
+          if (r < n) {
+            const bool cmp = e < kv0.n_sel;
+            const int64_t pr = logical_row(p, kv0, cmp, xs[it]);
+            if (pr >= 0) er = (pr * p.hkv + g) | (cmp ? kCmpBit : 0);
+          }
+          sm.row[r] = er;
+        }
+      }
+      c0 += n;
+    } else {
+      n = pair_rows<NT>(p, sm, i0, i1, has1, kv0, kv1, g);
+      more = false;
+      if (n <= 0) break;
     }
     __syncthreads();
+    const int32_t ntiles = (n + kPT - 1) / kPT;
 
     auto issue = [&](int j) {
       const int st = j % kBStages;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int64_t er = sm.row[kPT * j + 16 * wave + 4 * q4 + lane / kChunks];
+      for (int q4 = 0; q4 < kRowsPerWave / 4; ++q4) {
+        const int rr = kRowsPerWave * wave + 4 * q4;
+        const int64_t er = sm.row[kPT * j + rr + lane / kChunks];
         const bool cmp = (er & kCmpBit) != 0;
         const int64_t off = (er & ~kCmpBit) * kRowB + csrc[q4];
-        dma16(er >= 0 ? (cmp ? kcmp : kraw) + off : kZeroRow + csrc[q4], sm.k[st] + (16 * wave + 4 * q4) * kRowB);
-        dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + csrc[q4], sm.v[st] + (16 * wave + 4 * q4) * kRowB);
+        dma16(er >= 0 ? (cmp ? kcmp : kraw) + off : kZeroRow + csrc[q4], sm.u.t.k[st] + rr * kRowB);
+        dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + csrc[q4], sm.u.t.v[st] + rr * kRowB);
       }
+    };
+    // a row of the list is in this wave's query's set
+    auto in_set = [&](int r) -> bool {
+      if constexpr (NQ == 1) return sm.row[r] >= 0;
+      else return ((sm.flg[r] >> qw) & 1u) != 0;
     };
 
     issue(0);
@@ -239,11 +400,10 @@ __global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams
       block_sync();
       if (j + 1 < ntiles) issue(j + 1);
       const int st = j % kBStages;
-      const uint8_t *Kt = sm.k[st];
-      const uint8_t *Vt = sm.v[st];
-      const int64_t lrow = sm.row[kPT * j + (lane & 31)];
-      const uint32_t tm = (uint32_t)__ballot(lane < 32 && lrow >= 0);
-      const bool lvalid = lrow >= 0;
+      const uint8_t *Kt = sm.u.t.k[st];
+      const uint8_t *Vt = sm.u.t.v[st];
+      const bool lvalid = in_set(kPT * j + (lane & 31));
+      const uint32_t tm = (uint32_t)__ballot(lane < 32 && lvalid);
 
       // scores and dP in both orientations
       f32x16 s_rh = f32x16{}, s_hr = f32x16{}, dp_rh = f32x16{}, dp_hr = f32x16{};
@@ -271,8 +431,8 @@ __global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams
       bf16x8 pb[2], dsh[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 l4 = *(const float4 *)(&sm.lse2[wave * 32 + 8 * q4 + 4 * hi]);
-        const float4 d4 = *(const float4 *)(&sm.delta[wave * 32 + 8 * q4 + 4 * hi]);
+        const float4 l4 = *(const float4 *)(&sm.lse2[qw * 64 + hw * 32 + 8 * q4 + 4 * hi]);
+        const float4 d4 = *(const float4 *)(&sm.delta[qw * 64 + hw * 32 + 8 * q4 + 4 * hi]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
@@ -289,11 +449,11 @@ __global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
           dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Kt, lane, db, k2), dsb[k2], dqa[db], 0, 0, 0);
-      // dV = P . dO and dK = scale dS . Q for the tile's rows over all 64
-      // heads: the waves swap their P and dS fragments through LDS, and wave
-      // w takes head dimensions 64w .. 64w+63, so each gradient element is
-      // added once per workgroup.  Value r is row 8(r/4) + 4hi + r%4, lane
-      // column d.
+      // dV = P . dO and dK = scale dS . Q for the tile's rows over every
+      // wave's heads (both queries of a pair): the waves swap their P and dS
+      // fragments through LDS and split the head dimensions, so each gradient
+      // element is added once per workgroup.  Value r is row 8(r/4) + 4hi +
+      // r%4, lane column d.
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         sm.xp[wave][k2][lane] = pb[k2];
@@ -304,11 +464,11 @@ __global__ __launch_bounds__(kBThreads) void attn_bwd_kernel(Params p, BwdParams
       for (int r = 0; r < 16; ++r) er[r] = sm.row[kPT * j + 8 * (r >> 2) + 4 * hi + (r & 3)];
       block_sync();
 #pragma unroll
-      for (int dbi = 0; dbi < 2; ++dbi) {
-        const int db = 2 * wave + dbi;
+      for (int dbi = 0; dbi < 4 / NW; ++dbi) {
+        const int db = (4 / NW) * wave + dbi;
         f32x16 av = f32x16{}, ak = f32x16{};
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
+        for (int kc = 0; kc < 2 * NW; ++kc) {
           const int w2 = kc >> 1, k2 = kc & 1;
           av = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sm.xp[w2][k2][lane], tr_frag(sm.dO[w2], lane, db, k2), av, 0,
                                                        0, 0);
@@ -365,12 +525,26 @@ __global__ __launch_bounds__(256) void sink_reduce_kernel(const float *part, int
 
 bool backward_eligible(const Params &p) { return p.head_dim == kD && !p.cmp_fp8; }
 
-hipError_t launch_backward(const Params &p, const BwdParams &b, hipStream_t stream) {
-  if (!backward_eligible(p)) return hipErrorInvalidValue;
+// query pairs: a prefill call whose pair lists fit one chunk, with a top-k
+// list or no compressed part (an all-groups layer's lists can be long)
+bool backward_pairs_eligible(const Params &p) {
+  return p.query_seq != nullptr && p.query_pos != nullptr && (p.ratio == 0 || p.topk > 0) &&
+         2 * ((int64_t)p.topk + p.window) <= kPairRows;
+}
+
+hipError_t launch_backward(const Params &p, const BwdParams &b, bool pairs, hipStream_t stream) {
+  if (!backward_eligible(p) || (pairs && !backward_pairs_eligible(p))) return hipErrorInvalidValue;
   if (p.num_queries == 0) return hipSuccess;
-  const int64_t blocks = (int64_t)p.num_queries * p.hkv * ((p.group + 63) / 64);
-  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)blocks), dim3(kBThreads), 0, stream, p, b);
+  const int64_t hblocks = (p.group + 63) / 64;
+  if (pairs) {
+    const int64_t blocks = (int64_t)((p.num_queries + 1) / 2) * p.hkv * hblocks;
+    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_bwd_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, p, b);
+  } else {
+    const int64_t blocks = (int64_t)p.num_queries * p.hkv * hblocks;
+    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_bwd_kernel<1>, dim3((unsigned)blocks), dim3(128), 0, stream, p, b);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (b.dsink != nullptr && b.dsink_part != nullptr) {

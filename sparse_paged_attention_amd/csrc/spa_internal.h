@@ -87,6 +87,9 @@ struct BwdParams {
   float scale;
 };
 bool backward_eligible(const Params &p);
-hipError_t launch_backward(const Params &p, const BwdParams &b, hipStream_t stream);
+// query pairs (four waves, the union of two KV sets): a prefill call with a
+// top-k list or no compressed part and 2 * (topk + window) <= kPairRowsMax
+bool backward_pairs_eligible(const Params &p);
+hipError_t launch_backward(const Params &p, const BwdParams &b, bool pairs, hipStream_t stream);
 
 }  // namespace spa

@@ -1,6 +1,7 @@
 // Device helpers shared by the attention kernels: vector types, direct
-// global->LDS loads, wait and barrier primitives, the lane-pair max and the
-// XOR swizzle of LDS tile rows.  Device code only.
+// global->LDS loads, wait and barrier primitives, the lane-pair max, a
+// workgroup prefix sum and the XOR swizzle of LDS tile rows.  Device code
+// only.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -108,6 +109,31 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) { return __builtin_bit_ca
 // read one chunk of 16 consecutive rows, and the V transpose reads, where 16
 // lanes read 2 adjacent chunks of 4 consecutive rows.  For D 64 (8 chunks,
 // two rows per bank sweep) the K reads are conflict-free.
+// Exclusive prefix sum of v over a workgroup of NT threads; `total` gets
+// the sum.  wsum holds NT / 64 ints of LDS.  Every thread must call it.
+template <int NT>
+__device__ __forceinline__ int32_t block_excl_scan(int32_t v, int32_t &total, int32_t *wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int32_t s = wsum[w];
+    if (w < wave) before += s;
+    total += s;
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
 template <int CH>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (CH == 16) return ((r & 7) << 1) | ((r >> 3) & 1);

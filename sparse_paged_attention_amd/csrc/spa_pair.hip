@@ -114,29 +114,6 @@ static_assert(sizeof(PairSmem<2, false>::u) == 2 * 2 * kPTileB, "setup arrays fi
 static_assert(kBmWords == 4 * kThreads, "four bitmap words per thread in the rank scan");
 static_assert(kUMax % kPT == 0, "padding to a whole tile stays within the row list");
 
-// exclusive prefix sum over the workgroup's threads; `total` gets the sum
-__device__ __forceinline__ int32_t block_excl_scan(int32_t v, int32_t &total, int32_t *wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  int32_t before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    const int32_t s = wsum[w];
-    if (w < wave) before += s;
-    total += s;
-  }
-  __syncthreads();
-  return before + x - v;
-}
-
 // DEC = false: a prefill query pair (two queries, 64 heads: wave = query *
 // 2 + head half).  DEC = true: one KV slice of a decode query (one query,
 // 128 heads: wave = head quarter), whose sink-free partial the LSE merge
@@ -374,7 +351,7 @@ void attn_pair_kernel(const Params p) {
         own += wc[u];
       }
       int32_t ncu;                                      // groups in the union
-      int32_t pre = block_excl_scan(own, ncu, sm.wsum);
+      int32_t pre = block_excl_scan<kThreads>(own, ncu, sm.wsum);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int k = 4 * tid + u;

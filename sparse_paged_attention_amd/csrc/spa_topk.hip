@@ -29,6 +29,7 @@
 #include <cstdint>
 
 #include "spa_internal.h"
+#include "spa_kernel_util.h"
 
 namespace spa {
 namespace {
@@ -42,28 +43,6 @@ __device__ __forceinline__ uint32_t score_key(uint32_t bits) {
   return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
 }
 
-// exclusive prefix sum of v over the workgroup; `total` gets the sum
-__device__ __forceinline__ int32_t tk_scan(int32_t v, int32_t &total, int32_t *wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  int32_t before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kTkThreads / 64; ++w) {
-    const int32_t s = wsum[w];
-    if (w < wave) before += s;
-    total += s;
-  }
-  __syncthreads();
-  return before + x - v;
-}
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
   const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
@@ -176,7 +155,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float *scores, i
       // prefix sum in this order
       const int32_t h = (int32_t)hist[255 - tid];
       int32_t tot;
-      const int32_t above = tk_scan(h, tot, wsum);
+      const int32_t above = block_excl_scan<kTkThreads>(h, tot, wsum);
       if (above < krem && above + h >= krem) {
         sh_digit = 255 - tid;
         sh_krem = krem - above;
@@ -202,7 +181,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float *scores, i
       const bool gt = j < n && (u & mask) > prefix;
       const bool eq = j < n && (u & mask) == prefix;
       int32_t tot;
-      const int32_t r = eq_base + tk_scan(eq ? 1 : 0, tot, wsum);
+      const int32_t r = eq_base + block_excl_scan<kTkThreads>(eq ? 1 : 0, tot, wsum);
       const unsigned long long comp = ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)j);
       if (gt) {
         const int32_t slot = atomicAdd(&sh_ngt, 1);

@@ -38,7 +38,7 @@ def _dO(p, seed):
     return synth.f32_to_bf16_bits(rng.standard_normal(p.q.shape).astype(np.float32))
 
 
-def _run(p, dO_bits, want_dsink=True, repeat=1):
+def _run(p, dO_bits, want_dsink=True, repeat=1, qpb=0):
     from sparse_paged_attention_amd import api
     dp = api.DeviceProblem.from_problem(p)
     o, lse = api.forward(dp)
@@ -46,7 +46,7 @@ def _run(p, dO_bits, want_dsink=True, repeat=1):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     g = None
     for _ in range(repeat):
-        g = api.backward(dp, o, lse, d_o, err_flag=err, want_dsink=want_dsink, grads=g)
+        g = api.backward(dp, o, lse, d_o, err_flag=err, want_dsink=want_dsink, grads=g, queries_per_block=qpb)
     torch.cuda.synchronize()
     out = {k: (None if v is None else v.cpu().numpy().astype(np.float64)) for k, v in g.items()
            if not k.startswith("_")}
@@ -115,11 +115,11 @@ def _close(name, got, ref, bound):
         announce(f"  {name}: max |err| / bound = {np.max(np.abs(got - ref)[nz] / bound[nz]):.3f}")
 
 
-def _check(p, label, seed=1, want_dsink=True, repeat=1):
+def _check(p, label, seed=1, want_dsink=True, repeat=1, qpb=0):
     announce(f"backward {label}: Nq={p.num_queries} Hq={p.num_q_heads} Hkv={p.num_kv_heads} "
-             f"ratio={p.ratio} topk={p.topk} W={p.window}")
+             f"ratio={p.ratio} topk={p.topk} W={p.window} qpb={qpb}")
     dO = _dO(p, seed)
-    got, err = _run(p, dO, want_dsink, repeat)
+    got, err = _run(p, dO, want_dsink, repeat, qpb)
     ref = attention_backward(p, dO)
     bd = _bounds(p, dO)
     _close("dq", got["dq"], ref.dq, bd["dq"])
@@ -131,10 +131,45 @@ def _check(p, label, seed=1, want_dsink=True, repeat=1):
     return err
 
 
-def test_backward_prefill_csa():
+@pytest.mark.parametrize("qpb", [0, 1])
+def test_backward_prefill_csa(qpb):
+    """Query pairs (the library's choice here) and one query per workgroup."""
     p = synth.make_problem("bwd_csa", "prefill", [1500], 64, 1, 128, 16, 128, 4, 256, seed=81,
                            query_positions=[(0, t) for t in range(1400, 1464)], selection="score")
-    assert _check(p, "prefill csa") == 0
+    assert _check(p, "prefill csa", qpb=qpb) == 0
+
+
+def test_backward_pairs_across_sequences_and_odd_count():
+    """Pairs whose queries sit in different sequences stream the two lists
+    one after the other; an odd query count leaves the last pair with one
+    query; positions far apart in one sequence have disjoint windows."""
+    pos = [(0, 900), (1, 700), (1, 701), (0, 10), (0, 899), (1, 3), (0, 450), (0, 30), (1, 702)]
+    p = synth.make_problem("bwd_mix", "prefill", [901, 703], 64, 1, 128, 16, 128, 4, 128, seed=89,
+                           query_positions=pos, selection="random")
+    assert _check(p, "pairs across sequences") == 0
+
+
+def test_backward_group_listed_twice_pairs_match_single():
+    """A list that names a group twice is outside the oracle's contract;
+    both backward layouts count the entry twice, as the forward does (the
+    pair path falls back to the two lists one after the other)."""
+    from sparse_paged_attention_amd import api
+    p = synth.make_problem("bwd_dup", "prefill", [700], 64, 1, 128, 16, 64, 4, 32, seed=90,
+                           query_positions=[(0, t) for t in range(600, 608)], selection="random")
+    p.cmp_idx[2, 5] = p.cmp_idx[2, 1]
+    dp = api.DeviceProblem.from_problem(p)
+    o, lse = api.forward(dp)
+    d_o = torch.from_numpy(_dO(p, 3).view(np.int16)).cuda().view(torch.bfloat16)
+    announce("backward: a group listed twice, pairs vs single")
+    res = []
+    for qpb in (2, 1):
+        g = api.backward(dp, o, lse, d_o, queries_per_block=qpb)
+        torch.cuda.synchronize()
+        res.append({k: v.cpu().numpy() for k, v in g.items() if v is not None and not k.startswith("_")})
+    for k in res[0]:
+        a, b = res[0][k], res[1][k]
+        scale = float(np.max(np.abs(b))) or 1.0
+        assert np.max(np.abs(a - b)) <= 1e-5 * scale, k
 
 
 def test_backward_decode_two_head_blocks():
