@@ -73,7 +73,14 @@ typedef enum spa_status {
 
 typedef enum spa_dtype {
   SPA_BF16 = 0,
-  SPA_FP8_E4M3_OCP = 1      /* OCP e4m3: bias 7, no inf, 0x7F/0xFF NaN, max 448 */
+  SPA_FP8_E4M3_OCP = 1,     /* OCP e4m3: bias 7, no inf, 0x7F/0xFF NaN, max 448 */
+  SPA_FP8_E4M3_FNUZ = 2     /* FNUZ e4m3 (the gfx942 format, named beside OCP in
+                               the RL-Kernel joint attention PR, "Reuse and
+                               arithmetic"): bias 8, no inf, no -0, 0x80 NaN,
+                               max 240.  Compressed pages only, read by the
+                               decode-slice kernel (decode, head_dim 128,
+                               heads_per_block = queries_per_block = 0);
+                               SPA_ERR_UNSUPPORTED elsewhere               */
 } spa_dtype;
 
 #define SPA_MAX_SPLITS 64
@@ -98,7 +105,7 @@ typedef struct spa_fwd_args {
                              complete group, no list                              */
   float scale;            /* > 0, multiplies q.k; not applied to the sink        */
   int32_t raw_dtype;      /* spa_dtype: must be SPA_BF16                         */
-  int32_t cmp_dtype;      /* spa_dtype: SPA_BF16 or SPA_FP8_E4M3_OCP             */
+  int32_t cmp_dtype;      /* spa_dtype: SPA_BF16, SPA_FP8_E4M3_OCP or _FNUZ      */
   int32_t num_splits;     /* 1 = one pass; >1 = split-KV partials + LSE merge    */
   int32_t heads_per_block; /* query heads one job computes, sharing each KV
                               tile: 32 or 64, or 0 = chosen by the library: a

@@ -11,7 +11,7 @@ tables, score it, and take one softmax whose denominator also holds the
 per-head sink logit (which has no value row).  Everything runs in float64.
 
 Modules:
-  formats    bf16 and OCP e4m3 decoding (exact, to float64)
+  formats    bf16, OCP e4m3 and FNUZ e4m3 decoding (exact, to float64)
   sparse_attention  KV-set metadata, gather, attention with sink, (O, LSE) merge
   topk       top-k selection of compressed groups from per-token scores
   backward   gradients of q, the caches and the sink (float64)
@@ -20,7 +20,7 @@ Modules:
 Every function cites the passage it follows.  Pins live in
 ``tests/test_oracle_*.py``.
 """
-from .formats import bf16_to_f64, e4m3_table, e4m3_to_f64  # noqa: F401
+from .formats import bf16_to_f64, e4m3_table, e4m3_to_f64, e4m3fnuz_table, e4m3fnuz_to_f64  # noqa: F401
 from .sparse_attention import (  # noqa: F401
     KVSet, kv_set, kv_sets, gather_rows, attend, attend_partial, merge, attention,
     gather_plan, partial_split, physical_rows, query_f64, lse_merge_arrays,

@@ -36,7 +36,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from .formats import bf16_to_f64, e4m3_to_f64
+from .formats import bf16_to_f64, e4m3_to_f64, e4m3fnuz_to_f64
 
 
 @dataclasses.dataclass
@@ -127,8 +127,9 @@ def gather_rows(p, s: KVSet) -> Tuple[np.ndarray, np.ndarray]:
     kr = bf16_to_f64(p.k_raw[wrow // P, wrow % P])
     vr = bf16_to_f64(p.v_raw[wrow // P, wrow % P])
     if p.cmp_fp8:
-        kc = e4m3_to_f64(p.k_cmp[crow // P, crow % P])
-        vc = e4m3_to_f64(p.v_cmp[crow // P, crow % P])
+        dec = e4m3fnuz_to_f64 if getattr(p, "cmp_fp8_fnuz", False) else e4m3_to_f64
+        kc = dec(p.k_cmp[crow // P, crow % P])
+        vc = dec(p.v_cmp[crow // P, crow % P])
         kc = kc * p.k_cmp_scale[crow // P, crow % P].astype(np.float64)[..., None]
         vc = vc * p.v_cmp_scale[crow // P, crow % P].astype(np.float64)[..., None]
     else:

@@ -20,6 +20,7 @@ STATUS_NAMES = {
 }
 SPA_BF16 = 0
 SPA_FP8_E4M3_OCP = 1
+SPA_FP8_E4M3_FNUZ = 2
 SPA_MAX_SPLITS = 64
 
 # exported symbols, in include/spa.h order

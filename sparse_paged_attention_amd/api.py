@@ -55,6 +55,7 @@ class DeviceProblem:
     cmp_idx: Optional[torch.Tensor]
     cmp_cnt: Optional[torch.Tensor]
     sink: Optional[torch.Tensor]
+    cmp_fp8_fnuz: bool = False           # e4m3 pages in the FNUZ variant
 
     @classmethod
     def from_problem(cls, p, device="cuda") -> "DeviceProblem":
@@ -93,6 +94,7 @@ class DeviceProblem:
             cmp_idx=dev(p.cmp_idx) if (has_cmp and p.topk > 0) else None,
             cmp_cnt=dev(p.cmp_cnt) if (has_cmp and p.topk > 0) else None,
             sink=dev(p.sink) if p.sink is not None else None,
+            cmp_fp8_fnuz=bool(getattr(p, "cmp_fp8_fnuz", False)),
         )
 
     def args(self, num_splits: Optional[int] = None, heads_per_block: int = 0,
@@ -109,7 +111,8 @@ class DeviceProblem:
         a.topk = self.topk
         a.scale = self.scale
         a.raw_dtype = _lib.SPA_BF16
-        a.cmp_dtype = _lib.SPA_FP8_E4M3_OCP if self.cmp_fp8 else _lib.SPA_BF16
+        a.cmp_dtype = ((_lib.SPA_FP8_E4M3_FNUZ if self.cmp_fp8_fnuz else _lib.SPA_FP8_E4M3_OCP) if self.cmp_fp8
+                       else _lib.SPA_BF16)
         a.num_splits = self.num_splits if num_splits is None else num_splits
         a.heads_per_block = heads_per_block
         a.queries_per_block = queries_per_block

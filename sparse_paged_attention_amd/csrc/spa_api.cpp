@@ -71,7 +71,7 @@ spa_status validate(const spa_fwd_args *a, bool decode, bool need_outputs) {
       return fail(SPA_ERR_UNSUPPORTED, "head_dim 512 takes heads_per_block 0 and queries_per_block 0");
   }
   if (a->raw_dtype != SPA_BF16) return fail(SPA_ERR_DTYPE, "raw_dtype must be SPA_BF16 (got %d)", a->raw_dtype);
-  if (a->cmp_dtype != SPA_BF16 && a->cmp_dtype != SPA_FP8_E4M3_OCP)
+  if (a->cmp_dtype != SPA_BF16 && a->cmp_dtype != SPA_FP8_E4M3_OCP && a->cmp_dtype != SPA_FP8_E4M3_FNUZ)
     return fail(SPA_ERR_DTYPE, "cmp_dtype %d unknown", a->cmp_dtype);
   if (a->num_splits < 1 || a->num_splits > SPA_MAX_SPLITS)
     return fail(SPA_ERR_SPLITS, "num_splits %d outside [1, %d]", a->num_splits, SPA_MAX_SPLITS);
@@ -94,7 +94,7 @@ spa_status validate(const spa_fwd_args *a, bool decode, bool need_outputs) {
   if (a->ratio > 0) {
     if (a->k_cmp == nullptr || a->v_cmp == nullptr) return fail(SPA_ERR_NULL, "k_cmp/v_cmp is NULL");
     if (a->cmp_pt == nullptr) return fail(SPA_ERR_NULL, "cmp_pt is NULL");
-    if (a->cmp_dtype == SPA_FP8_E4M3_OCP && (a->k_cmp_scale == nullptr || a->v_cmp_scale == nullptr))
+    if (a->cmp_dtype != SPA_BF16 && (a->k_cmp_scale == nullptr || a->v_cmp_scale == nullptr))
       return fail(SPA_ERR_NULL, "FP8 compressed KV needs k_cmp_scale and v_cmp_scale");
   }
   if (a->topk > 0 && (a->cmp_idx == nullptr || a->cmp_cnt == nullptr))
@@ -189,7 +189,8 @@ spa::Params make_params(const spa_fwd_args *a, bool decode) {
   p.page_shift = -1;
   for (int32_t sh = 0; sh < 31; ++sh)
     if ((int32_t(1) << sh) == a->page_size) p.page_shift = sh;
-  p.cmp_fp8 = (a->ratio > 0 && a->cmp_dtype == SPA_FP8_E4M3_OCP) ? 1 : 0;
+  p.cmp_fp8 = (a->ratio > 0 && (a->cmp_dtype == SPA_FP8_E4M3_OCP || a->cmp_dtype == SPA_FP8_E4M3_FNUZ)) ? 1 : 0;
+  p.cmp_fnuz = (a->ratio > 0 && a->cmp_dtype == SPA_FP8_E4M3_FNUZ) ? 1 : 0;
   p.scale_log2 = a->scale * 1.4426950408889634f;
   return p;
 }
@@ -227,6 +228,9 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
   const bool slices = decode && a->heads_per_block == 0 && a->queries_per_block == 0 &&
                       spa::decode_slices_eligible(p);
   const bool latent = a->head_dim == 512;
+  if (p.cmp_fnuz && !slices)
+    return fail(SPA_ERR_UNSUPPORTED, "FNUZ e4m3 pages are read by the decode-slice kernel only: decode, head_dim "
+                "128, heads_per_block and queries_per_block 0, and slices within %d rows", spa::kPairRowsMax);
   hipError_t e = latent   ? spa::launch_latent(p, s)
                  : pairs  ? spa::launch_prefill_pairs(p, s)
                  : slices ? spa::launch_decode_slices(p, s)

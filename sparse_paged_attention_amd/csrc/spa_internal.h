@@ -37,7 +37,8 @@ struct Params {
   int32_t jobs_per_unit;
   int32_t unit_begin, unit_end;
   int32_t page_shift;                 // log2(page_size) when a power of two, else -1
-  int32_t cmp_fp8;
+  int32_t cmp_fp8;                    // e4m3 compressed pages
+  int32_t cmp_fnuz;                   // ... in the FNUZ variant (decode slices only)
   float scale_log2;                   // scale * log2(e)
 };
 

@@ -498,6 +498,7 @@ void attn_pair_kernel(const Params p) {
   }
   const int32_t ntiles = (U + kPT - 1) / kPT;
   const int32_t nf8 = FP8 ? wbase / kPT : 0;         // tiles 0 .. nf8-1 hold e4m3 rows
+  const bool fnuz = FP8 && p.cmp_fnuz != 0;          // e4m3 pages in the FNUZ variant
   int64_t nrow[2];
   // an e4m3 tile: wave w moves rows 8w .. 8w+7 of D bytes per side (one
   // 1 KiB load each, lane L: row 8w + L / 8, bytes 16 (L % 8) ..), into the
@@ -684,10 +685,24 @@ void attn_pair_kernel(const Params p) {
           const int r = idx / (kD / 8);
           const int piece = idx - r * (kD / 8);
           const uint2 w = *(const uint2 *)(src + r * kD + piece * 8);
-          const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-          const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-          const f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-          const f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+          f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+          f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+          f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+          f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+          if (fnuz) {
+            // FNUZ code c is OCP code c halved (bias 8 against 7), except
+            // 0x7F / 0xFF (+-240; OCP NaN) and 0x80 (NaN; OCP -0)
+            auto fix = [](float x, uint32_t word, int byte) {
+              const uint32_t c = (word >> (8 * byte)) & 0xFFu;
+              return (c & 0x7Fu) == 0x7Fu ? ((c & 0x80u) ? -240.f : 240.f)
+                     : c == 0x80u          ? __builtin_bit_cast(float, 0x7FC00000u)
+                                           : 0.5f * x;
+            };
+            a0 = f32x2{fix(a0[0], w.x, 0), fix(a0[1], w.x, 1)};
+            a1 = f32x2{fix(a1[0], w.x, 2), fix(a1[1], w.x, 3)};
+            a2 = f32x2{fix(a2[0], w.y, 0), fix(a2[1], w.y, 1)};
+            a3 = f32x2{fix(a3[0], w.y, 2), fix(a3[1], w.y, 3)};
+          }
           uint4 o;
           o.x = pack_bf16_hi(a0[0], a0[1]);
           o.y = pack_bf16_hi(a1[0], a1[1]);

@@ -47,8 +47,10 @@ import numpy as np
 
 BF16_NAN = np.uint16(0x7FC0)
 E4M3_NAN = np.uint8(0x7F)
+E4M3FNUZ_NAN = np.uint8(0x80)
 PT_PAD = np.int32(0x7FFFFFFF)
 E4M3_MAX = 448.0
+E4M3FNUZ_MAX = 240.0
 
 
 @dataclasses.dataclass
@@ -81,6 +83,7 @@ class Problem:
     cmp_idx: np.ndarray            # int32 [Nq, max(topk, 1)], -1 padded
     cmp_cnt: np.ndarray            # int32 [Nq]
     sink: Optional[np.ndarray]     # float32 [Hq] or None (= -inf)
+    cmp_fp8_fnuz: bool = False     # e4m3 pages in the FNUZ variant (else OCP)
     # logical (unpaged) copies, used only by tests that bypass page tables
     k_raw_logical: Optional[list] = None   # per seq: [len, Hkv, D]
     v_raw_logical: Optional[list] = None
@@ -147,6 +150,36 @@ def quantize_e4m3(y: np.ndarray) -> np.ndarray:
     return (codes | sign).astype(np.uint8)
 
 
+def _fnuz_grid() -> np.ndarray:
+    """The 128 non-negative finite FNUZ e4m3 values, by code 0x00 .. 0x7F
+    (bias 8: subnormals m/8 * 2^-7, normals (1 + m/8) * 2^(e-8))."""
+    v = []
+    for c in range(128):
+        e, m = c >> 3, c & 7
+        v.append((m / 8.0) * 2.0 ** -7 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 8))
+    return np.array(v, dtype=np.float64)
+
+
+_FNUZ_GRID = _fnuz_grid()
+
+
+def quantize_e4m3_fnuz(y: np.ndarray) -> np.ndarray:
+    """Encode float values as FNUZ e4m3 (bias 8, max 240, no negative zero).
+
+    Round to nearest, ties to the even code, saturating to +-240; zero and
+    values that round to zero get code 0x00 (0x80 is NaN).  Returns uint8.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), E4M3FNUZ_MAX)
+    hi = np.clip(np.searchsorted(_FNUZ_GRID, a, side="left"), 0, 127)
+    lo = np.clip(hi - 1, 0, 127)
+    dlo, dhi = a - _FNUZ_GRID[lo], _FNUZ_GRID[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    sign = (np.signbit(y) & (code != 0)).astype(np.uint8) << 7
+    return (code | sign).astype(np.uint8)
+
+
 # ---------------------------------------------------------------- builders
 
 def _spawn(seed: int, n: int):
@@ -193,7 +226,7 @@ def _scatter(pool, pages, logical, page_size):
 def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head_dim,
                  page_size, window, ratio, topk, *, seed, cmp_fp8=False, num_splits=1,
                  query_positions=None, selection="random", with_sink=True,
-                 scale=None, spare_pages=3, keep_logical=True, shared_kv=False):
+                 scale=None, spare_pages=3, keep_logical=True, shared_kv=False, fp8_format="ocp"):
     """Generic builder used by every named workload and by parametrised tests.
 
     ``query_positions``: prefill only, a list of (seq, pos) pairs.  Decode
@@ -203,7 +236,10 @@ def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head
     (list of every complete group in ascending order).
     ``shared_kv``: one latent cache per pool serves as K and V (the value
     arrays are the key arrays, the same objects); bf16 only.
+    ``fp8_format``: "ocp" (max 448) or "fnuz" (max 240) for e4m3 pages.
     """
+    fnuz = cmp_fp8 and fp8_format == "fnuz"
+    qmax = np.float32(E4M3FNUZ_MAX if fnuz else E4M3_MAX)
     if shared_kv and cmp_fp8:
         raise ValueError("a shared latent cache is bf16")
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
@@ -239,8 +275,9 @@ def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head
     cmp_pt, cmp_pages_n, cmp_pages = _page_pool(r_pages, n_groups, P, spare_pages)
     kc_log, vc_log, ks_log, vs_log = [], [], [], []
     if cmp_fp8:
-        k_cmp = np.full((cmp_pages_n, P, Hkv, D), E4M3_NAN, dtype=np.uint8)
-        v_cmp = np.full_like(k_cmp, E4M3_NAN)
+        poison = E4M3FNUZ_NAN if fnuz else E4M3_NAN
+        k_cmp = np.full((cmp_pages_n, P, Hkv, D), poison, dtype=np.uint8)
+        v_cmp = np.full_like(k_cmp, poison)
         k_sc = np.full((cmp_pages_n, P, Hkv), np.nan, dtype=np.float32)
         v_sc = np.full_like(k_sc, np.nan)
     else:
@@ -254,9 +291,10 @@ def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head
             for _ in range(2):
                 x = r_cmp.standard_normal((g, Hkv, D), dtype=np.float32)
                 amax = np.max(np.abs(x), axis=-1)
-                sc = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+                sc = (amax / qmax).astype(np.float32)
                 sc = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
-                codes = quantize_e4m3(x.astype(np.float64) / sc[..., None].astype(np.float64))
+                quant = quantize_e4m3_fnuz if fnuz else quantize_e4m3
+                codes = quant(x.astype(np.float64) / sc[..., None].astype(np.float64))
                 pair.append((codes, sc))
             (kc, ks), (vc, vs) = pair
             _scatter(k_sc, cmp_pages[b], ks, P)
@@ -307,7 +345,7 @@ def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head
         cmp_fp8=cmp_fp8, num_splits=num_splits, q=q, k_raw=k_raw, v_raw=v_raw,
         k_cmp=k_cmp, v_cmp=v_cmp, k_cmp_scale=k_sc, v_cmp_scale=v_sc, raw_pt=raw_pt,
         cmp_pt=cmp_pt, seq_lens=seq_lens, query_seq=qs, query_pos=qp, cmp_idx=cmp_idx,
-        cmp_cnt=cmp_cnt, sink=sink)
+        cmp_cnt=cmp_cnt, sink=sink, cmp_fp8_fnuz=fnuz)
     if keep_logical:
         p.k_raw_logical, p.v_raw_logical = k_log, v_log
         p.k_cmp_logical, p.v_cmp_logical = kc_log, vc_log

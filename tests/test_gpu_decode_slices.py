@@ -89,3 +89,24 @@ def test_fp8_partial_compressed_tiles():
     p = _decode("f8p", rng.integers(20, 900, size=7), 160, 2, 16, 45, 4, 37, cmp_fp8=True)
     for s in (1, 3, 11):
         check_against_oracle(p, num_splits=s, label=f"fp8 partial tiles S{s}")
+
+
+@pytest.mark.parametrize("splits", [1, 4, 8])
+def test_fnuz_pages_slices(splits):
+    """FNUZ e4m3 compressed pages (bias 8, max 240), quantised with scale
+    amax/240 so the 0x7F / 0xFF codes occur, read by the decode-slice
+    kernel; unowned page rows hold the FNUZ NaN code 0x80."""
+    p = synth.make_problem("fnuz", "decode", [3000, 1500, 700, 5000, 129], 128, 1, 128, 64, 128, 4, 512, seed=44,
+                           cmp_fp8=True, fp8_format="fnuz", selection="random")
+    assert np.any(p.k_cmp == 0x7F) and np.any(p.v_cmp == 0xFF)
+    check_against_oracle(p, splits, label=f"fnuz S={splits}")
+
+
+def test_fnuz_pages_refused_outside_the_slice_kernel():
+    from sparse_paged_attention_amd import api, _lib
+    p = synth.make_problem("fnuz_pre", "prefill", [600], 64, 1, 128, 16, 128, 4, 64, seed=45, cmp_fp8=True,
+                           fp8_format="fnuz", query_positions=[(0, t) for t in range(590, 598)])
+    dp = api.DeviceProblem.from_problem(p)
+    with pytest.raises(_lib.SpaError) as e:
+        api.forward(dp, 1)
+    assert e.value.status == -4

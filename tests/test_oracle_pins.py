@@ -174,8 +174,9 @@ def _brute(p):
         members = []   # (k row f64[Hkv,D], v row)
         kr, vr = _bf(p.k_raw_logical[b]), _bf(p.v_raw_logical[b])
         if p.cmp_fp8:
-            kc = oracle.e4m3_to_f64(p.k_cmp_logical[b]) * p.k_cmp_scale_logical[b].astype(np.float64)[..., None]
-            vc = oracle.e4m3_to_f64(p.v_cmp_logical[b]) * p.v_cmp_scale_logical[b].astype(np.float64)[..., None]
+            dec = oracle.e4m3fnuz_to_f64 if p.cmp_fp8_fnuz else oracle.e4m3_to_f64
+            kc = dec(p.k_cmp_logical[b]) * p.k_cmp_scale_logical[b].astype(np.float64)[..., None]
+            vc = dec(p.v_cmp_logical[b]) * p.v_cmp_scale_logical[b].astype(np.float64)[..., None]
         else:
             kc, vc = _bf(p.k_cmp_logical[b]), _bf(p.v_cmp_logical[b])
         for c in range(kc.shape[0]):
@@ -218,6 +219,17 @@ def test_brute_force_variants(fp8, topk, ratio):
     p = synth.make_problem("bv", "prefill", [L], 4, 2, 8, 8, 6, ratio, topk, seed=9,
                            cmp_fp8=fp8, query_positions=[(0, t) for t in (0, 5, 20, 36)],
                            selection="random")
+    O, LSE = oracle.attention(p)
+    Ob, Lb = _brute(p)
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(LSE, Lb, rtol=0, atol=1e-12)
+
+
+def test_brute_force_fnuz_pages():
+    L = 37
+    p = synth.make_problem("bvf", "prefill", [L], 4, 2, 8, 8, 6, 4, 5, seed=19, cmp_fp8=True,
+                           fp8_format="fnuz", query_positions=[(0, t) for t in (3, 20, 36)], selection="random")
+    assert p.cmp_fp8_fnuz
     O, LSE = oracle.attention(p)
     Ob, Lb = _brute(p)
     np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
@@ -412,6 +424,41 @@ def test_sink_limits():
 
 
 # ------------------------------------------------------------ formats
+
+def test_e4m3fnuz_table_properties():
+    """FNUZ e4m3 (bias 8): +-240 at 0x7F / 0xFF, the only NaN at 0x80, the
+    smallest subnormal 2^-10 and smallest normal 2^-7, sign symmetry, a
+    monotone positive half, and the cross-format identity FNUZ(c) = OCP(c)/2
+    for every other code (the exponent bias is one larger)."""
+    f = oracle.e4m3fnuz_table()
+    o = oracle.e4m3_table()
+    assert f[0x7F] == 240.0 and f[0xFF] == -240.0
+    assert np.isnan(f[0x80]) and np.isnan(f).sum() == 1
+    assert f[0x01] == 2.0 ** -10 and f[0x08] == 2.0 ** -7 and f[0x00] == 0.0
+    assert np.all(np.diff(f[:0x80]) > 0)
+    for c in range(1, 128):
+        assert f[c | 0x80] == -f[c]
+    for c in range(256):
+        if c not in (0x7F, 0xFF, 0x80):
+            assert f[c] == o[c] / 2, hex(c)
+
+
+def test_e4m3fnuz_quantise_roundtrip_and_rounding():
+    f = oracle.e4m3fnuz_table()
+    codes = np.array([c for c in range(256) if c != 0x80], dtype=np.uint8)
+    back = synth.quantize_e4m3_fnuz(f[codes])
+    assert np.all(f[back] == f[codes])           # every finite value maps to its own value
+    assert not np.any(back == 0x80)
+    # midpoints between neighbours round to the even code; beyond 240 saturates
+    pos = f[:0x80]
+    mids = (pos[:-1] + pos[1:]) / 2
+    got = synth.quantize_e4m3_fnuz(mids)
+    want = np.where(np.arange(127) % 2 == 0, np.arange(127), np.arange(1, 128))
+    assert np.array_equal(got, want.astype(np.uint8))
+    assert synth.quantize_e4m3_fnuz(np.array([1e6, -1e6]))[0] == 0x7F
+    assert synth.quantize_e4m3_fnuz(np.array([-1e6]))[0] == 0xFF
+    assert synth.quantize_e4m3_fnuz(np.array([-0.0, -1e-9]))[0] == 0x00
+
 
 def test_e4m3_table_enumeration():
     """The OCP e4m3 finite positives are m*2^-9 (m = 0..7, subnormal) and
