@@ -188,10 +188,6 @@ def test_merge_validation(lib):
     # o_parts is read 16 bytes per lane, o_out written 8 bytes per lane
     assert lib.attn_merge_lse(good["o"] + 8, good["l"], 2, 10, 128, 4, None, good["out"], None, None) == -5
     assert lib.attn_merge_lse(good["o"], good["l"], 2, 10, 128, 4, None, good["out"] + 4, None, None) == -5
-    assert lib.attn_merge_lse_bf16(None, good["l"], 2, 10, 128, 4, None, good["out"], None, None) == -1
-    assert lib.attn_merge_lse_bf16(good["o"], good["l"], 0, 10, 128, 4, None, good["out"], None, None) == -7
-    assert lib.attn_merge_lse_bf16(good["o"], good["l"], 2, 10, 64, 4, None, good["out"], None, None) == -4
-    assert lib.attn_merge_lse_bf16(good["o"] + 2, good["l"], 2, 10, 128, 4, None, good["out"], None, None) == -5
 
 
 def test_gather_validation(lib):
