@@ -8,9 +8,13 @@ HBM.  The default workload is "Decode CSA": batch 32, one query per sequence
 at context 4096, 128 query heads sharing one KV head, D 128, bf16, page 64,
 window 128 + top-k 512 of 1024 ratio-4 groups.
 
-Inputs are replicated on the device and the timed steps rotate through the
-replicas, so the KV rows each step reads are not resident in the 256 MB
-memory-side cache (the working set rotated through is > 512 MB).
+Inputs are replicated on the device and the steps rotate through the
+replicas: every replica is read once before any is read again, whatever
+--steps is, so the bytes read between two reads of the same replica exceed
+--rotate-mb (640 MB; the memory-side cache is 256 MB) and the KV rows each
+step reads are not resident in any cache.  The replicas are split into
+graphs of exactly --steps calls each; each timed measurement is one replay of
+one such graph, and the graphs are replayed in turn.
 
 Prints one JSON line (see --help for options).
 """
@@ -30,14 +34,15 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the sources whose change invalidates counter-measured traffic
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
-                  for f in ("spa_attention.hip", "spa_pair.hip", "spa_latent.hip", "spa_kernel_util.h", "spa_device.h",
-                            "spa_internal.h", "spa_api.cpp")]
+                  for f in ("spa_attention.hip", "spa_pair.hip", "spa_decode.hip", "spa_latent.hip",
+                            "spa_kernel_util.h", "spa_device.h", "spa_internal.h", "spa_api.cpp")]
 # sources of the top-k and backward kernels (their traffic entries carry these hashes)
 TOPK_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
                 for f in ("spa_topk.hip", "spa_internal.h", "spa_api.cpp")]
 BWD_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
                for f in ("spa_backward.hip", "spa_kernel_util.h", "spa_device.h", "spa_internal.h", "spa_api.cpp")]
 PAIR_ROWS_MAX = 1280           # rows a query pair's union can hold in the prefill pair kernel
+DECODE_ROWS_MAX = 1280         # rows of one decode slice in the decode kernel
 
 
 def attention_kernel(p, splits, hpb, qpb):
@@ -56,13 +61,14 @@ def attention_kernel(p, splits, hpb, qpb):
     cper = -(-cap // S)
     if p.cmp_fp8:
         cper = -(-cper // 32) * 32          # e4m3 rows fill whole tiles
-    slices_ok = (p.mode == "decode" and p.head_dim == 128 and hpb == 0 and qpb == 0
-                 and cper + -(-p.window // S) <= PAIR_ROWS_MAX)
+    decode_ok = (p.mode == "decode" and p.head_dim == 128 and hpb == 0 and qpb == 0 and S <= 64
+                 and cper + -(-p.window // S) <= DECODE_ROWS_MAX)
     if pairs:
         return "attn_pair_kernel<2, false, false>"
-    if slices_ok:
-        return "attn_pair_kernel<2, true, true>" if p.cmp_fp8 else "attn_pair_kernel<2, true, false>"
+    if decode_ok:
+        return "attn_decode_kernel<true>" if p.cmp_fp8 else "attn_decode_kernel<false>"
     return "attn_fwd_kernel"
+
 
 
 def kernel_source_hash(files=None):
@@ -134,30 +140,34 @@ def algorithmic_work(p, counts):
     return kv_bytes + idx_bytes + qo_bytes, flops, int((win_len + n_sel).sum())
 
 
-def cpu_baseline(p, budget_s):
-    """Time the FP64 oracle on the host cores over a bounded sample."""
-    import numpy as np
-    import oracle
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(p, budget_s):
+    """Time the FP64 oracle on the host over a bounded sample: one process,
+    its BLAS limited to one thread, so `cores` is what it used."""
+    import oracle
+    from threadpoolctl import threadpool_limits
     nq = p.num_queries
     done = 0
-    t0 = time.perf_counter()
-    while True:
-        for i in range(nq):
-            oracle.attention(p, [i])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 <= budget_s:
+            oracle.attention(p, [done % nq])
             done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} queries of the same workload (first {min(done, nq)} distinct), "
-                      f"{dt:.1f} s single process, numpy fp64"}
+        dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{done} queries of the same workload (query i % {nq}), {dt:.1f} s, one process, "
+                      f"numpy fp64 with one BLAS thread"}
 
 
 def parse_args(argv=None):
@@ -207,35 +217,47 @@ def eager_ms(launch, n):
     return ms, np.array([ms])
 
 
-def graph_replay_ms(launch, n):
-    """Per-launch time of `n` calls of `launch(stream, k)` captured in one
-    HIP graph and replayed 5 times back to back (HIP events on the capture
-    stream); also the per-replay times."""
+def graph_replay_ms(launch, steps, reps=1, rounds=2):
+    """Per-call time of `launch(stream, k)` from HIP graph replays.
+
+    Call k uses replica k % reps.  The calls are captured in G = ceil(reps /
+    steps) graphs of exactly `steps` calls (graph g holds calls g*steps ..
+    g*steps + steps - 1), so replaying the graphs in turn reads every replica
+    once before any is read again.  After one untimed replay of every graph,
+    each measurement is one replay of one graph (HIP events on the capture
+    stream); `rounds` passes over the G graphs.  Returns (median ms per call,
+    per-measurement ms per call, G)."""
     import numpy as np
     import torch
+    G = max(1, -(-reps // steps))
     cap_stream = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
+    graphs = []
     with torch.cuda.stream(cap_stream):
         for k in range(3):
             launch(cap_stream.cuda_stream, k)
         cap_stream.synchronize()
-        with torch.cuda.graph(graph, stream=cap_stream):
-            cs = torch.cuda.current_stream()
-            for k in range(n):
-                launch(cs.cuda_stream, k)
+        for g in range(G):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=cap_stream):
+                cs = torch.cuda.current_stream()
+                for k in range(steps):
+                    launch(cs.cuda_stream, g * steps + k)
+            graphs.append(graph)
         torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        reps_g = 5
-        ge = [torch.cuda.Event(enable_timing=True) for _ in range(reps_g + 1)]
-        ge[0].record(cap_stream)
-        for r in range(reps_g):
+        for graph in graphs:
             graph.replay()
-            ge[r + 1].record(cap_stream)
         torch.cuda.synchronize()
-    per = np.array([ge[r].elapsed_time(ge[r + 1]) / n for r in range(reps_g)])
-    return float(ge[0].elapsed_time(ge[reps_g]) / (n * reps_g)), per
-
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * G * rounds)]
+        n = 0
+        for _ in range(rounds):
+            for graph in graphs:
+                ev[n].record(cap_stream)
+                graph.replay()
+                ev[n + 1].record(cap_stream)
+                n += 2
+        torch.cuda.synchronize()
+    per = np.array([ev[2 * m].elapsed_time(ev[2 * m + 1]) / steps for m in range(G * rounds)])
+    return float(np.median(per)), per, G
 
 
 def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries_per_block=-1,
@@ -311,22 +333,22 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
     wall = time.perf_counter() - t_wall0
     eager_ms = e0.elapsed_time(e1) / steps
 
-    replay_ms = graph_replay_ms
-
     def fwd_launch(s, k):
         st = fn(prepared[k % reps], s)
         if st != 0:
             _lib.check(st)
 
+    kernel = attention_kernel(p, splits, hpb, qpb)
+    n_graphs = 1
     if eager_only:
         ms_per_step, per = eager_ms, np.array([eager_ms])
         merge_ms = 0.0
     else:
-        # the whole step: attention (+ the LSE merge when split)
-        ms_per_step, per = replay_ms(fwd_launch, steps)
-        # the merge alone (same launch through its own entry point, on the
-        # partials the step left in each replica's workspace), so that the
-        # attention kernel's own duration is the difference
+        # the whole call: attention (+ the LSE merge when split)
+        ms_per_step, per, n_graphs = graph_replay_ms(fwd_launch, steps, reps)
+        # the merge kernel of a split call, timed alone through attn_merge_lse
+        # on the partials each call left in its replica's workspace, so that
+        # the attention kernel's own duration is the difference
         merge_ms = 0.0
         if splits > 1:
             rows = p.num_queries * p.num_q_heads
@@ -340,23 +362,30 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
                 if st != 0:
                     _lib.check(st)
 
-            merge_ms, _ = replay_ms(merge_launch, steps)
+            merge_ms, _, _ = graph_replay_ms(merge_launch, steps, reps)
     kernel_ms = ms_per_step - merge_ms
 
     nq = p.num_queries
     decode = p.mode == "decode"
+    # the roofline of the whole call (attention, plus a separate merge kernel
+    # where there is one); the attention kernel alone beside it
     if decode:
-        roof = {"bound": "hbm", "achieved": alg_bytes / (kernel_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+        roof = {"bound": "hbm", "achieved": alg_bytes / (ms_per_step / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
+        kernel_achieved = alg_bytes / (kernel_ms / 1e3) / 1e9
     else:
-        roof = {"bound": "mfma", "achieved": alg_flops / (kernel_ms / 1e3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "achieved": alg_flops / (ms_per_step / 1e3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
+        kernel_achieved = alg_flops / (kernel_ms / 1e3) / 1e12
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None   # filled in below from the committed counter runs, if they match
-    roof["kernel"] = attention_kernel(p, splits, hpb, qpb)
+    roof["kernel"] = kernel
+    roof["launches_per_call"] = 2 if merge_ms > 0 else 1
     roof["kernel_ms"] = kernel_ms
-    roof["kernel_ms_how"] = ("graph replay of the step minus graph replay of the merge alone" if merge_ms > 0
-                             else "graph replay of the step (one kernel)")
+    roof["kernel_ms_how"] = ("graph replay of the call minus graph replay of the merge alone" if merge_ms > 0
+                             else "graph replay of the call (one kernel)")
+    roof["kernel_achieved"] = kernel_achieved
+    roof["kernel_frac"] = kernel_achieved / roof["peak"]
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     roof["algorithmic_flops_per_launch"] = alg_flops
 
@@ -378,11 +407,14 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
                    "page_size": p.page_size, "window": p.window, "ratio": p.ratio, "topk": p.topk,
                    "kv_entries": kv_entries, "num_splits": splits, "heads_per_block": hpb,
                    "queries_per_block": qpb,
-                   "replicas": reps},
+                   "replicas": reps, "rotated_mb": round(reps * alg_bytes / 1e6, 1), "graphs": n_graphs},
         "roofline": roof,
         "cpu_baseline": cpu_baseline(p, cpu_budget) if cpu_budget > 0 else None,
         "timing": {"graph_replay_ms_per_step_min": float(per.min()),
                    "graph_replay_ms_per_step_max": float(per.max()),
+                   "graph_replay_ms_per_step_p10": float(np.percentile(per, 10)),
+                   "graph_replay_ms_per_step_p90": float(np.percentile(per, 90)),
+                   "measurements": int(per.size),
                    "eager_ms_per_step": eager_ms,
                    "merge_ms": merge_ms,
                    "host_wall_ms_per_step": wall / steps * 1e3,
@@ -432,7 +464,7 @@ def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0, eager_only=False
     for r in range(warmup):
         api.topk_select(sc[r % reps], nv, k)
     torch.cuda.synchronize()
-    ms, per = eager_ms(launch, steps) if eager_only else graph_replay_ms(launch, steps)
+    ms, per = eager_ms(launch, steps) if eager_only else graph_replay_ms(launch, steps, reps)[:2]
     read_b = int(n_valid.sum()) * 4 + rows * 4
     write_b = rows * k * 4 + rows * 4
     achieved = (read_b + write_b) / (ms / 1e3) / 1e9
@@ -520,7 +552,7 @@ def run_backward(workload, *, steps=20, warmup=3, cpu_budget=0.0, rotate_mb=640.
     for k in range(warmup):
         launch(torch.cuda.current_stream().cuda_stream, k)
     torch.cuda.synchronize()
-    ms, per = eager_ms(launch, steps) if eager_only else graph_replay_ms(launch, steps)
+    ms, per = eager_ms(launch, steps) if eager_only else graph_replay_ms(launch, steps, reps)[:2]
     achieved = alg_flops / (ms / 1e3) / 1e12
     cpu = None
     if cpu_budget > 0:

@@ -41,9 +41,12 @@
  *    (never dereferenced) and, when err_flag is not NULL, a bit is OR-ed into
  *    *err_flag: 1 = query sequence/position, 2 = compressed id outside the
  *    complete groups, 4 = page id outside the pool or page-table column out of
- *    range, 8 = list count outside [0, topk].  Page-table columns past the
- *    last page a query needs are never read (RL-Kernel "Fixed paged CK
- *    attention on ROCm": unused page-table columns are not loaded).
+ *    range, 8 = list count outside [0, topk].  Page ids in page-table
+ *    columns past the last page a query needs are never used to address a
+ *    cache (RL-Kernel "Fixed paged CK attention on ROCm": the ids of unused
+ *    columns must not reach the loads); the decode kernel may read such
+ *    columns of a row no longer than 2048 entries (both tables together) in
+ *    one wide load, within the row.
  *  - Inputs are read-only.  After SPA_ERR_LAUNCH the outputs and the
  *    workspace are undefined.
  */
@@ -78,7 +81,7 @@ typedef enum spa_dtype {
                                the RL-Kernel joint attention PR, "Reuse and
                                arithmetic"): bias 8, no inf, no -0, 0x80 NaN,
                                max 240.  Compressed pages only, read by the
-                               decode-slice kernel (decode, head_dim 128,
+                               decode kernel (decode, head_dim 128,
                                heads_per_block = queries_per_block = 0);
                                SPA_ERR_UNSUPPORTED elsewhere               */
 } spa_dtype;
@@ -156,22 +159,23 @@ typedef struct spa_fwd_args {
   int32_t *err_flag;        /* device i32 or NULL, see the conventions above     */
   void *workspace;          /* num_splits > 1: attn_workspace_size() bytes of
                                scratch for the split partials (no initial
-                               contents needed); one call at a time          */
+                               contents needed), 16-byte aligned; one call at
+                               a time                                        */
   size_t workspace_bytes;
 } spa_fwd_args;
 
 /* Bytes of workspace the call needs: 0 when num_splits == 1, otherwise the
-   sink-free split partials f32 O [S, Nq, Hq, D] and f32 LSE [S, Nq, Hq].
+   sink-free split partials f32 O [S, Nq, Hq, D] and f32 LSE [S, Nq, Hq]
+   (the LSE at a 256-byte boundary; no initial contents needed).
    Returns 0 for a NULL or inconsistent argument block. */
 size_t attn_workspace_size(const spa_fwd_args *args);
 
 /* Decode: one query per sequence at position seq_lens[b] - 1
    (query_seq = query_pos = NULL, num_queries = num_seqs).  With num_splits
-   S > 1 every query's canonical KV list is cut into S contiguous slices, each
-   slice yields a sink-free partial (O_s, LSE_s) in the workspace, and a
-   second kernel on the same stream combines the partials plus the sink
-   exactly as attn_merge_lse does (in slice order, so the result is
-   deterministic). */
+   S > 1 every query's canonical KV list is cut into S slices, each slice
+   yields a sink-free partial (O_s, LSE_s) in the workspace, and a second
+   kernel on the same stream combines the partials plus the sink exactly as
+   attn_merge_lse does (in slice order, so the result is deterministic). */
 spa_status attn_fwd_decode(const spa_fwd_args *args, void *stream);
 
 /* Prefill / chunked prefill / multi-token decode: query i sits at

@@ -223,24 +223,24 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
                 "compressed part, and 2 * (topk + window) <= %d", spa::kPairRowsMax);
   const bool pairs = pairs_ok && (a->queries_per_block == 2 ||
                                   (a->queries_per_block == 0 && a->heads_per_block != 32));
-  // Decode: one workgroup per query slice and 128 heads, when the call fits
-  // it and the caller leaves both block sizes to the library.
-  const bool slices = decode && a->heads_per_block == 0 && a->queries_per_block == 0 &&
-                      spa::decode_slices_eligible(p);
+  // Decode: one workgroup per (query, KV head, 128-head block, slice), when
+  // the call fits it and the caller leaves both block sizes to the library.
+  const bool dec = decode && a->heads_per_block == 0 && a->queries_per_block == 0 && spa::decode_eligible(p);
   const bool latent = a->head_dim == 512;
-  if (p.cmp_fnuz && !slices)
-    return fail(SPA_ERR_UNSUPPORTED, "FNUZ e4m3 pages are read by the decode-slice kernel only: decode, head_dim "
-                "128, heads_per_block and queries_per_block 0, and slices within %d rows", spa::kPairRowsMax);
-  hipError_t e = latent   ? spa::launch_latent(p, s)
-                 : pairs  ? spa::launch_prefill_pairs(p, s)
-                 : slices ? spa::launch_decode_slices(p, s)
-                          : spa::launch_attention(p, s);
+  if (p.cmp_fnuz && !dec)
+    return fail(SPA_ERR_UNSUPPORTED, "FNUZ e4m3 pages are read by the decode kernel only: decode, head_dim 128, "
+                "heads_per_block and queries_per_block 0, and slices within %d rows", spa::kDecodeRowsMax);
+  hipError_t e = latent  ? spa::launch_latent(p, s)
+                 : pairs ? spa::launch_prefill_pairs(p, s)
+                 : dec   ? spa::launch_decode(p, s)
+                         : spa::launch_attention(p, s);
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
   if (a->num_splits > 1) {
     // the job-stream kernel writes each (query, KV head) unit's partials on
-    // one XCD and the merge reads them there; the slice kernel in row order
+    // one XCD and the merge reads them there; the decode and latent kernels
+    // in row order
     e = spa::launch_merge(p.part_o, p.part_lse, a->num_splits, (int64_t)a->num_queries * a->num_q_heads,
-                          a->head_dim, a->num_q_heads, a->sink, p.o, a->lse, (slices || latent) ? 0 : p.group, s);
+                          a->head_dim, a->num_q_heads, a->sink, p.o, a->lse, (dec || latent) ? 0 : p.group, s);
     if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "merge launch failed: %s", hipGetErrorString(e));
   }
   return ok();
@@ -251,7 +251,9 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
 extern "C" {
 
 size_t attn_workspace_size(const spa_fwd_args *args) {
-  if (args == nullptr || args->num_splits < 1 || args->num_queries < 0 || args->num_q_heads < 1) return 0;
+  if (args == nullptr || args->num_splits < 1 || args->num_queries < 0 || args->num_q_heads < 1 ||
+      args->num_kv_heads < 1)
+    return 0;
   if (args->head_dim != 64 && args->head_dim != 128 && args->head_dim != 512) return 0;
   return workspace_bytes_for(args);
 }

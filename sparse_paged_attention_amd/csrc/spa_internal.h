@@ -49,6 +49,7 @@ hipError_t launch_attention(const Params &p, hipStream_t stream);
 // kPairRowsMax rows in the union of a pair's KV sets, which holds whenever
 // 2 * (topk + window) <= kPairRowsMax.
 constexpr int kPairRowsMax = 1280;
+constexpr int kMaxSplits = 64;      // SPA_MAX_SPLITS
 constexpr int kPairStages = 2;      // LDS stages of the tile pipeline (prefill pairs)
 constexpr int kDecodeStages = 2;    // the same for decode slices
 bool prefill_pairs_eligible(const Params &p);
@@ -59,6 +60,14 @@ hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream);
 // merge (in plain row order).
 bool decode_slices_eligible(const Params &p);
 hipError_t launch_decode_slices(const Params &p, hipStream_t stream);
+// Decode (spa_decode.hip): D 128, bf16 or e4m3 compressed pages, one
+// workgroup per (query, KV head, 128-head block, KV slice), a slice's rows
+// (compressed ones rounded up to whole tiles for e4m3) within
+// kDecodeRowsMax.  With several slices it writes sink-free partials (plain
+// row order) for the LSE merge.
+constexpr int kDecodeRowsMax = 1280;
+bool decode_eligible(const Params &p);
+hipError_t launch_decode(const Params &p, hipStream_t stream);
 // 512-wide heads over a shared latent cache (spa_latent.hip): bf16, k_raw ==
 // v_raw and k_cmp == v_cmp; one workgroup per (query, KV head, 64-head block,
 // KV slice); with several slices it writes sink-free partials (plain order).

@@ -27,8 +27,12 @@ def test_kernel_names_follow_the_selection():
     assert bench.attention_kernel(pre, 1, 0, 0) == "attn_pair_kernel<2, false, false>"
     assert bench.attention_kernel(pre, 1, 0, 1) == "attn_fwd_kernel"
     dec = synth.make_workload("decode_csa", batch=2)
-    assert bench.attention_kernel(dec, 4, 0, 0) == "attn_pair_kernel<2, true, false>"
+    assert bench.attention_kernel(dec, 4, 0, 0) == "attn_decode_kernel<false>"
     assert bench.attention_kernel(dec, 4, 64, 0) == "attn_fwd_kernel"
+    fp8 = synth.make_workload("mixed_fp8", batch=2)
+    assert bench.attention_kernel(fp8, 8, 0, 0) == "attn_decode_kernel<true>"
+    # one slice of 512 listed + 128 window rows fits the decode kernel
+    assert bench.attention_kernel(dec, 1, 0, 0) == "attn_decode_kernel<false>"
     lat = synth.make_workload("decode_latent", batch=2)
     assert bench.attention_kernel(lat, 4, 0, 0) == "attn_latent_kernel"
 
@@ -69,3 +73,18 @@ def test_traffic_needs_matching_source_and_config(tmp_path, monkeypatch):
     assert bench.measured_traffic("prefill_csa", cfg) is None
     f.write_text(json.dumps({"decode_csa": {"kernel_source": "0" * 16, "bytes_per_launch": 1.0, "config": cfg}}))
     assert bench.measured_traffic("decode_csa", cfg) is None
+
+
+def test_rotation_reads_every_replica_before_repeating():
+    """The graphs of exactly `steps` calls cover every replica once per pass,
+    for any --steps (the replica of call k is k % reps)."""
+    for steps, reps in ((20, 51), (200, 51), (7, 7), (1, 3)):
+        G = max(1, -(-reps // steps))
+        seen = [(g * steps + k) % reps for g in range(G) for k in range(steps)]
+        assert set(seen) == set(range(reps))
+        first = seen[:reps]
+        assert len(set(first)) == reps        # no replica read twice before all are read
+
+
+def test_cpu_model_is_reported():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()

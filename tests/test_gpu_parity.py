@@ -90,7 +90,7 @@ def test_workspace_reused_across_calls():
     from sparse_paged_attention_amd import api
     ws = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device="cuda")   # NaN-ish garbage
     for name, batch, s in (("decode_csa", 5, 4), ("decode_csa", 5, 4), ("decode_hca", 2, 7),
-                           ("mixed_fp8", 3, 3), ("decode_csa", 2, 8)):
+                           ("mixed_fp8", 3, 3), ("decode_csa", 2, 8), ("decode_csa", 7, 64)):
         p = synth.make_workload(name, batch=batch)
         dp = api.DeviceProblem.from_problem(p)
         O, L = api.forward(dp, s, workspace=ws)
