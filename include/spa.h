@@ -178,6 +178,20 @@ size_t attn_workspace_size(const spa_fwd_args *args);
    attn_merge_lse does (in slice order, so the result is deterministic). */
 spa_status attn_fwd_decode(const spa_fwd_args *args, void *stream);
 
+/* Decode that allocates nothing and needs no workspace, for callers that
+   cannot allocate device memory (code under HIP graph capture, tight serving
+   loops, harnesses that forbid allocation): the same operation and kernels
+   as attn_fwd_decode, with the split partials in a scratch array of
+   attn_noalloc_scratch_bytes() bytes (32 MiB) that the library holds per GPU
+   until the process ends.  args->workspace and workspace_bytes are ignored.
+   A call whose partials need more (4 * S * Nq * Hq * (D + 1) bytes, plus
+   alignment) returns SPA_ERR_WORKSPACE before any HIP call.  Every call on a
+   GPU shares that GPU's array (its contents are the last call's), so calls
+   that overlap on one GPU (other streams, other host threads) race; they
+   must be ordered by the caller. */
+spa_status attn_fwd_decode_noalloc(const spa_fwd_args *args, void *stream);
+size_t attn_noalloc_scratch_bytes(void);
+
 /* Prefill / chunked prefill / multi-token decode: query i sits at
    (query_seq[i], query_pos[i]); every KV row it needs, its own and those of
    tokens of the same chunk included, is already in the paged caches. */

@@ -24,7 +24,8 @@ SPA_FP8_E4M3_FNUZ = 2
 SPA_MAX_SPLITS = 64
 
 # exported symbols, in include/spa.h order
-SYMBOLS = ("attn_workspace_size", "attn_fwd_decode", "attn_fwd_prefill", "attn_merge_lse",
+SYMBOLS = ("attn_workspace_size", "attn_fwd_decode", "attn_fwd_decode_noalloc", "attn_noalloc_scratch_bytes",
+           "attn_fwd_prefill", "attn_merge_lse",
            "attn_build_gather", "attn_topk_select", "attn_bwd_workspace_size", "attn_bwd", "attn_last_error",
            "attn_abi_version")
 SPA_MAX_TOPK = 2048
@@ -108,9 +109,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.POINTER(SpaFwdArgs)
     lib.attn_workspace_size.argtypes = [P]
     lib.attn_workspace_size.restype = ctypes.c_size_t
-    for fn in (lib.attn_fwd_decode, lib.attn_fwd_prefill):
+    for fn in (lib.attn_fwd_decode, lib.attn_fwd_prefill, lib.attn_fwd_decode_noalloc):
         fn.argtypes = [P, ctypes.c_void_p]
         fn.restype = ctypes.c_int
+    lib.attn_noalloc_scratch_bytes.argtypes = []
+    lib.attn_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.attn_merge_lse.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_void_p]

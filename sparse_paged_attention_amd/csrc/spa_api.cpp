@@ -8,10 +8,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "spa.h"
@@ -195,19 +197,24 @@ spa::Params make_params(const spa_fwd_args *a, bool decode) {
   return p;
 }
 
-spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
+// `scratch` (the no-allocation entry point): the split partials go there
+// instead of into args->workspace, which is then ignored.
+spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream, void *scratch = nullptr) {
   spa_status st = validate(a, decode, true);
   if (st != SPA_OK) return st;
   if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return fail(SPA_ERR_SHAPE, "scale must be finite and > 0");
   spa::Params p = make_params(a, decode);
   const size_t need = workspace_bytes_for(a);
   if (need > 0) {
-    if (a->workspace == nullptr) return fail(SPA_ERR_WORKSPACE, "num_splits > 1 needs a workspace");
-    if (a->workspace_bytes < need)
-      return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a->workspace_bytes, need);
-    if (!aligned16(a->workspace)) return fail(SPA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    void *ws = scratch != nullptr ? scratch : a->workspace;
+    if (scratch == nullptr) {
+      if (a->workspace == nullptr) return fail(SPA_ERR_WORKSPACE, "num_splits > 1 needs a workspace");
+      if (a->workspace_bytes < need)
+        return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a->workspace_bytes, need);
+      if (!aligned16(a->workspace)) return fail(SPA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
     const WorkspaceLayout w = workspace_layout(a);
-    char *base = static_cast<char *>(a->workspace);
+    char *base = static_cast<char *>(ws);
     p.part_o = reinterpret_cast<float *>(base + w.part_o);
     p.part_lse = reinterpret_cast<float *>(base + w.part_lse);
   }
@@ -246,6 +253,35 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream) {
   return ok();
 }
 
+// ---- the no-allocation decode entry point: its split partials live in a
+// file-scope device array (one per GPU, zero-initialised by the loader, kept
+// until the process ends).  In host code `scratch` is a host-side stand-in,
+// not a device address: the device address is taken once per device with
+// hipGetSymbolAddress (that device current) and used wherever the array's
+// memory is needed.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's scratch array, or nullptr (with
+// the reason recorded) if it cannot be had.
+void *scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -261,6 +297,24 @@ size_t attn_workspace_size(const spa_fwd_args *args) {
 spa_status attn_fwd_decode(const spa_fwd_args *args, void *stream) { return run_forward(args, true, stream); }
 
 spa_status attn_fwd_prefill(const spa_fwd_args *args, void *stream) { return run_forward(args, false, stream); }
+
+size_t attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+spa_status attn_fwd_decode_noalloc(const spa_fwd_args *args, void *stream) {
+  if (args == nullptr) return fail(SPA_ERR_NULL, "args is NULL");
+  spa_status st = validate(args, true, true);
+  if (st != SPA_OK) return st;
+  const size_t need = workspace_bytes_for(args);
+  if (need > kScratchBytes)
+    return fail(SPA_ERR_WORKSPACE, "the split partials need %zu bytes; the no-allocation scratch holds %zu "
+                "(fewer splits or queries per call)", need, kScratchBytes);
+  void *ptr = nullptr;
+  if (need > 0) {
+    ptr = scratch_on_current_device();
+    if (ptr == nullptr) return fail(SPA_ERR_LAUNCH, "no device address for the no-allocation scratch on this device");
+  }
+  return run_forward(args, true, stream, ptr);
+}
 
 spa_status attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t num_parts, int64_t rows,
                           int32_t head_dim, int32_t num_q_heads, const float *sink, void *o_out,

@@ -265,3 +265,17 @@ def test_backward_validation(lib, name, mut_a, mut_g, code):
     assert st == code, (name, st, lib.attn_last_error())
     assert lib.attn_last_error().decode()
     assert lib.attn_bwd_workspace_size(None) == 0
+
+
+def test_noalloc_refuses_oversize_before_any_hip_call(lib):
+    """The no-allocation decode entry point checks the size of its split
+    partials against its fixed scratch array before touching the GPU."""
+    assert lib.attn_noalloc_scratch_bytes() == 32 << 20
+    a = _good_args()
+    a.num_splits = 64
+    a.num_q_heads = a.num_kv_heads * 4096
+    a.workspace = None
+    a.workspace_bytes = 0
+    assert lib.attn_fwd_decode_noalloc(ctypes.byref(a), None) == -6
+    assert b"no-allocation scratch" in lib.attn_last_error()
+    assert lib.attn_fwd_decode_noalloc(None, None) == -1
