@@ -8,6 +8,8 @@ most of them empty."""
 import numpy as np
 import pytest
 
+import oracle
+from oracle.compare import accept
 from sparse_paged_attention_amd import synth
 
 from gpu_helpers import announce, check_against_oracle, need_gpu, run_hip
@@ -110,3 +112,32 @@ def test_fnuz_pages_refused_outside_the_slice_kernel():
     with pytest.raises(_lib.SpaError) as e:
         api.forward(dp, 1)
     assert e.value.status == -4
+
+
+def test_fnuz_every_code():
+    """Every FNUZ e4m3 code in a selected row: one compressed row per query,
+    window 0 and no sink, so O is the decoded V row times its scale.  The 255
+    finite codes (0x7F / 0xFF are +-240) are checked against the oracle's
+    decode table; the NaN code 0x80 sits in V of a query of its own, whose O
+    must be NaN exactly at those dimensions and match elsewhere."""
+    D = 128
+    p = synth.make_problem("fnuzcodes", "decode", [4] * 4, 4, 1, D, 4, 0, 4, 1, seed=2, cmp_fp8=True,
+                           fp8_format="fnuz", with_sink=False)
+    codes = np.array([c for c in range(256) if c != 0x80], dtype=np.uint8)
+    rows = np.resize(codes, (3, D))
+    nan_row = np.resize(np.array([c for c in range(0x01, 0x40)], dtype=np.uint8), D)
+    nan_at = np.arange(3, D, 8)
+    nan_row[nan_at] = 0x80
+    for i in range(4):
+        c = p.cmp_idx[i, 0]
+        pg = p.cmp_pt[i, c // p.page_size]
+        p.v_cmp[pg, c % p.page_size, 0] = rows[i] if i < 3 else nan_row
+        p.k_cmp[pg, c % p.page_size, 0] = rows[(i + 1) % 3] if i < 3 else rows[0]
+    O, L, _ = run_hip(p)
+    Oref, Lref = oracle.attention(p)
+    assert accept(O[:3], L[:3], Oref[:3], Lref[:3]).ok
+    assert np.array_equal(np.isnan(O[3]), np.isnan(Oref[3]))
+    assert np.isnan(O[3][:, nan_at]).all() and not np.isnan(np.delete(O[3], nan_at, axis=1)).any()
+    fin = ~np.isnan(Oref[3])
+    assert np.all(np.abs(O[3][fin] - Oref[3][fin]) <= 1e-2 + 1e-2 * np.abs(Oref[3][fin]))
+    assert np.all(np.abs(L[3] - Lref[3]) <= 1e-3)
