@@ -64,7 +64,7 @@ def attention_kernel(p, splits, hpb, qpb):
     decode_ok = (p.mode == "decode" and p.head_dim == 128 and hpb == 0 and qpb == 0 and S <= 64
                  and cper + -(-p.window // S) <= DECODE_ROWS_MAX)
     if pairs:
-        return "attn_pair_kernel<2, false, false>"
+        return "attn_pair_kernel<3>"
     if decode_ok:
         return "attn_decode_kernel<true>" if p.cmp_fp8 else "attn_decode_kernel<false>"
     return "attn_fwd_kernel"

@@ -324,11 +324,7 @@ void attn_decode_kernel(const Params p) {
           sc[t][4 * q4 + 3] *= k4.w;
         }
       }
-      if (tm[t] != 0xFFFFFFFFu) {            // rows masked (wave-uniform; the tiles are mostly full)
-        const uint32_t tmh = tm[t] >> (4 * hi);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) sc[t][q] = ((tmh >> (8 * (q >> 2) + (q & 3))) & 1u) ? sc[t][q] : -INFINITY;
-      }
+      mask_tile_rows(sc[t], tm[t]);
 #pragma unroll
       for (int q = 0; q < 16; ++q) smax = fmaxf(smax, sc[t][q]);
     }

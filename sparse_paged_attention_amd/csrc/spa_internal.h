@@ -50,16 +50,9 @@ hipError_t launch_attention(const Params &p, hipStream_t stream);
 // 2 * (topk + window) <= kPairRowsMax.
 constexpr int kPairRowsMax = 1280;
 constexpr int kMaxSplits = 64;      // SPA_MAX_SPLITS
-constexpr int kPairStages = 2;      // LDS stages of the tile pipeline (prefill pairs)
-constexpr int kDecodeStages = 2;    // the same for decode slices
+constexpr int kPairStages = 3;      // LDS stages of the tile pipeline (prefill pairs)
 bool prefill_pairs_eligible(const Params &p);
 hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream);
-// Decode with one workgroup per (query, KV head, 128-head block, KV slice)
-// (spa_pair.hip): D 128, bf16 or e4m3 compressed pages, and a slice's rows
-// (compressed ones rounded up to whole tiles for e4m3) within kPairRowsMax.  With several slices it writes sink-free partials for the
-// merge (in plain row order).
-bool decode_slices_eligible(const Params &p);
-hipError_t launch_decode_slices(const Params &p, hipStream_t stream);
 // Decode (spa_decode.hip): D 128, bf16 or e4m3 compressed pages, one
 // workgroup per (query, KV head, 128-head block, KV slice), a slice's rows
 // (compressed ones rounded up to whole tiles for e4m3) within

@@ -17,6 +17,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -59,6 +60,14 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
                : "v"(src), "s"(lds)
                : "memory", "m0");
 }
+// The same with the LDS destination given as a byte offset (wave-uniform).
+__device__ __forceinline__ void dma16_at(const void *src, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void *src, void *lds_dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_offset(lds_dst));
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -92,6 +101,27 @@ __device__ __forceinline__ float max_lane_pair(float v) {
   float a = v, b = v;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
+}
+
+// Masks the scores of a 32-row tile held in the MFMA accumulator layout
+// (lane l holds rows 8*(q/4) + 4*(l/32) + q%4, q = 0..15, of column l%32):
+// a row whose bit in the wave-uniform mask tm is clear gets -inf.  The lane
+// mask of each score (two bits of tm: one for lanes 0-31, one for 32-63) is
+// formed in scalar registers and applied with one v_cndmask; a full mask
+// costs nothing.
+__device__ __forceinline__ void mask_tile_rows(float (&sc)[16], uint32_t tm) {
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  if (tm == 0xFFFFFFFFu) return;
+  const float ninf = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int r0 = 8 * (q >> 2) + (q & 3);
+    const uint64_t m = (((tm >> r0) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
+                       (((tm >> (r0 + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(ninf), "v"(sc[q]), "s"(m));
+    sc[q] = r;
+  }
 }
 
 __device__ __forceinline__ uint32_t pack_bf16_hi(float lo, float hi) {

@@ -24,7 +24,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_kernel_names_follow_the_selection():
     pre = synth.make_workload("prefill_csa")
-    assert bench.attention_kernel(pre, 1, 0, 0) == "attn_pair_kernel<2, false, false>"
+    assert bench.attention_kernel(pre, 1, 0, 0) == "attn_pair_kernel<3>"
     assert bench.attention_kernel(pre, 1, 0, 1) == "attn_fwd_kernel"
     dec = synth.make_workload("decode_csa", batch=2)
     assert bench.attention_kernel(dec, 4, 0, 0) == "attn_decode_kernel<false>"
