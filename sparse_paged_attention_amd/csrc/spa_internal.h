@@ -40,6 +40,7 @@ struct Params {
   int32_t cmp_fp8;                    // e4m3 compressed pages
   int32_t cmp_fnuz;                   // ... in the FNUZ variant (decode slices only)
   float scale_log2;                   // scale * log2(e)
+  int32_t num_cus;                    // compute units of the device (prefill pairs' item order)
 };
 
 hipError_t launch_attention(const Params &p, hipStream_t stream);

@@ -116,8 +116,10 @@ __device__ __forceinline__ void mask_tile_rows(float (&sc)[16], uint32_t tm) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int r0 = 8 * (q >> 2) + (q & 3);
-    const uint64_t m = (((tm >> r0) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
-                       (((tm >> (r0 + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
+    // all ones where the row bit is set: bit r0 (lanes 0-31), bit r0+4 (32-63)
+    const uint32_t lo = (uint32_t)((int32_t)(tm << (31 - r0)) >> 31);
+    const uint32_t hi = (uint32_t)((int32_t)(tm << (27 - r0)) >> 31);
+    const uint64_t m = (uint64_t)lo | ((uint64_t)hi << 32);
     float r;
     asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(ninf), "v"(sc[q]), "s"(m));
     sc[q] = r;

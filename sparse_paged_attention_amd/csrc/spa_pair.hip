@@ -57,6 +57,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -123,7 +124,14 @@ void attn_pair_kernel(const Params p) {
     const int32_t hblocks = (p.group + 63) / 64;
     const int32_t per_pair = p.hkv * hblocks;
     const int32_t npairs = (p.num_queries + 1) / 2;
-    const int32_t pr = npairs - 1 - (int32_t)(blockIdx.x / per_pair);
+    // the first 2C items (C compute units, two resident workgroups each)
+    // put the C longest with the C shortest, so that the two workgroups of
+    // a CU finish at different times and the setups of later items overlap
+    // the tile loops of others; the rest follow longest first
+    const int32_t w = (int32_t)(blockIdx.x / per_pair);
+    const int32_t C = p.num_cus;
+    int32_t pr = npairs - 1 - w;
+    if (C > 0 && npairs >= 2 * C) pr = w < C ? npairs - 1 - w : w < 2 * C ? w - C : npairs - 1 - (w - C);
     const int32_t rem = (int32_t)(blockIdx.x % per_pair);
     g = rem / hblocks;
     hb = rem - g * hblocks;
@@ -520,8 +528,24 @@ void attn_pair_kernel(const Params p) {
   }
 
   // ---- one step of the tile loop (tile j in stage ST, a compile-time
-  // constant, so that every LDS address is a register plus an immediate);
-  // lane rows of S^T: 8*(i/4) + 4*hi + i%4
+  // constant, so that every LDS address is a register plus an immediate).
+  // Step j runs three independent pieces together: the scores of tile j+1
+  // and O^T += V^T.P^T of tile j-1 on the matrix cores, the softmax of tile
+  // j on the vector ALUs; it ends by reading V of tile j for the next step.
+  // Lane rows of S^T: 8*(i/4) + 4*hi + i%4.
+  i16x8 vprev[kD / 32][2];                  // V^T fragments of the previous tile
+  bf16x8 pprev[2];                          // its P (bf16), relative to its m
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db) vprev[db][0] = vprev[db][1] = i16x8{};
+  pprev[0] = pprev[1] = bf16x8{};
+  auto pv_prev = [&]() {
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vprev[db][k2]), pprev[k2], acc[db],
+                                                          0, 0, 0);
+  };
   auto step = [&](const int j, auto stage) {
     constexpr int ST = decltype(stage)::value;
     const bool more = j + 1 < ntiles;
@@ -551,18 +575,6 @@ void attn_pair_kernel(const Params p) {
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) asm volatile("" : "+v"(voff[db][rr]));
     read_k(std::integral_constant<int, (ST + 1) % NST>{}, kf);
-    // the V^T fragments of tile j (MFMA A operand through the transpose read)
-    i16x4 vf[kD / 32][2][2];
-#pragma unroll
-    for (int db = 0; db < kD / 32; ++db)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-          vf[db][k2][rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4_t *)(uintptr_t)(voff[db][rr] + ST * kPTileB + 16 * k2 * kRowB));
-    // the scores of tile j+1 on the matrix cores, the softmax of tile j on
-    // the vector ALUs
     float sc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = s[i];
@@ -570,6 +582,7 @@ void attn_pair_kernel(const Params p) {
     f32x16 sn = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < kD / 16; ++kk) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sn, 0, 0, 0);
+    pv_prev();
     float smax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     smax = fmaxf(smax, fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])),
                              fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]))));
@@ -586,31 +599,36 @@ void attn_pair_kernel(const Params p) {
     float psum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
     psum += ((pr[8] + pr[9]) + (pr[10] + pr[11])) + ((pr[12] + pr[13]) + (pr[14] + pr[15]));
     l = l * alpha + psum;
-    bf16x8 pb[2];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) pb[k2][jj] = (__bf16)pr[8 * k2 + jj];
+      for (int jj = 0; jj < 8; ++jj) pprev[k2][jj] = (__bf16)pr[8 * k2 + jj];
     // P is complete here (not sunk past the rescale branch), and the region
     // issues one MFMA, then a share of the softmax's vector instructions, in
     // turn
-    asm volatile("" ::"v"(pb[0]), "v"(pb[1]));
+    asm volatile("" ::"v"(pprev[0]), "v"(pprev[1]));
 #pragma unroll
-    for (int kk = 0; kk < kD / 16; ++kk) {
+    for (int kk = 0; kk < kD / 8; ++kk) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
+    // O (with tile j-1's PV in) to this tile's m, before tile j's PV
     if (rescale) {
 #pragma unroll
       for (int db = 0; db < kD / 32; ++db) acc[db] *= alpha;
     }
+    // the V^T fragments of tile j (MFMA A operand through the transpose
+    // read), for the next step
 #pragma unroll
     for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const i16x8 cat = {vf[db][k2][0][0], vf[db][k2][0][1], vf[db][k2][0][2], vf[db][k2][0][3],
-                           vf[db][k2][1][0], vf[db][k2][1][1], vf[db][k2][1][2], vf[db][k2][1][3]};
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pb[k2], acc[db], 0, 0, 0);
+        i16x4 h[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+          h[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t *)(uintptr_t)(voff[db][rr] + ST * kPTileB + 16 * k2 * kRowB));
+        vprev[db][k2] = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
       }
     s = sn;
     tm = tm_next;
@@ -623,6 +641,7 @@ void attn_pair_kernel(const Params p) {
   }
   if (j < ntiles) step(j, std::integral_constant<int, 0>{});
   if (j + 1 < ntiles) step(j + 1, std::integral_constant<int, 1>{});
+  pv_prev();                                 // the last tile's PV
 
   // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) ln 2; a query
   // that failed its checks has no rows and writes O = 0 and LSE = sink
@@ -655,13 +674,30 @@ bool prefill_pairs_eligible(const Params &p) {
          2 * ((int64_t)p.topk + p.window) <= kUMax;
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+static int32_t device_cus() {
+  static std::atomic<int32_t> cache[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int32_t n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    n = v;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream) {
   if (p.num_queries == 0) return hipSuccess;
   if (!prefill_pairs_eligible(p)) return hipErrorInvalidConfiguration;
   const int64_t npairs = (p.num_queries + 1) / 2;
   const int64_t grid = npairs * p.hkv * ((p.group + 63) / 64);
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_pair_kernel<kPairStages>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  Params q = p;
+  q.num_cus = (p.hkv * ((p.group + 63) / 64) == 1) ? device_cus() : 0;   // one item per pair
+  hipLaunchKernelGGL((attn_pair_kernel<kPairStages>), dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 
