@@ -179,6 +179,8 @@ def parse_args(argv=None):
                     choices=["decode_csa", "decode_hca", "mixed_fp8", "prefill_csa", "tiny", "decode_latent",
                              "topk_decode", "topk_prefill", "bwd_prefill_csa"])
     ap.add_argument("--batch", type=int, default=0, help="decode batch override (0 = the workload's)")
+    ap.add_argument("--context", type=int, default=0,
+                    help="decode sequence length for every query (0 = the workload's); a sweep of the KV-set size")
     ap.add_argument("--splits", type=int, default=0, help="0 = the default for the workload")
     ap.add_argument("--heads-per-block", type=int, default=-1,
                     help="query heads per workgroup (32/64/128, 0 = library choice, -1 = workload default)")
@@ -261,7 +263,7 @@ def graph_replay_ms(launch, steps, reps=1, rounds=2):
 
 
 def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries_per_block=-1,
-        rotate_mb=640.0, batch=0, cpu_budget=0.0, problem=None, eager_only=False):
+        rotate_mb=640.0, batch=0, cpu_budget=0.0, problem=None, eager_only=False, context=0):
     """Time `steps` calls of the hot path; returns the result dict."""
     import ctypes
 
@@ -271,7 +273,7 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
 
     lib = _lib.load()
     dev = torch.device("cuda:0")
-    p = problem if problem is not None else synth.make_workload(workload, batch=batch or None)
+    p = problem if problem is not None else synth.make_workload(workload, batch=batch or None, context=context or None)
     d_splits, d_hpb, d_qpb = DEFAULTS.get(workload, (1, 0, 0))
     splits = splits or d_splits
     hpb = d_hpb if heads_per_block < 0 else heads_per_block
@@ -407,7 +409,8 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
                    "page_size": p.page_size, "window": p.window, "ratio": p.ratio, "topk": p.topk,
                    "kv_entries": kv_entries, "num_splits": splits, "heads_per_block": hpb,
                    "queries_per_block": qpb,
-                   "replicas": reps, "rotated_mb": round(reps * alg_bytes / 1e6, 1), "graphs": n_graphs},
+                   "replicas": reps, "rotated_mb": round(reps * alg_bytes / 1e6, 1), "graphs": n_graphs}
+                  | ({"context": context} if context else {}),
         "roofline": roof,
         "cpu_baseline": cpu_baseline(p, cpu_budget) if cpu_budget > 0 else None,
         "timing": {"graph_replay_ms_per_step_min": float(per.min()),
@@ -421,7 +424,7 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
                    "tflops": alg_flops / (ms_per_step / 1e3) / 1e12,
                    "gbs_step": alg_bytes / (ms_per_step / 1e3) / 1e9},
     }
-    out["roofline"]["traffic"] = measured_traffic(workload, out["config"])
+    out["roofline"]["traffic"] = None if context else measured_traffic(workload, out["config"])
     return out
 
 
@@ -616,7 +619,7 @@ def main():
         return
     out = run(args.workload, steps=args.steps, warmup=args.warmup, splits=args.splits,
               heads_per_block=args.heads_per_block, queries_per_block=args.queries_per_block, rotate_mb=args.rotate_mb, batch=args.batch,
-              cpu_budget=args.cpu_budget, eager_only=args.eager_only)
+              cpu_budget=args.cpu_budget, eager_only=args.eager_only, context=args.context)
     print(json.dumps(out), flush=True)
 
 

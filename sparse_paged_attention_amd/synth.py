@@ -357,17 +357,21 @@ def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head
 WORKLOADS = ("tiny", "decode_csa", "prefill_csa", "decode_hca", "mixed_fp8", "decode_latent")
 
 
-def make_workload(name: str, *, batch: Optional[int] = None, keep_logical: bool = False) -> Problem:
+def make_workload(name: str, *, batch: Optional[int] = None, keep_logical: bool = False,
+                  context: Optional[int] = None) -> Problem:
     """The named workloads (the five measured configurations and the 512-wide
     shared-latent decode).  ``batch`` overrides the decode batch size
-    (one GPU's share of a larger batch, or a bounded CPU sample)."""
+    (one GPU's share of a larger batch, or a bounded CPU sample); ``context``
+    gives every decode sequence that length (for sweeps of the KV-set size)."""
+    if context is not None and name in ("tiny", "prefill_csa"):
+        raise ValueError("context applies to the decode workloads")
     if name == "tiny":
         return make_problem("tiny", "prefill", [64], 4, 1, 64, 16, 16, 4, 8, seed=0,
                             query_positions=[(0, p) for p in range(48, 64)],
                             selection="random", keep_logical=True)
     if name == "decode_csa":
         b = batch or 32
-        return make_problem("decode_csa", "decode", [4096] * b, 128, 1, 128, 64, 128, 4, 512,
+        return make_problem("decode_csa", "decode", [context or 4096] * b, 128, 1, 128, 64, 128, 4, 512,
                             seed=1, selection="random", keep_logical=keep_logical)
     if name == "prefill_csa":
         return make_problem("prefill_csa", "prefill", [2560], 64, 1, 128, 16, 128, 4, 512,
@@ -375,18 +379,20 @@ def make_workload(name: str, *, batch: Optional[int] = None, keep_logical: bool 
                             selection="score", keep_logical=keep_logical)
     if name == "decode_hca":
         b = batch or 4
-        return make_problem("decode_hca", "decode", [32768] * b, 128, 1, 128, 128, 128, 128, 0,
+        return make_problem("decode_hca", "decode", [context or 32768] * b, 128, 1, 128, 128, 128, 128, 0,
                             seed=3, num_splits=4, keep_logical=keep_logical)
     if name == "mixed_fp8":
         b = batch or 16
         rng = np.random.Generator(np.random.PCG64(4))
         lens = rng.integers(1024, 16384, size=b, endpoint=True).astype(np.int32)
+        if context is not None:
+            lens[:] = context
         return make_problem("mixed_fp8", "decode", lens, 128, 1, 128, 64, 128, 4, 512,
                             seed=4, cmp_fp8=True, selection="random", keep_logical=keep_logical)
     if name == "decode_latent":
         # the 512-wide shared latent cache (K = V) in 256-token pages, with
         # the CSA layer's window and top-k of decode_csa and 64 query heads
         b = batch or 32
-        return make_problem("decode_latent", "decode", [4096] * b, 64, 1, 512, 256, 128, 4, 512,
+        return make_problem("decode_latent", "decode", [context or 4096] * b, 64, 1, 512, 256, 128, 4, 512,
                             seed=5, selection="random", num_splits=8, shared_kv=True, keep_logical=keep_logical)
     raise ValueError(f"unknown workload {name!r}")
