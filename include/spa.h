@@ -80,10 +80,10 @@ typedef enum spa_dtype {
   SPA_FP8_E4M3_FNUZ = 2     /* FNUZ e4m3 (the gfx942 format, named beside OCP in
                                the RL-Kernel joint attention PR, "Reuse and
                                arithmetic"): bias 8, no inf, no -0, 0x80 NaN,
-                               max 240.  Compressed pages only, read by the
-                               decode kernel (decode, head_dim 128,
-                               heads_per_block = queries_per_block = 0);
-                               SPA_ERR_UNSUPPORTED elsewhere               */
+                               max 240.  Compressed pages only, wherever
+                               e4m3 pages are taken (head_dim 64 or 128,
+                               forward); SPA_ERR_UNSUPPORTED at head_dim
+                               512 and in the backward, as for OCP         */
 } spa_dtype;
 
 #define SPA_MAX_SPLITS 64

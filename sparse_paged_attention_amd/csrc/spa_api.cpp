@@ -234,9 +234,6 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream, void *s
   // the call fits it and the caller leaves both block sizes to the library.
   const bool dec = decode && a->heads_per_block == 0 && a->queries_per_block == 0 && spa::decode_eligible(p);
   const bool latent = a->head_dim == 512;
-  if (p.cmp_fnuz && !dec)
-    return fail(SPA_ERR_UNSUPPORTED, "FNUZ e4m3 pages are read by the decode kernel only: decode, head_dim 128, "
-                "heads_per_block and queries_per_block 0, and slices within %d rows", spa::kDecodeRowsMax);
   hipError_t e = latent  ? spa::launch_latent(p, s)
                  : pairs ? spa::launch_prefill_pairs(p, s)
                  : dec   ? spa::launch_decode(p, s)

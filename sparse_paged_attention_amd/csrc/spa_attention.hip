@@ -730,22 +730,16 @@ void attn_fwd_kernel(const Params p) {
     }
   };
 
-  // FP8: widen a staged e4m3 tile to bf16 (exact) into its swizzled slot
+  // FP8: widen a staged e4m3 tile (OCP, or FNUZ) to bf16 (exact) into its
+  // swizzled slot
+  const bool fnuz = FP8 && p.cmp_fnuz != 0;
   auto widen = [&](const uint8_t *src, uint8_t *dst) {
     constexpr int kPieces = kTile * D / 8;   // 8-byte pieces per tile
     for (int idx = hw * 64 + lane; idx < kPieces; idx += C::kThreads) {
       const int r = idx / (D / 8);
       const int piece = idx - r * (D / 8);
       const uint2 w = *(const uint2 *)(src + r * D + piece * 8);
-      const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-      const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-      const f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-      const f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-      uint4 o;
-      o.x = pack_bf16_hi(a0[0], a0[1]);
-      o.y = pack_bf16_hi(a1[0], a1[1]);
-      o.z = pack_bf16_hi(a2[0], a2[1]);
-      o.w = pack_bf16_hi(a3[0], a3[1]);
+      const uint4 o = widen8_e4m3(w, fnuz);
       *(uint4 *)(dst + r * C::kRowB + ((piece ^ swz<C::kChunks>(r)) * 16)) = o;
     }
   };

@@ -429,29 +429,7 @@ void attn_decode_kernel(const Params p) {
         const int piece = rem % (kD / 8);
         const int st = jj % NST;
         const uint2 w = *(const uint2 *)(sm.f8[FP8 ? st : 0] + side * kF8TileB + r * kD + piece * 8);
-        f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-        f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-        f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-        f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-        if (fnuz) {
-          // FNUZ code c is OCP code c halved (bias 8 against 7), except
-          // 0x7F / 0xFF (+-240; OCP NaN) and 0x80 (NaN; OCP -0)
-          auto fix = [](float x, uint32_t word, int byte) {
-            const uint32_t c = (word >> (8 * byte)) & 0xFFu;
-            return (c & 0x7Fu) == 0x7Fu ? ((c & 0x80u) ? -240.f : 240.f)
-                   : c == 0x80u          ? __builtin_bit_cast(float, 0x7FC00000u)
-                                         : 0.5f * x;
-          };
-          a0 = f32x2{fix(a0[0], w.x, 0), fix(a0[1], w.x, 1)};
-          a1 = f32x2{fix(a1[0], w.x, 2), fix(a1[1], w.x, 3)};
-          a2 = f32x2{fix(a2[0], w.y, 0), fix(a2[1], w.y, 1)};
-          a3 = f32x2{fix(a3[0], w.y, 2), fix(a3[1], w.y, 3)};
-        }
-        uint4 o;
-        o.x = pack_bf16_hi(a0[0], a0[1]);
-        o.y = pack_bf16_hi(a1[0], a1[1]);
-        o.z = pack_bf16_hi(a2[0], a2[1]);
-        o.w = pack_bf16_hi(a3[0], a3[1]);
+        const uint4 o = widen8_e4m3(w, fnuz);
         uint8_t *dst = side ? sm.v[st] : sm.k[st];
         *(uint4 *)(dst + r * kRowB + ((piece ^ swz<kChunks>(r)) * 16)) = o;
       }

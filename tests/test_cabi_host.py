@@ -105,10 +105,6 @@ FAULTS = [
     ("heads_per_block_128", lambda a: (setattr(a, "num_q_heads", 128), setattr(a, "heads_per_block", 128)), -4),
     ("d512_separate_kv", lambda a: setattr(a, "head_dim", 512), -4),
     ("fnuz_without_scales", lambda a: setattr(a, "cmp_dtype", _lib.SPA_FP8_E4M3_FNUZ), -1),
-    ("fnuz_off_the_slice_kernel", lambda a: (setattr(a, "cmp_dtype", _lib.SPA_FP8_E4M3_FNUZ),
-                                             setattr(a, "k_cmp_scale", 0x30000000),
-                                             setattr(a, "v_cmp_scale", 0x30001000),
-                                             setattr(a, "heads_per_block", 64)), -4),
     ("d512_fp8", lambda a: (setattr(a, "head_dim", 512), setattr(a, "v_raw", a.k_raw), setattr(a, "v_cmp", a.k_cmp),
                             setattr(a, "cmp_dtype", _lib.SPA_FP8_E4M3_OCP), setattr(a, "k_cmp_scale", 0x30000000),
                             setattr(a, "v_cmp_scale", 0x30001000)), -4),

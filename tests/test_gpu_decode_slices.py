@@ -104,14 +104,20 @@ def test_fnuz_pages_slices(splits):
     check_against_oracle(p, splits, label=f"fnuz S={splits}")
 
 
-def test_fnuz_pages_refused_outside_the_slice_kernel():
-    from sparse_paged_attention_amd import api, _lib
-    p = synth.make_problem("fnuz_pre", "prefill", [600], 64, 1, 128, 16, 128, 4, 64, seed=45, cmp_fp8=True,
-                           fp8_format="fnuz", query_positions=[(0, t) for t in range(590, 598)])
-    dp = api.DeviceProblem.from_problem(p)
-    with pytest.raises(_lib.SpaError) as e:
-        api.forward(dp, 1)
-    assert e.value.status == -4
+def test_fnuz_pages_job_streams():
+    """FNUZ e4m3 compressed pages through the job-stream kernel: a prefill
+    (the pair kernel takes bf16 caches only, so the call runs on job streams)
+    and a decode with 64 query heads per job, both against the oracle."""
+    p = synth.make_problem("fnuz_pre", "prefill", [600, 300], 64, 1, 128, 16, 128, 4, 64, seed=45, cmp_fp8=True,
+                           fp8_format="fnuz", query_positions=[(0, t) for t in range(560, 598)] + [(1, 299), (1, 5)],
+                           selection="random")
+    assert np.any(p.k_cmp == 0x7F) or np.any(p.k_cmp == 0xFF)
+    check_against_oracle(p, label="fnuz prefill job streams")
+    check_against_oracle(p, queries_per_block=1, label="fnuz prefill one query per job")
+    d = synth.make_problem("fnuz_dec", "decode", [3000, 700, 129], 128, 1, 128, 64, 128, 4, 512, seed=46,
+                           cmp_fp8=True, fp8_format="fnuz", selection="random")
+    for s in (1, 4):
+        check_against_oracle(d, num_splits=s, heads_per_block=64, label=f"fnuz decode job streams S{s}")
 
 
 def test_fnuz_every_code():
