@@ -81,9 +81,9 @@ typedef enum spa_dtype {
                                the RL-Kernel joint attention PR, "Reuse and
                                arithmetic"): bias 8, no inf, no -0, 0x80 NaN,
                                max 240.  Compressed pages only, wherever
-                               e4m3 pages are taken (head_dim 64 or 128,
-                               forward); SPA_ERR_UNSUPPORTED at head_dim
-                               512 and in the backward, as for OCP         */
+                               e4m3 pages are taken (the forward at every
+                               head_dim); SPA_ERR_UNSUPPORTED in the
+                               backward, as for OCP                        */
 } spa_dtype;
 
 #define SPA_MAX_SPLITS 64
@@ -98,9 +98,11 @@ typedef struct spa_fwd_args {
                               "Roadmap item 24", review of the joint-attention
                               contract and the packed-page gather: one bf16
                               `_kv` buffer is K and V, heads 512 wide): it
-                              needs v_raw == k_raw, v_cmp == k_cmp, bf16
-                              caches and heads_per_block = queries_per_block
-                              = 0 (SPA_ERR_UNSUPPORTED otherwise)            */
+                              needs v_raw == k_raw, v_cmp == k_cmp, with e4m3
+                              compressed pages also v_cmp_scale ==
+                              k_cmp_scale (one scale per latent row), and
+                              heads_per_block = queries_per_block = 0
+                              (SPA_ERR_UNSUPPORTED otherwise)                */
   int32_t page_size;      /* P >= 1 tokens (rows) per page, same for both caches */
   int32_t window;         /* W >= 0 raw tokens ending at the query token         */
   int32_t ratio;          /* r >= 0 tokens per compressed group; 0 = no groups   */

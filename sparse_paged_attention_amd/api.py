@@ -76,6 +76,7 @@ class DeviceProblem:
         # one device buffer, so the library sees K == V
         k_raw = bits16(p.k_raw)
         k_cmp = (dev(p.k_cmp) if p.cmp_fp8 else bits16(p.k_cmp)) if has_cmp else None
+        k_scale = dev(p.k_cmp_scale) if (has_cmp and p.cmp_fp8) else None
         return cls(
             mode=p.mode, num_seqs=p.num_seqs, num_queries=p.num_queries,
             num_q_heads=p.num_q_heads, num_kv_heads=p.num_kv_heads, head_dim=p.head_dim,
@@ -85,8 +86,9 @@ class DeviceProblem:
             k_cmp=k_cmp,
             v_cmp=(k_cmp if p.v_cmp is p.k_cmp else (dev(p.v_cmp) if p.cmp_fp8 else bits16(p.v_cmp))) if has_cmp
             else None,
-            k_cmp_scale=dev(p.k_cmp_scale) if (has_cmp and p.cmp_fp8) else None,
-            v_cmp_scale=dev(p.v_cmp_scale) if (has_cmp and p.cmp_fp8) else None,
+            k_cmp_scale=k_scale,
+            v_cmp_scale=(k_scale if p.v_cmp_scale is p.k_cmp_scale else dev(p.v_cmp_scale))
+            if (has_cmp and p.cmp_fp8) else None,
             raw_pt=dev(p.raw_pt), cmp_pt=dev(p.cmp_pt) if has_cmp else None,
             seq_lens=dev(p.seq_lens),
             query_seq=dev(p.query_seq) if p.mode == "prefill" else None,

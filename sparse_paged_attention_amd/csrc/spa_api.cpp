@@ -67,8 +67,9 @@ spa_status validate(const spa_fwd_args *a, bool decode, bool need_outputs) {
     // the 512-wide path is the shared latent cache: one row is K and V
     if (a->k_raw != a->v_raw || (a->ratio > 0 && a->k_cmp != a->v_cmp))
       return fail(SPA_ERR_UNSUPPORTED, "head_dim 512 needs a shared latent cache (k_raw == v_raw, k_cmp == v_cmp)");
-    if (a->ratio > 0 && a->cmp_dtype != SPA_BF16)
-      return fail(SPA_ERR_UNSUPPORTED, "head_dim 512 takes bf16 caches");
+    if (a->ratio > 0 && a->cmp_dtype != SPA_BF16 && a->k_cmp_scale != a->v_cmp_scale)
+      return fail(SPA_ERR_UNSUPPORTED, "head_dim 512 with e4m3 pages needs one shared scale array "
+                  "(k_cmp_scale == v_cmp_scale)");
     if (a->heads_per_block != 0 || a->queries_per_block != 0)
       return fail(SPA_ERR_UNSUPPORTED, "head_dim 512 takes heads_per_block 0 and queries_per_block 0");
   }

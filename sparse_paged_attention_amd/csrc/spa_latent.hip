@@ -29,6 +29,16 @@
 // 128-wide row, so the fragment reads have the 128-wide path's conflict
 // behaviour.  With several slices the workgroup writes a sink-free partial
 // (O_s in fp32, LSE_s) for the LSE merge.
+//
+// FP8: the compressed pool may hold e4m3 codes (OCP or FNUZ) with one fp32
+// scale per latent row, shared by its key and value roles.  A slice then
+// takes its compressed entries and its window entries as separate chunks,
+// so every tile is all e4m3 or all bf16.  An e4m3 tile's 512-byte rows (two
+// per 1 KiB direct load) land in the upper half of the tile's stage with
+// their scales; after the tile's barrier every thread reads its codes, and
+// after a second barrier widens them exactly to bf16 over the whole stage.
+// The scale multiplies the summed fp32 scores and p before its bf16
+// rounding, as on the 128-wide path.
 
 #include <hip/hip_runtime.h>
 
@@ -50,8 +60,10 @@ constexpr int kLRows = 512;                // rows translated per chunk (one per
 constexpr int kLStages = 3;               // two tiles in flight while one is computed
 constexpr int64_t kCmpBit = int64_t(1) << 62;
 
+template <bool FP8>
 struct LatentSmem {
   alignas(16) uint8_t kv[kLStages][kTileB];
+  alignas(16) float f8s[FP8 ? kLStages : 1][64];   // e4m3 tiles: row scales (32 used)
   alignas(16) float4 xs[2][4][4][64];      // partial S^T: [head group][quarter][float4][lane]
   alignas(16) float4 xf[2][4][64];         // summed S^T: [head group][float4][lane]
   alignas(16) int64_t row[kLRows];         // row * Hkv + g (bit 62: compressed), -1: masked
@@ -62,8 +74,9 @@ __device__ __forceinline__ int chunk_off(int r, int c) {
   return r * kRowB + (c >> 4) * kQB + (((c & 15) ^ swz<16>(r)) * 16);
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
-  __shared__ LatentSmem sm;
+  __shared__ LatentSmem<FP8> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -103,6 +116,9 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
   for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
 
   const uint8_t *const kraw = in_sgpr(p.k_raw), *const kcmp = in_sgpr(p.k_cmp);
+  const float *const kscale = in_sgpr(p.k_cmp_scale);
+  const bool fnuz = FP8 && p.cmp_fnuz != 0;
+  constexpr int kF8Off = kTileB / 2;         // e4m3 codes staged in the upper half of a stage
   // tile loads: wave w moves rows 4w .. 4w+3, one 1 KiB load per row; lane
   // L's chunk is logical chunk 16 (L / 16) + ((L % 16) ^ swz(row))
   auto issue = [&](int j) {
@@ -118,8 +134,27 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
     }
   };
 
-  for (int32_t c0 = e_lo; c0 < e_hi; c0 += kLRows) {
-    const int32_t n = min(kLRows, e_hi - c0);
+  // an e4m3 tile: wave w moves rows 4w .. 4w+3, two 512-byte rows per
+  // 1 KiB load (lane L: row 4w + 2n + L / 32, bytes 16 (L % 32) ..); wave 0
+  // also loads the 32 scales
+  auto issue_f8 = [&](int j) {
+    const int st = j % kLStages;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int r = 4 * wave + 2 * n + (lane >> 5);
+      const int64_t er = sm.row[kPT * j + r];
+      dma16(er >= 0 ? kcmp + (er & ~kCmpBit) * kD + (lane & 31) * 16 : kZeroRow + (lane & 15) * 16,
+            sm.kv[st] + kF8Off + (4 * wave + 2 * n) * kD);
+    }
+    if (wave == 0) {
+      const int64_t er = lane < kPT ? sm.row[kPT * j + lane] : -1;
+      dma4(er >= 0 ? (const void *)(kscale + (er & ~kCmpBit)) : (const void *)(kZeroRow + 4 * lane),
+           sm.f8s[FP8 ? st : 0]);
+    }
+  };
+
+  // one chunk: canonical entries c0 .. c0+n-1, all compressed when f8c
+  auto run_chunk = [&](const int32_t c0, const int32_t n, const bool f8c) {
     const int32_t ntiles = (n + kPT - 1) / kPT;
     {
       const int32_t e = c0 + tid;
@@ -132,16 +167,47 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
       if (tid < ntiles * kPT) sm.row[tid] = er;
     }
     __syncthreads();
-    issue(0);
-    if (ntiles > 1) issue(1);
+    auto issue_tile = [&](int j) {
+      if (FP8 && f8c) issue_f8(j);
+      else issue(j);
+    };
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
     for (int j = 0; j < ntiles; ++j) {
-      // this wave's loads of tile j are complete (tile j+1's four may still
-      // be in flight), then everyone's; every wave is done with tile j-1,
-      // whose stage tile j+2 refills
-      if (j + 1 < ntiles) wait_vmcnt<4>();
-      else wait_vmcnt<0>();
+      // this wave's loads of tile j are complete (tile j+1's may still be in
+      // flight: four loads, or two and wave 0's scales for an e4m3 tile),
+      // then everyone's; every wave is done with tile j-1, whose stage tile
+      // j+2 refills
+      if (j + 1 < ntiles) {
+        if (FP8 && f8c) {
+          if (wave == 0) wait_vmcnt<3>();
+          else wait_vmcnt<2>();
+        } else {
+          wait_vmcnt<4>();
+        }
+      } else {
+        wait_vmcnt<0>();
+      }
       block_sync();
-      if (j + 2 < ntiles) issue(j + 2);
+      if (FP8 && f8c) {
+        // widen the staged codes over the whole stage: every thread reads
+        // its four 8-code pieces before any bf16 write lands on them
+        uint8_t *W = sm.kv[j % kLStages];
+        uint2 cw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int idx = tid + kLThreads * k;   // row idx / 64, piece idx % 64
+          cw[k] = *(const uint2 *)(W + kF8Off + (idx >> 6) * kD + (idx & 63) * 8);
+        }
+        block_sync();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int idx = tid + kLThreads * k;
+          *(uint4 *)(W + chunk_off(idx >> 6, idx & 63)) = widen8_e4m3(cw[k], fnuz);
+        }
+        block_sync();                        // the widened tile is in
+      }
+      if (j + 2 < ntiles) issue_tile(j + 2);
       const uint8_t *T = sm.kv[j % kLStages];
       const uint32_t tm = (uint32_t)__ballot(lane < 32 && sm.row[kPT * j + (lane & 31)] >= 0);
       // partial scores over this wave's 128 dimensions
@@ -202,6 +268,17 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
         sc[4 * c + 2] = t.z;
         sc[4 * c + 3] = t.w;
       }
+      // the row scale multiplies the summed scores of an e4m3 tile
+      if (FP8 && f8c) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 k4 = *(const float4 *)(&sm.f8s[FP8 ? j % kLStages : 0][8 * q4 + 4 * hi]);
+          sc[4 * q4 + 0] *= k4.x;
+          sc[4 * q4 + 1] *= k4.y;
+          sc[4 * q4 + 2] *= k4.z;
+          sc[4 * q4 + 3] *= k4.w;
+        }
+      }
       // online softmax; lane rows of S^T: 8 (r / 4) + 4 hi + r % 4
       const uint32_t tmh = tm >> (4 * hi);
 #pragma unroll
@@ -226,7 +303,9 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
       for (int r = 0; r < 16; ++r) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], p.scale_log2, negm));
         psum += pr;
-        pb[r >> 3][r & 7] = (__bf16)pr;
+        // an e4m3 tile: the row scale multiplies p before its bf16 rounding
+        const float pv = (FP8 && f8c) ? pr * sm.f8s[FP8 ? j % kLStages : 0][8 * (r >> 2) + 4 * hi + (r & 3)] : pr;
+        pb[r >> 3][r & 7] = (__bf16)pv;
       }
       l += psum;
 #pragma unroll
@@ -237,6 +316,13 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
     }
     wait_vmcnt<0>();
     __syncthreads();                         // the row list is rewritten by the next chunk
+  };
+  if (FP8) {
+    const int32_t c_hi = min(e_hi, kv.n_sel);
+    for (int32_t c0 = e_lo; c0 < c_hi; c0 += kLRows) run_chunk(c0, min(kLRows, c_hi - c0), true);
+    for (int32_t c0 = max(e_lo, kv.n_sel); c0 < e_hi; c0 += kLRows) run_chunk(c0, min(kLRows, e_hi - c0), false);
+  } else {
+    for (int32_t c0 = e_lo; c0 < e_hi; c0 += kLRows) run_chunk(c0, min(kLRows, e_hi - c0), false);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2; lane column = head,
@@ -275,12 +361,15 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
 }  // namespace
 
 hipError_t launch_latent(const Params &p, hipStream_t stream) {
-  if (p.head_dim != kD || p.cmp_fp8 || p.k_raw != p.v_raw || (p.ratio > 0 && p.k_cmp != p.v_cmp))
-    return hipErrorInvalidValue;
+  if (p.head_dim != kD || p.k_raw != p.v_raw || (p.ratio > 0 && p.k_cmp != p.v_cmp)) return hipErrorInvalidValue;
+  if (p.cmp_fp8 && p.k_cmp_scale != p.v_cmp_scale) return hipErrorInvalidValue;
   if (p.num_queries == 0) return hipSuccess;
   const int64_t grid = (int64_t)p.num_queries * p.hkv * ((p.group + 63) / 64) * p.num_splits;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(attn_latent_kernel, dim3((unsigned)grid), dim3(kLThreads), 0, stream, p);
+  if (p.cmp_fp8)
+    hipLaunchKernelGGL(attn_latent_kernel<true>, dim3((unsigned)grid), dim3(kLThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_latent_kernel<false>, dim3((unsigned)grid), dim3(kLThreads), 0, stream, p);
   return hipGetLastError();
 }
 

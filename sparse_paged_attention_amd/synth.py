@@ -235,13 +235,12 @@ def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head
     (top-k of a seeded random score, ties to the lower index), or "all"
     (list of every complete group in ascending order).
     ``shared_kv``: one latent cache per pool serves as K and V (the value
-    arrays are the key arrays, the same objects); bf16 only.
+    arrays are the key arrays, the same objects); with e4m3 compressed
+    pages the row scales are shared too (one scale per latent row).
     ``fp8_format``: "ocp" (max 448) or "fnuz" (max 240) for e4m3 pages.
     """
     fnuz = cmp_fp8 and fp8_format == "fnuz"
     qmax = np.float32(E4M3FNUZ_MAX if fnuz else E4M3_MAX)
-    if shared_kv and cmp_fp8:
-        raise ValueError("a shared latent cache is bf16")
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     B = len(seq_lens)
     Hq, Hkv, D, P = num_q_heads, num_kv_heads, head_dim, page_size
@@ -311,6 +310,8 @@ def make_problem(name: str, mode: str, seq_lens, num_q_heads, num_kv_heads, head
 
     if shared_kv:
         v_raw, v_log, v_cmp, vc_log = k_raw, k_log, k_cmp, kc_log
+        if cmp_fp8:
+            v_sc, vs_log = k_sc, ks_log
 
     # per-query compressed index lists
     cap = max(topk, 1)

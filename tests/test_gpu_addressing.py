@@ -9,7 +9,8 @@ does not change the result, so every kernel must still match the oracle run
 on the original problem, and the gather export must name the remapped rows.
 Each kernel path is covered: the decode kernel (bf16 and e4m3 pages, one and
 several slices), the job-stream kernel, the prefill query pairs and the
-one-query prefill, the 512-wide latent kernel, the backward and the gather."""
+one-query prefill, the 512-wide latent kernel (bf16 and e4m3 pages), the
+backward and the gather."""
 import dataclasses
 
 import numpy as np
@@ -81,7 +82,8 @@ def relocate(dp):
         out.v_cmp = out.k_cmp if dp.v_cmp is dp.k_cmp else _relocate_pool(dp.v_cmp, n_cmp, cmp_ids, fill)
         if dp.k_cmp_scale is not None:
             out.k_cmp_scale = _relocate_pool(dp.k_cmp_scale, n_cmp, cmp_ids, 0xFF)
-            out.v_cmp_scale = _relocate_pool(dp.v_cmp_scale, n_cmp, cmp_ids, 0xFF)
+            out.v_cmp_scale = (out.k_cmp_scale if dp.v_cmp_scale is dp.k_cmp_scale
+                               else _relocate_pool(dp.v_cmp_scale, n_cmp, cmp_ids, 0xFF))
         out.cmp_pt = _remap_pt(dp.cmp_pt, cmp_ids)
     return out, raw_ids, cmp_ids
 
@@ -133,6 +135,12 @@ def test_prefill_kernels_beyond_4gib(qpb):
 
 def test_latent_kernel_beyond_4gib():
     _forward_check(synth.make_workload("decode_latent", batch=2), "latent D512 S2", num_splits=2)
+
+
+def test_latent_e4m3_beyond_4gib():
+    p = synth.make_problem("lat_f8_far", "decode", [1300, 4096, 130], 64, 1, 512, 256, 128, 4, 200, seed=38,
+                           shared_kv=True, cmp_fp8=True)
+    _forward_check(p, "latent e4m3 D512 S2", num_splits=2)
 
 
 def test_gather_beyond_4gib():

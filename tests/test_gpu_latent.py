@@ -57,3 +57,22 @@ def test_latent_no_sink_and_empty_lists():
 def test_latent_full_workload():
     p = synth.make_workload("decode_latent")
     check_against_oracle(p, p.num_splits, label="decode_latent")
+
+
+@pytest.mark.parametrize("fmt,splits", [("ocp", 1), ("ocp", 4), ("fnuz", 1), ("fnuz", 3)])
+def test_latent_e4m3_pages(fmt, splits):
+    """e4m3 compressed latent pages (one code row and one fp32 scale per
+    token, shared by the key and value roles), OCP and FNUZ, decode with and
+    without slices: a slice's compressed entries and window entries run as
+    separate chunks of e4m3 and bf16 tiles."""
+    p = synth.make_problem("lat_f8", "decode", [700, 1300, 4096, 130, 2, 2100], 64, 1, 512, 256, 128, 4, 200,
+                           seed=36, shared_kv=True, cmp_fp8=True, fp8_format=fmt)
+    assert p.k_cmp is p.v_cmp and p.k_cmp_scale is p.v_cmp_scale
+    check_against_oracle(p, splits, label=f"latent e4m3 {fmt} S={splits}")
+
+
+def test_latent_e4m3_prefill():
+    pos = [(0, t) for t in (0, 3, 4, 127, 128, 600, 1000)] + [(1, 300)]
+    p = synth.make_problem("lat_f8_pre", "prefill", [1001, 301], 64, 1, 512, 256, 128, 4, 64, seed=37,
+                           query_positions=pos, selection="score", shared_kv=True, cmp_fp8=True)
+    check_against_oracle(p, 1, label="latent e4m3 prefill")
