@@ -34,7 +34,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the sources whose change invalidates counter-measured traffic
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
-                  for f in ("spa_attention.hip", "spa_pair.hip", "spa_decode.hip", "spa_latent.hip",
+                  for f in ("spa_attention.hip", "spa_pair.hip", "spa_decode.hip", "spa_decode_rows.hip", "spa_latent.hip",
                             "spa_kernel_util.h", "spa_device.h", "spa_internal.h", "spa_api.cpp")]
 # sources of the top-k and backward kernels (their traffic entries carry these hashes)
 TOPK_SOURCES = [os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f)
@@ -45,12 +45,12 @@ PAIR_ROWS_MAX = 1280           # rows a query pair's union can hold in the prefi
 DECODE_ROWS_MAX = 1280         # rows of one decode slice in the decode kernel
 
 
-def attention_kernel(p, splits, hpb, qpb):
+def attention_kernel(p, splits, hpb, qpb, cus=256):
     """Name of the attention kernel the library launches for this call: the
     prefill pair kernel when the call fits it and the library's choice (or
     the caller's) is query pairs, else the one-query-per-job kernel.  Mirrors
-    the selection in spa_api.cpp (the decode-slice kernel for a decode the
-    library sizes itself)."""
+    the selection in spa_api.cpp (for a decode the library sizes itself: the
+    one-pass kernel with one slice, the slice kernel with several)."""
     if p.head_dim == 512:
         return "attn_latent_kernel"
     pairs_ok = (p.mode == "prefill" and p.head_dim == 128 and not p.cmp_fp8 and splits == 1
@@ -65,6 +65,9 @@ def attention_kernel(p, splits, hpb, qpb):
                  and cper + -(-p.window // S) <= DECODE_ROWS_MAX)
     if pairs:
         return "attn_pair_kernel<3>"
+    rows_wgs = p.num_queries * p.num_kv_heads * -(-(p.num_q_heads // p.num_kv_heads) // 32)
+    if decode_ok and S == 1 and rows_wgs <= cus:
+        return "attn_decode_rows_kernel<true>" if p.cmp_fp8 else "attn_decode_rows_kernel<false>"
     if decode_ok:
         return "attn_decode_kernel<true>" if p.cmp_fp8 else "attn_decode_kernel<false>"
     return "attn_fwd_kernel"
@@ -198,7 +201,7 @@ def parse_args(argv=None):
 
 
 DEFAULTS = {   # (num_splits, heads_per_block, queries_per_block) per workload; 0 = library choice
-    "decode_csa": (4, 0, 0), "decode_hca": (4, 0, 0), "mixed_fp8": (8, 0, 0), "prefill_csa": (1, 0, 0),
+    "decode_csa": (1, 0, 0), "decode_hca": (1, 0, 0), "mixed_fp8": (8, 0, 0), "prefill_csa": (1, 0, 0),
     "tiny": (1, 0, 0), "decode_latent": (4, 0, 0),
 }
 
@@ -340,7 +343,7 @@ def run(workload, *, steps=200, warmup=20, splits=0, heads_per_block=-1, queries
         if st != 0:
             _lib.check(st)
 
-    kernel = attention_kernel(p, splits, hpb, qpb)
+    kernel = attention_kernel(p, splits, hpb, qpb, torch.cuda.get_device_properties(0).multi_processor_count)
     n_graphs = 1
     if eager_only:
         ms_per_step, per = eager_ms, np.array([eager_ms])

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["spa_api.cpp", "spa_attention.hip", "spa_pair.hip", "spa_decode.hip", "spa_merge.hip", "spa_gather.hip", "spa_topk.hip",
+SOURCES = ["spa_api.cpp", "spa_attention.hip", "spa_pair.hip", "spa_decode.hip", "spa_decode_rows.hip", "spa_merge.hip", "spa_gather.hip", "spa_topk.hip",
            "spa_backward.hip", "spa_latent.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for every HIP source file.
@@ -30,7 +30,8 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 # through the MFMAs and the exponentials into O.)
 SOURCE_FLAGS = {"spa_attention.hip": ["-fno-honor-nans"], "spa_pair.hip": ["-fno-honor-nans"],
                 "spa_decode.hip": ["-fno-honor-nans"],
-                "spa_latent.hip": ["-fno-honor-nans"]}
+                "spa_latent.hip": ["-fno-honor-nans"],
+                "spa_decode_rows.hip": ["-fno-honor-nans"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]
 

@@ -234,9 +234,16 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream, void *s
   // Decode: one workgroup per (query, KV head, 128-head block, slice), when
   // the call fits it and the caller leaves both block sizes to the library.
   const bool dec = decode && a->heads_per_block == 0 && a->queries_per_block == 0 && spa::decode_eligible(p);
+  // one slice: the waves of a workgroup split the query's rows (no partials),
+  // while its workgroups (one per query, KV head and 32 heads) fit on the
+  // chip at once; a larger batch keeps the 128-head workgroups
+  const int64_t rows_wgs = (int64_t)a->num_queries * a->num_kv_heads * ((p.group + 31) / 32);
+  const bool dec_rows = dec && a->num_splits == 1 && spa::decode_rows_eligible(p) &&
+                        rows_wgs <= spa::device_cu_count();
   const bool latent = a->head_dim == 512;
   hipError_t e = latent  ? spa::launch_latent(p, s)
                  : pairs ? spa::launch_prefill_pairs(p, s)
+                 : dec_rows ? spa::launch_decode_rows(p, s)
                  : dec   ? spa::launch_decode(p, s)
                          : spa::launch_attention(p, s);
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "attention launch failed: %s", hipGetErrorString(e));
@@ -281,6 +288,22 @@ void *scratch_on_current_device() {
 }
 
 }  // namespace
+
+namespace spa {
+int32_t device_cu_count() {
+  static std::atomic<int32_t> cache[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int32_t n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    n = v;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+}  // namespace spa
 
 extern "C" {
 

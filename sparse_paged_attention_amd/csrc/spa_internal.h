@@ -45,6 +45,9 @@ struct Params {
 
 hipError_t launch_attention(const Params &p, hipStream_t stream);
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int32_t device_cu_count();
+
 // Prefill with query pairs sharing KV tiles (spa_pair.hip): bf16 caches,
 // D 128, one slice, a top-k list (or no compressed part) and at most
 // kPairRowsMax rows in the union of a pair's KV sets, which holds whenever
@@ -62,6 +65,11 @@ hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream);
 constexpr int kDecodeRowsMax = 1280;
 bool decode_eligible(const Params &p);
 hipError_t launch_decode(const Params &p, hipStream_t stream);
+// Decode in one KV pass per query (spa_decode_rows.hip): D 128, one slice,
+// bf16 or e4m3 compressed pages; one workgroup per (query, KV head, block of
+// 32 query heads) whose waves split the rows, their states combined in LDS.
+bool decode_rows_eligible(const Params &p);
+hipError_t launch_decode_rows(const Params &p, hipStream_t stream);
 // 512-wide heads over a shared latent cache (spa_latent.hip): bf16, k_raw ==
 // v_raw and k_cmp == v_cmp; one workgroup per (query, KV head, 64-head block,
 // KV slice); with several slices it writes sink-free partials (plain order).

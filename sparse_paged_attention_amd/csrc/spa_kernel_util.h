@@ -107,12 +107,12 @@ __device__ __forceinline__ float max_lane_pair(float v) {
 // (lane l holds rows 8*(q/4) + 4*(l/32) + q%4, q = 0..15, of column l%32):
 // a row whose bit in the wave-uniform mask tm is clear gets -inf.  The lane
 // mask of each score (two bits of tm: one for lanes 0-31, one for 32-63) is
-// formed in scalar registers and applied with one v_cndmask; a full mask
-// costs nothing.
+// formed in scalar registers and applied by one v_cndmask (inverse ballot),
+// so the compiler still sees the scores' dependence on the MFMA that wrote
+// them; a full mask costs nothing.
 __device__ __forceinline__ void mask_tile_rows(float (&sc)[16], uint32_t tm) {
   tm = __builtin_amdgcn_readfirstlane(tm);
   if (tm == 0xFFFFFFFFu) return;
-  const float ninf = -INFINITY;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int r0 = 8 * (q >> 2) + (q & 3);
@@ -120,9 +120,7 @@ __device__ __forceinline__ void mask_tile_rows(float (&sc)[16], uint32_t tm) {
     const uint32_t lo = (uint32_t)((int32_t)(tm << (31 - r0)) >> 31);
     const uint32_t hi = (uint32_t)((int32_t)(tm << (27 - r0)) >> 31);
     const uint64_t m = (uint64_t)lo | ((uint64_t)hi << 32);
-    float r;
-    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(ninf), "v"(sc[q]), "s"(m));
-    sc[q] = r;
+    sc[q] = __builtin_amdgcn_inverse_ballot_w64(m) ? sc[q] : -INFINITY;
   }
 }
 

@@ -57,7 +57,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -674,21 +673,6 @@ bool prefill_pairs_eligible(const Params &p) {
          2 * ((int64_t)p.topk + p.window) <= kUMax;
 }
 
-// Compute units of the current device (cached per device; 0 if unknown).
-static int32_t device_cus() {
-  static std::atomic<int32_t> cache[64];
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int32_t n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    n = v;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream) {
   if (p.num_queries == 0) return hipSuccess;
   if (!prefill_pairs_eligible(p)) return hipErrorInvalidConfiguration;
@@ -696,7 +680,7 @@ hipError_t launch_prefill_pairs(const Params &p, hipStream_t stream) {
   const int64_t grid = npairs * p.hkv * ((p.group + 63) / 64);
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   Params q = p;
-  q.num_cus = (p.hkv * ((p.group + 63) / 64) == 1) ? device_cus() : 0;   // one item per pair
+  q.num_cus = (p.hkv * ((p.group + 63) / 64) == 1) ? device_cu_count() : 0;   // one item per pair
   hipLaunchKernelGGL((attn_pair_kernel<kPairStages>), dim3((unsigned)grid), dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }

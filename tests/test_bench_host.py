@@ -31,8 +31,12 @@ def test_kernel_names_follow_the_selection():
     assert bench.attention_kernel(dec, 4, 64, 0) == "attn_fwd_kernel"
     fp8 = synth.make_workload("mixed_fp8", batch=2)
     assert bench.attention_kernel(fp8, 8, 0, 0) == "attn_decode_kernel<true>"
-    # one slice of 512 listed + 128 window rows fits the decode kernel
-    assert bench.attention_kernel(dec, 1, 0, 0) == "attn_decode_kernel<false>"
+    # one slice of 512 listed + 128 window rows: the one-pass decode kernel
+    assert bench.attention_kernel(dec, 1, 0, 0) == "attn_decode_rows_kernel<false>"
+    assert bench.attention_kernel(fp8, 1, 0, 0) == "attn_decode_rows_kernel<true>"
+    # a batch whose 32-head workgroups exceed the CUs keeps the 128-head kernel
+    big = synth.make_workload("decode_csa", batch=128)
+    assert bench.attention_kernel(big, 1, 0, 0, cus=256) == "attn_decode_kernel<false>"
     lat = synth.make_workload("decode_latent", batch=2)
     assert bench.attention_kernel(lat, 4, 0, 0) == "attn_latent_kernel"
 

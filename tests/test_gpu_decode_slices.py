@@ -147,3 +147,26 @@ def test_fnuz_every_code():
     fin = ~np.isnan(Oref[3])
     assert np.all(np.abs(O[3][fin] - Oref[3][fin]) <= 1e-2 + 1e-2 * np.abs(Oref[3][fin]))
     assert np.all(np.abs(L[3] - Lref[3]) <= 1e-3)
+
+
+@pytest.mark.parametrize("name", ["decode_csa", "decode_hca", "mixed_fp8"])
+def test_one_pass_kernel_workloads(name):
+    """One slice: the kernel whose four waves split a query's rows and meet
+    in LDS (no partials, no merge kernel)."""
+    check_against_oracle(synth.make_workload(name), num_splits=1, label=f"{name} one pass")
+
+
+def test_one_pass_kernel_edges():
+    """Heads per KV group not a multiple of 32 (the last head block partial),
+    two KV heads, a batch that is not a multiple of 8 (the grid is padded),
+    a query with one row, empty lists, no sink, and FNUZ pages."""
+    p = _decode("rows_gqa", [3000, 1, 700, 64, 5000], 80, 2, 64, 128, 4, 512, seed=61)
+    p.cmp_cnt[2] = 0
+    check_against_oracle(p, num_splits=1, label="one pass gqa")
+    q = _decode("rows_nosink", [129, 2100, 4096], 128, 1, 64, 128, 4, 512, seed=62, with_sink=False)
+    check_against_oracle(q, num_splits=1, label="one pass no sink")
+    f = _decode("rows_fnuz", [3000, 1500, 700, 5000, 129], 128, 1, 64, 128, 4, 512, seed=63, cmp_fp8=True,
+                fp8_format="fnuz", selection="random")
+    check_against_oracle(f, num_splits=1, label="one pass fnuz")
+    w = _decode("rows_window", [40, 300, 1000], 64, 1, 16, 128, 0, 0, seed=64)
+    check_against_oracle(w, num_splits=1, label="one pass window only")
