@@ -1,9 +1,13 @@
 """Bitwise batch and chunk invariance: a query's O and LSE do not depend on
 which other queries share its call.
 
-* Decode (both kernels, fixed split count): a query's slices, tiles and the
-  merge read only its own rows, so any batch that contains it gives the
-  same bits.
+* Decode (fixed split count): a query's slices, tiles and the merge, or
+  with one slice the one-pass kernel's waves, read only its own rows, so
+  any batch that contains it gives the same bits as long as the same kernel
+  serves both calls.  With one slice the library takes the one-pass kernel
+  only while its workgroups fit the chip, so bits may change where a batch
+  crosses that size; a caller who needs them fixed passes two or more
+  slices.
 * Prefill with one query per job (queries_per_block 1): a chunked prefill
   gives the same bits as one call over all its queries.
 * Prefill with query pairs (the library's default) streams the union of two
@@ -53,6 +57,15 @@ def test_decode_batch_invariance(hpb):
     O, L, _ = run_hip(p, 4, heads_per_block=hpb)
     for idx in ([31, 7, 2, 19, 0, 11, 25, 3], list(range(0, 32, 3)), [5]):
         Os, Ls, _ = run_hip(_decode_subset(p, idx), 4, heads_per_block=hpb)
+        assert np.array_equal(Os, O[idx]) and np.array_equal(Ls, L[idx]), idx
+
+
+def test_decode_one_pass_batch_invariance():
+    p = synth.make_workload("decode_csa")
+    announce("decode batch invariance, one pass")
+    O, L, _ = run_hip(p, 1)
+    for idx in ([31, 7, 2, 19, 0, 11, 25, 3], list(range(1, 32, 5)), [30]):
+        Os, Ls, _ = run_hip(_decode_subset(p, idx), 1)
         assert np.array_equal(Os, O[idx]) and np.array_equal(Ls, L[idx]), idx
 
 
