@@ -182,6 +182,9 @@ def parse_args(argv=None):
                     choices=["decode_csa", "decode_hca", "mixed_fp8", "prefill_csa", "tiny", "decode_latent",
                              "topk_decode", "topk_prefill", "bwd_prefill_csa"])
     ap.add_argument("--batch", type=int, default=0, help="decode batch override (0 = the workload's)")
+    ap.add_argument("--topk-order", default="score", choices=["score", "id"],
+                    help="top-k workloads: ids by descending score (attn_topk_select) or by id "
+                         "(attn_topk_select_ids)")
     ap.add_argument("--context", type=int, default=0,
                     help="decode sequence length for every query (0 = the workload's); a sweep of the KV-set size")
     ap.add_argument("--splits", type=int, default=0, help="0 = the default for the workload")
@@ -437,10 +440,11 @@ TOPK_SHAPES = {   # rows, per-row counts (complete ratio-4 groups), k
 }
 
 
-def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0, eager_only=False):
-    """Time attn_topk_select on scores over the complete groups of the
-    decode CSA or prefill CSA workload (seeded N(0,1) scores; the pages do
-    not define the indexer's scoring).  One step = one call."""
+def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0, eager_only=False, order="score"):
+    """Time attn_topk_select (order "score") or attn_topk_select_ids (order
+    "id") on scores over the complete groups of the decode CSA or prefill
+    CSA workload (seeded N(0,1) scores; the pages do not define the
+    indexer's scoring).  One step = one call."""
     import numpy as np
     import torch
     from sparse_paged_attention_amd import api, _lib
@@ -463,12 +467,14 @@ def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0, eager_only=False
     ids = torch.empty((rows, k), dtype=torch.int32, device="cuda")
     cnt = torch.empty(rows, dtype=torch.int32, device="cuda")
 
+    by_id = order == "id"
+    fn = lib.attn_topk_select_ids if by_id else lib.attn_topk_select
+
     def launch(stream, r):
-        _lib.check(lib.attn_topk_select(sc[r % reps].data_ptr(), ld, nv.data_ptr(), rows, k, ids.data_ptr(),
-                                        cnt.data_ptr(), stream))
+        _lib.check(fn(sc[r % reps].data_ptr(), ld, nv.data_ptr(), rows, k, ids.data_ptr(), cnt.data_ptr(), stream))
 
     for r in range(warmup):
-        api.topk_select(sc[r % reps], nv, k)
+        api.topk_select(sc[r % reps], nv, k, by_id=by_id)
     torch.cuda.synchronize()
     ms, per = eager_ms(launch, steps) if eager_only else graph_replay_ms(launch, steps, reps)[:2]
     read_b = int(n_valid.sum()) * 4 + rows * 4
@@ -481,7 +487,7 @@ def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0, eager_only=False
         done = 0
         while time.perf_counter() - t0 < cpu_budget:
             i = done % rows
-            oracle.topk_select(scores_h[i:i + 1], n_valid[i:i + 1], k)
+            oracle.topk_select(scores_h[i:i + 1], n_valid[i:i + 1], k, by_id=by_id)
             done += 1
         dt = time.perf_counter() - t0
         cpu = {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
@@ -491,14 +497,16 @@ def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0, eager_only=False
         "value": rows / (ms / 1e3), "unit": "rows/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": workload, "shape": TOPK_SHAPES[workload], "rows": rows, "k": k, "replicas": reps},
+        "config": {"workload": workload, "shape": TOPK_SHAPES[workload], "rows": rows, "k": k, "order": order,
+                   "replicas": reps},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "topk_kernel",
                      "kernel_ms": ms, "kernel_ms_how": ("host-launched calls" if eager_only
                                                         else "graph replay of the step (one kernel)"),
                      "algorithmic_bytes_per_launch": read_b + write_b},
         "cpu_baseline": cpu,
-    } | {"_traffic": measured_traffic(workload, {"rows": rows, "k": k}, TOPK_SOURCES, ("rows", "k"))}
+    } | {"_traffic": measured_traffic(workload, {"rows": rows, "k": k, "order": order}, TOPK_SOURCES,
+                                      ("rows", "k", "order"))}
 
 
 def run_backward(workload, *, steps=20, warmup=3, cpu_budget=0.0, rotate_mb=640.0, eager_only=False):
@@ -616,7 +624,7 @@ def main():
         return
     if args.workload.startswith("topk_"):
         out = run_topk(args.workload, steps=args.steps, warmup=args.warmup, cpu_budget=args.cpu_budget,
-                       eager_only=args.eager_only)
+                       eager_only=args.eager_only, order=args.topk_order)
         out["roofline"]["traffic"] = out.pop("_traffic")
         print(json.dumps(out), flush=True)
         return

@@ -245,6 +245,15 @@ spa_status attn_build_gather(const spa_fwd_args *args, int32_t decode, int32_t c
 spa_status attn_topk_select(const float *scores, int64_t ld, const int32_t *n_valid, int32_t num_rows,
                             int32_t k, int32_t *ids_out, int32_t *cnt_out, void *stream);
 
+/* The same selection as attn_topk_select, with the ids of each row written
+   in ascending id order instead of by score (the same arguments, limits and
+   errors).  The attention core takes a query's list as a set (its result
+   depends on the order only through rounding), and ascending ids visit the
+   compressed cache's pages in address order; this order also needs no sort
+   of the selection. */
+spa_status attn_topk_select_ids(const float *scores, int64_t ld, const int32_t *n_valid, int32_t num_rows,
+                                int32_t k, int32_t *ids_out, int32_t *cnt_out, void *stream);
+
 /* Backward pass: gradients of q, of both KV caches and of the sink, from
    the forward's saved O and LSE.  RL-Kernel PR "Roadmap item 24: joint
    compressed/window attention with sink": section "Reuse and arithmetic"

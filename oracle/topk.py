@@ -22,7 +22,8 @@ The order is a reading, since the pages fix none:
 * a NaN score below every number, -inf included.
 
 It is a total order, so the selected list is unique and parity with it is
-bit-exact.
+bit-exact.  With ``by_id`` the same selection is listed in ascending id
+order (the attention core takes a list as a set).
 """
 from __future__ import annotations
 
@@ -40,9 +41,11 @@ def order_key(scores: np.ndarray) -> np.ndarray:
     return np.where(np.isnan(scores), np.uint32(0), key).astype(np.uint32)
 
 
-def topk_select(scores: np.ndarray, n_valid: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+def topk_select(scores: np.ndarray, n_valid: np.ndarray, k: int,
+                by_id: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """For each row i, the min(k, n_i) highest of scores[i, :n_i] (n_i is
-    n_valid[i] clamped to [0, row length]), in the order above.
+    n_valid[i] clamped to [0, row length]), in the order above, or by
+    ascending id with ``by_id``.
 
     Returns (ids int32 [rows, k], -1 past the count; counts int32 [rows])."""
     scores = np.asarray(scores, dtype=np.float32)
@@ -54,6 +57,6 @@ def topk_select(scores: np.ndarray, n_valid: np.ndarray, k: int) -> Tuple[np.nda
         keys = order_key(scores[i, :n]).astype(np.int64)
         order = np.lexsort((np.arange(n), -keys))     # primary: key descending; then id ascending
         take = min(k, n)
-        ids[i, :take] = order[:take]
+        ids[i, :take] = np.sort(order[:take]) if by_id else order[:take]
         cnt[i] = take
     return ids, cnt

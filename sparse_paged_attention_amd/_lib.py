@@ -26,8 +26,8 @@ SPA_MAX_SPLITS = 64
 # exported symbols, in include/spa.h order
 SYMBOLS = ("attn_workspace_size", "attn_fwd_decode", "attn_fwd_decode_noalloc", "attn_noalloc_scratch_bytes",
            "attn_fwd_prefill", "attn_merge_lse",
-           "attn_build_gather", "attn_topk_select", "attn_bwd_workspace_size", "attn_bwd", "attn_last_error",
-           "attn_abi_version")
+           "attn_build_gather", "attn_topk_select", "attn_topk_select_ids", "attn_bwd_workspace_size", "attn_bwd",
+           "attn_last_error", "attn_abi_version")
 SPA_MAX_TOPK = 2048
 
 
@@ -121,9 +121,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_build_gather.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_build_gather.restype = ctypes.c_int
-    lib.attn_topk_select.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    lib.attn_topk_select.restype = ctypes.c_int
+    for fn in (lib.attn_topk_select, lib.attn_topk_select_ids):
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
     lib.attn_bwd_workspace_size.argtypes = [P]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_bwd.argtypes = [P, ctypes.POINTER(SpaBwdGrads), ctypes.c_void_p]

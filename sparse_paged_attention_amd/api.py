@@ -203,9 +203,12 @@ def build_gather(dp: DeviceProblem, cap: int) -> Tuple[torch.Tensor, torch.Tenso
     return rows, counts
 
 
-def topk_select(scores: torch.Tensor, n_valid: torch.Tensor, k: int) -> Tuple[torch.Tensor, torch.Tensor]:
-    """attn_topk_select: scores f32 [rows, ld] (row stride ld), n_valid i32
-    [rows] -> (ids i32 [rows, k], -1 past the count; counts i32 [rows])."""
+def topk_select(scores: torch.Tensor, n_valid: torch.Tensor, k: int,
+                by_id: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """attn_topk_select (by score) or attn_topk_select_ids (by_id: the same
+    selection in ascending id order): scores f32 [rows, ld] (row stride ld),
+    n_valid i32 [rows] -> (ids i32 [rows, k], -1 past the count; counts i32
+    [rows])."""
     lib = _lib.load()
     if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
         raise ValueError("scores must be a float32 [rows, ld] tensor with unit column stride")
@@ -213,8 +216,9 @@ def topk_select(scores: torch.Tensor, n_valid: torch.Tensor, k: int) -> Tuple[to
     ids = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
     cnt = torch.empty(rows, dtype=torch.int32, device=scores.device)
     nv = n_valid.to(device=scores.device, dtype=torch.int32).contiguous()
-    _lib.check(lib.attn_topk_select(_ptr(scores), scores.stride(0) if rows else max(scores.shape[1], 1), _ptr(nv),
-                                    rows, k, _ptr(ids), _ptr(cnt), _stream()))
+    fn = lib.attn_topk_select_ids if by_id else lib.attn_topk_select
+    _lib.check(fn(_ptr(scores), scores.stride(0) if rows else max(scores.shape[1], 1), _ptr(nv), rows, k, _ptr(ids),
+                  _ptr(cnt), _stream()))
     return ids, cnt
 
 

@@ -85,7 +85,7 @@ hipError_t launch_gather(const Params &p, int32_t cap, int64_t *rows_out, int32_
 // Top-k selection from per-token scores (spa_topk.hip); 1 <= k <= kTopkMax.
 constexpr int kTopkMax = 2048;
 hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, int32_t rows, int32_t k,
-                       int32_t *ids_out, int32_t *cnt_out, hipStream_t stream);
+                       int32_t *ids_out, int32_t *cnt_out, bool by_id, hipStream_t stream);
 
 // Backward (spa_backward.hip): bf16 caches, D 128.  dq is written; the
 // gradient caches and dsink are accumulated into.

@@ -164,6 +164,11 @@ int main() {
                                   static_cast<int32_t *>(fake(0x300000)), static_cast<int32_t *>(fake(0x400000)),
                                   nullptr),
          SPA_ERR_LAUNCH);
+  expect("topk ids", attn_topk_select_ids(static_cast<const float *>(fake(0x100000)), 1024,
+                                          static_cast<const int32_t *>(fake(0x200000)), 32, 512,
+                                          static_cast<int32_t *>(fake(0x300000)),
+                                          static_cast<int32_t *>(fake(0x400000)), nullptr),
+         SPA_ERR_LAUNCH);
   if (attn_abi_version() != 1) ++failures;
   std::printf("host paths driven; %d unexpected statuses\n", failures);
   return failures == 0 ? 0 : 1;

@@ -194,15 +194,18 @@ def test_gather_validation(lib):
     assert lib.attn_build_gather(ctypes.byref(a), 1, 16, 0x10000000, 0x10000000, None) == -4
 
 
-def test_topk_validation(lib):
-    """attn_topk_select refuses bad arguments before any HIP call."""
+@pytest.mark.parametrize("name", ["attn_topk_select", "attn_topk_select_ids"])
+def test_topk_validation(lib, name):
+    """attn_topk_select and attn_topk_select_ids refuse bad arguments before
+    any HIP call."""
     P = 0x10000000
-    assert lib.attn_topk_select(None, 8, P, 1, 4, P, P, None) == -1
-    assert lib.attn_topk_select(P, 8, P, 1, 4, None, P, None) == -1
-    assert lib.attn_topk_select(P, 8, P, -1, 4, P, P, None) == -2
-    assert lib.attn_topk_select(P, 0, P, 1, 4, P, P, None) == -2
-    assert lib.attn_topk_select(P, 8, P, 1, 0, P, P, None) == -4
-    assert lib.attn_topk_select(P, 8, P, 1, _lib.SPA_MAX_TOPK + 1, P, P, None) == -4
+    fn = getattr(lib, name)
+    assert fn(None, 8, P, 1, 4, P, P, None) == -1
+    assert fn(P, 8, P, 1, 4, None, P, None) == -1
+    assert fn(P, 8, P, -1, 4, P, P, None) == -2
+    assert fn(P, 0, P, 1, 4, P, P, None) == -2
+    assert fn(P, 8, P, 1, 0, P, P, None) == -4
+    assert fn(P, 8, P, 1, _lib.SPA_MAX_TOPK + 1, P, P, None) == -4
     assert b"k " in lib.attn_last_error()
 
 

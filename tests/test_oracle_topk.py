@@ -49,6 +49,23 @@ def test_topk_matches_brute_force(seed):
             assert np.all(ids[i, cnt[i]:] == -1)
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_topk_by_id_matches_brute_force(seed):
+    """The id-ordered list is the brute-force selection sorted by id."""
+    rng = np.random.default_rng(100 + seed)
+    rows, ld = 7, 50
+    scores = np.stack([_special_row(rng, ld) for _ in range(rows)])
+    n_valid = rng.integers(-2, ld + 5, size=rows)
+    for k in (1, 9, 25, 64):
+        ids, cnt = topk_select(scores, n_valid, k, by_id=True)
+        for i in range(rows):
+            n = min(max(int(n_valid[i]), 0), ld)
+            want = sorted(_brute(scores[i], n, k))
+            assert cnt[i] == len(want)
+            assert list(ids[i, :cnt[i]]) == want, (seed, k, i)
+            assert np.all(ids[i, cnt[i]:] == -1)
+
+
 def test_order_key_is_monotone():
     vals = np.array([-np.inf, -3e38, -1.0, -1e-40, -0.0, 0.0, 1e-40, 1.0, 2.0, 3e38, np.inf], dtype=np.float32)
     keys = order_key(vals)
