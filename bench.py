@@ -549,7 +549,9 @@ def run_backward(workload, *, steps=20, warmup=3, cpu_budget=0.0, rotate_mb=640.
         d_o = torch.from_numpy(dO_bits.view(np.int16)).cuda().view(torch.bfloat16)
         args = dp.args(1)
         args.o, args.lse = o.data_ptr(), lse.data_ptr()
-        ws = torch.empty(int(lib.attn_bwd_workspace_size(ctypes.byref(args))), dtype=torch.uint8, device="cuda")
+        need = int(lib.attn_bwd_workspace_size(ctypes.byref(args)))
+        kv_path = need > nq * Hq * 4
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
         dq = torch.empty(p.q.shape, dtype=torch.float32, device="cuda")
         gr = _lib.SpaBwdGrads()
@@ -593,9 +595,10 @@ def run_backward(workload, *, steps=20, warmup=3, cpu_budget=0.0, rotate_mb=640.
                    "window": p.window, "ratio": p.ratio, "topk": p.topk, "kv_entries": kv_entries,
                    "replicas": reps},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "attn_bwd_kernel",
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "attn_bwd_kernel<2, false> + attn_bwd_kv_kernel" if kv_path else "attn_bwd_kernel<2, true>",
                      "kernel_ms": ms, "kernel_ms_how": ("host-launched calls" if eager_only else
-                                                        "graph replay of the step (backward kernel + sink reduction)"),
+                                                        "graph replay of the step (every kernel of the call)"),
                      "algorithmic_flops_per_launch": alg_flops},
         "cpu_baseline": cpu,
         "timing": {"graph_replay_ms_per_step_min": float(per.min()), "graph_replay_ms_per_step_max": float(per.max())},

@@ -281,10 +281,18 @@ spa_status attn_topk_select_ids(const float *scores, int64_t ld, const int32_t *
    when ratio > 0); d_sink f32 [Hq] or NULL (no sink gradient; must be NULL
    when args->sink is).  The accumulated buffers are zeroed by the caller
    before the first call; dk/dv are added with float atomics, so their
-   rounding order, and their last bits, vary from run to run.  With d_sink
-   the call needs a workspace of attn_bwd_workspace_size(args) bytes in
-   args->workspace (16-byte aligned; SPA_ERR_WORKSPACE otherwise).  Invalid
-   metadata is flagged and masked as in the forward. */
+   rounding order, and their last bits, vary from run to run.
+   Workspace (args->workspace, 16-byte aligned, SPA_ERR_ALIGN otherwise):
+   attn_bwd_workspace_size(args) bytes let a prefill call take the
+   KV-block path, in which dk and dv are summed per block of 32 cache rows
+   over every query that reads them and added once per block and slice of
+   32 queries; the size then covers per-head LSE and Delta arrays and, for
+   a top-k layer, a bitmap of each query's listed groups.  A smaller
+   workspace (or a decode call) keeps the fused kernel, whose workgroups add
+   dk and dv per query or query pair; it needs num_queries * num_q_heads * 4
+   bytes with d_sink and none without (SPA_ERR_WORKSPACE when d_sink is
+   set and the workspace is smaller).  Invalid metadata is flagged and
+   masked as in the forward. */
 typedef struct spa_bwd_grads {
   const void *d_o;
   float *dq;

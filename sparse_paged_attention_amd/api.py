@@ -224,12 +224,16 @@ def topk_select(scores: torch.Tensor, n_valid: torch.Tensor, k: int,
 
 def backward(dp: DeviceProblem, o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor, *,
              err_flag: Optional[torch.Tensor] = None, want_dsink: bool = True,
-             grads: Optional[dict] = None, stream: Optional[int] = None, queries_per_block: int = 0) -> dict:
+             grads: Optional[dict] = None, stream: Optional[int] = None, queries_per_block: int = 0,
+             fused: bool = False) -> dict:
     """attn_bwd: gradients of the forward call described by ``dp`` from its
     outputs (o bf16, lse f32) and the upstream gradient d_o (bf16 [Nq,Hq,D]).
     Returns dict dq, dk_raw, dv_raw, dk_cmp, dv_cmp, d_sink (f32; the cache
     gradients have the caches' shapes).  ``grads`` reuses buffers, which the
-    call accumulates into (dq is overwritten)."""
+    call accumulates into (dq is overwritten).  The workspace is sized by
+    attn_bwd_workspace_size, which lets the library take the KV-block path;
+    ``fused`` passes only the sink partials' share, which keeps the fused
+    kernel."""
     lib = _lib.load()
     dev = dp.q.device
     if grads is None:
@@ -247,8 +251,10 @@ def backward(dp: DeviceProblem, o: torch.Tensor, lse: torch.Tensor, d_o: torch.T
     args.lse = _ptr(lse)
     args.err_flag = _ptr(err_flag)
     ws = None
-    if grads["d_sink"] is not None:
-        need = int(lib.attn_bwd_workspace_size(ctypes.byref(args)))
+    need = int(lib.attn_bwd_workspace_size(ctypes.byref(args)))
+    if fused:
+        need = dp.num_queries * dp.num_q_heads * 4 if grads["d_sink"] is not None else 0
+    if need > 0:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         args.workspace = _ptr(ws)
         args.workspace_bytes = ws.numel()

@@ -32,8 +32,21 @@ SOURCE_FLAGS = {"spa_attention.hip": ["-fno-honor-nans"], "spa_pair.hip": ["-fno
                 "spa_decode.hip": ["-fno-honor-nans"],
                 "spa_latent.hip": ["-fno-honor-nans"],
                 "spa_decode_rows.hip": ["-fno-honor-nans"]}
+# The backward keeps its MFMA accumulators in AGPRs: the KV-block kernel's
+# dK and dV sums (128 registers) leave the VGPRs free for its LDS operands.
+AGPR_ACC = {"spa_backward.hip"}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]
+
+
+def device_flags(src: str) -> list:
+    """DEVICE_FLAGS, without the VGPR accumulator form for AGPR_ACC files."""
+    if src not in AGPR_ACC:
+        return list(DEVICE_FLAGS)
+    f = list(DEVICE_FLAGS)
+    i = f.index("-amdgpu-mfma-vgpr-form")
+    del f[i - 1:i + 1]
+    return f
 
 
 def _hipcc():
@@ -45,7 +58,7 @@ def _hipcc():
 
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS + SOURCE_FLAGS.get(src, [])
+    cmd = [_hipcc(), "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + COMMON + device_flags(src) + SOURCE_FLAGS.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -398,7 +398,12 @@ spa_status attn_topk_select_ids(const float *scores, int64_t ld, const int32_t *
 }
 
 size_t attn_bwd_workspace_size(const spa_fwd_args *args) {
-  if (args == nullptr || args->num_queries < 0 || args->num_q_heads < 1) return 0;
+  if (args == nullptr || args->num_queries < 0 || args->num_q_heads < 1 || args->num_kv_heads < 1 ||
+      args->num_q_heads % args->num_kv_heads != 0 || args->page_size < 1 || args->num_seqs < 0)
+    return 0;
+  const bool decode = args->query_seq == nullptr && args->query_pos == nullptr;
+  const spa::Params p = make_params(args, decode);
+  if (spa::backward_kv_eligible(p)) return spa::backward_kv_workspace(p, nullptr, nullptr, nullptr);
   return (size_t)args->num_queries * (size_t)args->num_q_heads * sizeof(float);
 }
 
@@ -442,17 +447,25 @@ spa_status attn_bwd(const spa_fwd_args *args, const spa_bwd_grads *grads, void *
   b.dv_cmp = a.ratio > 0 ? grads->dv_cmp : nullptr;
   b.dsink = grads->d_sink;
   b.scale = a.scale;
+  // the KV-block path when the workspace holds its plan, else the fused
+  // kernel (float atomics per query or query pair), which needs a
+  // workspace only for the sink gradient
+  spa::BwdKvPlan plan{};
+  const size_t need_kv = spa::backward_kv_eligible(p) ? spa::backward_kv_workspace(p, nullptr, nullptr, nullptr) : 0;
+  const bool use_kv = need_kv > 0 && a.workspace != nullptr && a.workspace_bytes >= need_kv;
+  const size_t need_sink = (size_t)a.num_queries * (size_t)a.num_q_heads * sizeof(float);
+  if (a.workspace != nullptr && (use_kv || grads->d_sink != nullptr) && !aligned16(a.workspace))
+    return fail(SPA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (use_kv) spa::backward_kv_workspace(p, a.workspace, &plan, &b);
   if (grads->d_sink != nullptr) {
-    const size_t need = attn_bwd_workspace_size(&a);
-    if (need > 0 && (a.workspace == nullptr || a.workspace_bytes < need))
-      return fail(SPA_ERR_WORKSPACE, "the sink gradient needs a workspace of %zu bytes", need);
-    if (need > 0 && !aligned16(a.workspace)) return fail(SPA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (need_sink > 0 && (a.workspace == nullptr || a.workspace_bytes < need_sink))
+      return fail(SPA_ERR_WORKSPACE, "the sink gradient needs a workspace of %zu bytes", need_sink);
     b.dsink_part = static_cast<float *>(a.workspace);
   }
   if (a.num_queries == 0) return ok();
   if ((int64_t)a.num_queries * a.num_kv_heads * ((a.num_q_heads / a.num_kv_heads + 63) / 64) > 0x7FFFFFFFLL)
     return fail(SPA_ERR_SHAPE, "the job count exceeds the launch grid");
-  hipError_t e = spa::launch_backward(p, b, pairs, static_cast<hipStream_t>(stream));
+  hipError_t e = spa::launch_backward(p, b, pairs, use_kv ? &plan : nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SPA_ERR_LAUNCH, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }

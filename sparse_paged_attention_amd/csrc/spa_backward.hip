@@ -39,9 +39,15 @@
 // atomic instruction covers 128 contiguous bytes of two rows.  dQ is written once
 // (fp32).  The sink gradient is written per (query, head) and summed over
 // the queries by sink_reduce_kernel, in a fixed order.
+//
+// With a workspace for it, a prefill call instead forms dK and dV in the
+// KV-block pass further down (rows summed over the queries that read them
+// before one atomic add per block and query slice), and the kernel above
+// runs without its dK and dV part.
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "spa_device.h"
@@ -62,8 +68,9 @@ constexpr int kBStages = 2;
 constexpr int64_t kCmpBit = int64_t(1) << 62;
 
 // NQ queries per workgroup (1, or 2 for a prefill query pair); 2 NQ waves,
-// wave w = query (w / 2) x head half (w % 2).
-template <int NQ>
+// wave w = query (w / 2) x head half (w % 2).  DKV: the workgroup also forms
+// dK and dV (Q, dO, P and dS exchanged through LDS); without it only dQ.
+template <int NQ, bool DKV>
 struct BwdSmem {
   static constexpr int kRows = NQ == 1 ? kBRows : kPairRows;
   union {
@@ -73,18 +80,19 @@ struct BwdSmem {
     } t;
     uint32_t bm[2][kBmWords];              // query pair setup: each query's selected groups
   } u;
-  alignas(16) uint8_t q[2 * NQ][kTileB];   // wave w: its query's 32 heads as tile rows
-  alignas(16) uint8_t dO[2 * NQ][kTileB];
+  static constexpr int kX = DKV ? 2 * NQ : 1;
+  alignas(16) uint8_t q[kX][DKV ? kTileB : 16];   // wave w: its query's 32 heads as tile rows
+  alignas(16) uint8_t dO[kX][DKV ? kTileB : 16];
   alignas(16) int64_t row[kRows];          // row * Hkv + g (bit 62: compressed), -1: masked
   uint8_t flg[NQ == 1 ? 1 : kRows];        // query pair: bit q = in query q's set
-  alignas(16) bf16x8 xp[2 * NQ][2][64];    // P and dS of each wave's heads, A-fragment order
-  alignas(16) bf16x8 xd[2 * NQ][2][64];
+  alignas(16) bf16x8 xp[kX][2][DKV ? 64 : 1];   // P and dS of each wave's heads, A-fragment order
+  alignas(16) bf16x8 xd[kX][2][DKV ? 64 : 1];
   alignas(16) float lse2[NQ * 64];         // LSE * log2(e); +inf: no softmax (no rows, not a head)
   alignas(16) float delta[NQ * 64];
   int32_t wsum[2 * NQ];
   int32_t dup;                             // a pair's list names a group twice
 };
-static_assert(sizeof(BwdSmem<2>::u) >= 2 * kBmWords * 4, "bitmaps fit the tile stages");
+static_assert(sizeof(BwdSmem<2, true>::u) >= 2 * kBmWords * 4, "bitmaps fit the tile stages");
 
 // A K^T, V^T, Q^T or dO^T fragment of a tile in LDS (transposing reads):
 // as the A operand, lane L holds column d = 32 db + L % 32 and the tile rows
@@ -223,12 +231,12 @@ __device__ int32_t pair_rows(const Params &p, Smem &sm, int32_t i0, int32_t i1, 
   return U;
 }
 
-template <int NQ>
+template <int NQ, bool DKV>
 __global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams b) {
   constexpr int NT = 128 * NQ;
   constexpr int NW = 2 * NQ;                 // waves
   constexpr int kRowsPerWave = kPT / NW;     // tile rows each wave loads
-  __shared__ BwdSmem<NQ> sm;
+  __shared__ BwdSmem<NQ, DKV> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -259,11 +267,13 @@ __global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams 
     const int r = idx >> 4, c = idx & 15;
     const bool ok = qvalid && h0 + r < p.group;
     const int64_t off = (qbase + h0 + r) * kD + c * 8;
-    const uint4 qv = ok ? *(const uint4 *)(p.q + off) : uint4{0, 0, 0, 0};
-    const uint4 ov = ok ? *(const uint4 *)(b.d_o + off) : uint4{0, 0, 0, 0};
-    const int dst = r * kRowB + ((c ^ swz<kChunks>(r)) * 16);
-    *(uint4 *)(sm.q[wave] + dst) = qv;
-    *(uint4 *)(sm.dO[wave] + dst) = ov;
+    if constexpr (DKV) {
+      const uint4 qv = ok ? *(const uint4 *)(p.q + off) : uint4{0, 0, 0, 0};
+      const uint4 ov = ok ? *(const uint4 *)(b.d_o + off) : uint4{0, 0, 0, 0};
+      const int dst = r * kRowB + ((c ^ swz<kChunks>(r)) * 16);
+      *(uint4 *)(sm.q[wave] + dst) = qv;
+      *(uint4 *)(sm.dO[wave] + dst) = ov;
+    }
   }
   const int hl = h0 + (lane & 31);                    // this lane's head (head-column layouts)
   const bool hvalid = qvalid && hl < p.group;
@@ -303,6 +313,13 @@ __global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams 
       const bool live = hvalid && lse != -INFINITY;
       sm.lse2[hslot] = live ? lse * kLog2e : INFINITY;
       sm.delta[hslot] = live ? dsum : 0.f;
+      // for the KV-block pass: every head slot of the padded group, the
+      // heads past the group as +inf / 0
+      if (b.lse2_ws != nullptr && qvalid && hl < b.gp) {
+        const int64_t wi = ((int64_t)iq * p.hkv + g) * b.gp + hl;
+        b.lse2_ws[wi] = live ? lse * kLog2e : INFINITY;
+        b.delta_ws[wi] = live ? dsum : 0.f;
+      }
       if (hvalid && b.dsink_part != nullptr) {
         const float part = (live && p.sink != nullptr) ? -__expf(p.sink[g * p.group + hl] - lse) * dsum : 0.f;
         b.dsink_part[qbase + hl] = part;
@@ -411,13 +428,13 @@ __global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams 
       for (int kk = 0; kk < kD / 16; ++kk) {
         const bf16x8 kf = row_frag(Kt, lane, kk);
         s_rh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s_rh, 0, 0, 0);
-        s_hr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kf, s_hr, 0, 0, 0);
+        if constexpr (DKV) s_hr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kf, s_hr, 0, 0, 0);
       }
 #pragma unroll
       for (int kk = 0; kk < kD / 16; ++kk) {
         const bf16x8 vf = row_frag(Vt, lane, kk);
         dp_rh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[kk], dp_rh, 0, 0, 0);
-        dp_hr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dof[kk], vf, dp_hr, 0, 0, 0);
+        if constexpr (DKV) dp_hr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dof[kk], vf, dp_hr, 0, 0, 0);
       }
       // head-column layout: value r is row 8(r/4) + 4hi + r%4 of the tile
       bf16x8 dsb[2];
@@ -427,6 +444,13 @@ __global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams 
         const float pr = ((tm >> row) & 1u) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s_rh[r], sl2, -my_lse2)) : 0.f;
         dsb[r >> 3][r & 7] = (__bf16)(pr * (dp_rh[r] - my_delta));
       }
+      // dQ^T += K^T . dS^T
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Kt, lane, db, k2), dsb[k2], dqa[db], 0, 0, 0);
+      if constexpr (!DKV) continue;
       // row-column layout: value r is head 8(r/4) + 4hi + r%4 of the wave
       bf16x8 pb[2], dsh[2];
 #pragma unroll
@@ -443,12 +467,6 @@ __global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams 
           dsh[r >> 3][r & 7] = (__bf16)(pr * (dp_hr[r] - dv[e]));
         }
       }
-      // dQ^T += K^T . dS^T
-#pragma unroll
-      for (int db = 0; db < kD / 32; ++db)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Kt, lane, db, k2), dsb[k2], dqa[db], 0, 0, 0);
       // dV = P . dO and dK = scale dS . Q for the tile's rows over every
       // wave's heads (both queries of a pair): the waves swap their P and dS
       // fragments through LDS and split the head dimensions, so each gradient
@@ -521,6 +539,328 @@ __global__ __launch_bounds__(256) void sink_reduce_kernel(const float *part, int
   if (threadIdx.x == 0) dsink[h] += red[0];
 }
 
+
+// ---------------------------------------------------------------------------
+// KV-block pass: dK and dV for blocks of 32 rows of one sequence's raw or
+// compressed rows, summed in registers over every (query, 64-head chunk)
+// that reads them and added to the gradient caches once per workgroup.
+// The query-centric kernel above, without its dK and dV part, gives dQ,
+// the sink partials, and each head's LSE log2(e) and Delta.
+//
+// A workgroup takes four consecutive blocks (one per wave, its K and V rows
+// held as B fragments in registers) and a slice of 32 consecutive queries.
+// The slice's queries that read any of the four blocks become items, each
+// with a row mask per block: the window's rows, computed from the query's
+// position; for a top-k layer the bitmap words of its listed groups
+// (written once per query by bwd_bitmap_kernel); for an all-groups layer
+// its complete groups.  A group a query lists again is a further item of
+// its own (the extras list), so it counts once per listing, as in the
+// forward.  The four waves share each item's Q and dO rows (64 heads) in
+// a ring of four LDS buffers, three items' loads in flight; per item and
+// wave, on the wave's own block:
+//   S = Q.K^T, dP = dO.V^T (a lane per row, the item's heads in registers)
+//   P = exp2(S scale log2 e - LSE log2 e) on the item's rows, dS = P (dP - Delta)
+//   dV += P^T.dO, dK += dS^T.Q   (dO, Q by transposing LDS reads)
+// Each wave then adds its block's dK and dV rows with float atomics.
+
+constexpr int kKvQ = 32;                   // queries per workgroup
+constexpr int kKvRing = 4;                 // item buffers
+constexpr int kKvAhead = kKvRing - 1;      // items whose loads are in flight
+constexpr int kKvLoads = 9;                // direct loads per wave and item
+
+__device__ __forceinline__ int64_t quiet_row(const Params &p, int32_t b, bool cmp, int32_t x) {
+  const int32_t P = p.page_size;
+  const int32_t col = x / P;
+  const int32_t stride = cmp ? p.cmp_pt_stride : p.raw_pt_stride;
+  if (col >= stride) return -1;
+  const int32_t page = (cmp ? p.cmp_pt : p.raw_pt)[(int64_t)b * stride + col];
+  if (page < 0 || (int64_t)page >= (cmp ? p.cmp_pages : p.raw_pages)) return -1;
+  return (int64_t)page * P + (x - col * P);
+}
+
+__global__ __launch_bounds__(64) void bwd_extras_zero_kernel(int32_t *n) {
+  if (threadIdx.x == 0) *n = 0;
+}
+
+// Per query of a top-k layer: the bitmap words of its listed groups, and an
+// extras entry (query, group) for each repeated listing.
+__global__ __launch_bounds__(256) void bwd_bitmap_kernel(Params p, BwdKvPlan pl) {
+  __shared__ uint32_t bm[kBmWords];
+  const int tid = threadIdx.x;
+  const int32_t i = blockIdx.x;
+  const QueryKV kv = query_kv(p, i);
+  const int32_t nw = min((kv.n_c + 31) >> 5, pl.nb_cmp);
+  for (int32_t w = tid; w < pl.nb_cmp; w += 256) bm[w] = 0u;
+  __syncthreads();
+  for (int32_t e = tid; e < kv.n_sel; e += 256) {
+    const int32_t c = check_cmp_id(p, kv, p.cmp_idx[(int64_t)i * p.topk + e]);
+    if (c >= 0 && (c >> 5) < nw) {
+      const uint32_t bit = 1u << (c & 31);
+      if (atomicOr(&bm[c >> 5], bit) & bit) {
+        const int32_t slot = atomicAdd(pl.n_extra, 1);
+        if (slot < pl.cap_extra) pl.extra[slot] = make_int2(i, c);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t *const words = pl.bitmap + (int64_t)i * pl.nb_cmp;
+  for (int32_t w = tid; w < pl.nb_cmp; w += 256) words[w] = bm[w];
+}
+
+struct KvItem {
+  int32_t q;
+  uint32_t m[4];                           // row mask of each wave's block
+};
+
+struct KvBuf {
+  alignas(16) uint8_t q[2][kTileB];        // the item's 64 heads as two 32-row tiles
+  alignas(16) uint8_t dO[2][kTileB];
+  alignas(16) uint8_t meta[4][1024];       // wave w's direct load: LSE log2(e) in meta[0], Delta in meta[1]
+};
+
+struct KvSmem {
+  KvBuf buf[kKvRing];
+  KvItem item[64];
+  int64_t row[4][kPT];                     // physical row * Hkv + g, -1: no row
+  int32_t n_items;
+};
+
+// The row mask of block kb (rows 32 kb .. 32 kb + 31) within [lo, hi].
+__device__ __forceinline__ uint32_t span_mask(int32_t kb, int32_t lo, int32_t hi) {
+  const int32_t a = max(lo - 32 * kb, 0), z = min(hi - 32 * kb, 31);
+  if (z < a) return 0u;
+  const uint32_t upto = z == 31 ? 0xFFFFFFFFu : (1u << (z + 1)) - 1u;
+  return upto & ~((1u << a) - 1u);
+}
+
+__global__ __launch_bounds__(256) void attn_bwd_kv_kernel(Params p, BwdParams b, BwdKvPlan pl) {
+  __shared__ KvSmem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // (query slice, KV head, block group): workgroup x runs on XCD x % 8, so
+  // slice ch's workgroups all run on XCD ch % 8, one after another, and
+  // read its Q and dO rows from that XCD's L2; compressed groups (the
+  // longer lists) first within a slice
+  const int64_t x = blockIdx.x;
+  const int64_t m = x >> 3;
+  const int g = (int)(m % p.hkv);
+  const int64_t y = m / p.hkv;
+  const int32_t ngt = p.num_seqs * (pl.ng_cmp + pl.ng_raw);
+  const int32_t grp = (int32_t)(y % ngt);
+  const int32_t ch = (int32_t)(8 * (y / ngt) + (x & 7));
+  if (ch >= pl.nch) return;
+  const int32_t ncg = p.num_seqs * pl.ng_cmp;
+  const bool cmp = grp < ncg;
+  const int32_t gi = cmp ? grp : grp - ncg;
+  const int32_t ngk = cmp ? pl.ng_cmp : pl.ng_raw;
+  const int32_t nbk = cmp ? pl.nb_cmp : pl.nb_raw;
+  const int32_t sb = gi / ngk;
+  const int32_t kb0 = 4 * (gi % ngk);
+  const int32_t q0 = ch * kKvQ;
+  const bool topk_cmp = cmp && p.topk > 0;
+  const int32_t n_extra = topk_cmp ? min(*pl.n_extra, pl.cap_extra) : 0;
+  const int rounds = 1 + (n_extra + 63) / 64;
+
+  // the wave's block: rows and their K and V B fragments (lane L: row L % 32,
+  // dimensions 16 s + 8 (L / 32) .. + 8)
+  const int32_t kb = kb0 + wave;
+  if (lane < kPT) {
+    const int64_t pr = kb < nbk ? quiet_row(p, sb, cmp, 32 * kb + lane) : -1;
+    sm.row[wave][lane] = pr >= 0 ? pr * p.hkv + g : -1;
+  }
+  __syncthreads();
+  const int64_t my_row = sm.row[wave][lane & 31];
+  const bool rvalid = my_row >= 0;
+  const uint8_t *const kbase = cmp ? p.k_cmp : p.k_raw;
+  const uint8_t *const vbase = cmp ? p.v_cmp : p.v_raw;
+  bf16x8 kf[kD / 16], vf[kD / 16];
+#pragma unroll
+  for (int s2 = 0; s2 < kD / 16; ++s2) {
+    const int64_t off = my_row * kRowB + (16 * s2 + 8 * hi) * 2;
+    kf[s2] = rvalid ? *(const bf16x8 *)(kbase + off) : bf16x8{};
+    vf[s2] = rvalid ? *(const bf16x8 *)(vbase + off) : bf16x8{};
+  }
+
+  f32x16 av[kD / 32], ak[kD / 32];
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db) {
+    av[db] = f32x16{};
+    ak[db] = f32x16{};
+  }
+  const int nhc = (p.group + 63) / 64;
+  const float sl2 = p.scale_log2;
+  bool any = false;
+
+  for (int round = 0; round < rounds; ++round) {
+    // ---- the round's items: round 0 the slice's queries, later rounds
+    // the extras list 64 at a time (wave 0 builds the list)
+    if (wave == 0) {
+      KvItem it{0, {0u, 0u, 0u, 0u}};
+      bool use = false;
+      if (round == 0) {
+        const int32_t i = q0 + lane;
+        if (lane < kKvQ && i < p.num_queries) {
+          const QueryKV kv = query_kv(p, i);
+          it.q = i;
+          if (kv.b == sb && (cmp ? kv.n_sel > 0 : kv.win_len > 0)) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const int32_t k2 = kb0 + w;
+              uint32_t m = 0u;
+              if (k2 < nbk) {
+                if (!cmp) m = span_mask(k2, kv.win_lo, kv.t);
+                else if (p.topk > 0) m = pl.bitmap[(int64_t)i * pl.nb_cmp + k2];
+                else m = span_mask(k2, 0, kv.n_sel - 1);
+              }
+              it.m[w] = m;
+            }
+            use = (it.m[0] | it.m[1] | it.m[2] | it.m[3]) != 0u;
+          }
+        }
+      } else {
+        const int32_t xe = 64 * (round - 1) + lane;
+        if (xe < n_extra) {
+          const int2 ex = pl.extra[xe];
+          const int32_t w = (ex.y >> 5) - kb0;
+          if (ex.x >= q0 && ex.x < q0 + kKvQ && w >= 0 && w < 4 && p.query_seq[ex.x] == sb) {
+            it.q = ex.x;
+            it.m[w] = 1u << (ex.y & 31);
+            use = true;
+          }
+        }
+      }
+      const unsigned long long bal = __ballot(use);
+      if (use) sm.item[__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = it;
+      if (lane == 0) sm.n_items = __builtin_popcountll(bal);
+    }
+    __syncthreads();
+    const int32_t nt = sm.n_items * nhc;
+    if (nt == 0) {
+      __syncthreads();                       // the list is rebuilt next round
+      continue;
+    }
+    any = true;
+
+    // item f -> slot f % 4: wave w moves tile rows 16 n + 4 w .. + 3 of Q
+    // and dO (n = 0..3) and its meta row
+    auto issue = [&](int32_t f) {
+      const int32_t k = f / nhc;
+      const int hc = f - k * nhc;
+      const int32_t q = sm.item[k].q;
+      KvBuf &B = sm.buf[f % kKvRing];
+      const int64_t hrow0 = (int64_t)q * p.hq + (int64_t)g * p.group + 64 * hc;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int R = 16 * n + 4 * wave + (lane >> 4);
+        const int cs = ((lane & 15) ^ swz<kChunks>(R & 31)) * 16;
+        const bool hv = 64 * hc + R < p.group;
+        const int64_t off = (hrow0 + R) * kRowB + cs;
+        dma16(hv ? (const uint8_t *)p.q + off : kZeroRow + cs, &B.q[0][0] + (16 * n + 4 * wave) * kRowB);
+        dma16(hv ? (const uint8_t *)b.d_o + off : kZeroRow + cs, &B.dO[0][0] + (16 * n + 4 * wave) * kRowB);
+      }
+      const int64_t mrow = ((int64_t)q * p.hkv + g) * b.gp + 64 * hc;
+      dma16(((wave & 1) ? b.delta_ws : b.lse2_ws) + mrow + 4 * (lane & 15), B.meta[wave]);
+    };
+    const int32_t pro = min(nt, kKvAhead);
+    for (int32_t f = 0; f < pro; ++f) issue(f);
+    for (int32_t j = 0; j < nt; ++j) {
+      const int32_t pending = min(nt - 1 - j, kKvAhead - 1);
+      if (pending >= 2) wait_vmcnt<2 * kKvLoads>();
+      else if (pending == 1) wait_vmcnt<kKvLoads>();
+      else wait_vmcnt<0>();
+      block_sync();                          // item j is in; every wave is done with item j - 1
+      if (j + kKvAhead < nt) issue(j + kKvAhead);
+      const int32_t k = j / nhc;
+      const int hc = j - k * nhc;
+      const uint32_t mask = sm.item[k].m[wave];
+      if (mask == 0u) continue;
+      const KvBuf &B = sm.buf[j % kKvRing];
+      const bool rin = rvalid && ((mask >> (lane & 31)) & 1u) != 0u;
+      const float *const lsev = (const float *)B.meta[0];
+      const float *const delv = (const float *)B.meta[1];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        if (64 * hc + 32 * hb >= p.group) break;
+        const uint8_t *Qt = B.q[hb];
+        const uint8_t *Ot = B.dO[hb];
+        // every fragment read is issued ahead of the products that use it
+        bf16x8 qa[kD / 16], oa[kD / 16];
+#pragma unroll
+        for (int kk = 0; kk < kD / 16; ++kk) {
+          qa[kk] = row_frag(Qt, lane, kk);
+          oa[kk] = row_frag(Ot, lane, kk);
+        }
+        f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < kD / 16; ++kk) {
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], sc, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kk], vf[kk], dp, 0, 0, 0);
+        }
+        bf16x8 ot[kD / 32][2], qt[kD / 32][2];
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            ot[db][k2] = tr_frag(Ot, lane, db, k2);
+            qt[db][k2] = tr_frag(Qt, lane, db, k2);
+          }
+        // a lane per row; value r is head 32 hb + 8(r/4) + 4hi + r%4 of the chunk
+        bf16x8 pa[2], da[2];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 l4 = *(const float4 *)(lsev + 32 * hb + 8 * q4 + 4 * hi);
+          const float4 d4 = *(const float4 *)(delv + 32 * hb + 8 * q4 + 4 * hi);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * q4 + c;
+            const float pr = rin ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], sl2, -lv[c])) : 0.f;
+            pa[r >> 3][r & 7] = (__bf16)pr;
+            da[r >> 3][r & 7] = (__bf16)(rin ? pr * (dp[r] - dv[c]) : 0.f);   // rows outside the set may hold NaN
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            av[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[k2], ot[db][k2], av[db], 0, 0, 0);
+            ak[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[k2], qt[db][k2], ak[db], 0, 0, 0);
+          }
+        // issue order: the 16 fragment reads, the S and dP products with
+        // the 32 transposing reads between them, then the rest
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      }
+    }
+    __syncthreads();                         // the item list and the buffers are rewritten next round
+  }
+  if (!any) return;
+
+  // ---- the wave's block: value r is row 8(r/4) + 4hi + r%4, lane column
+  // d = 32 db + L % 32
+  float *const dv_out = cmp ? b.dv_cmp : b.dv_raw;
+  float *const dk_out = cmp ? b.dk_cmp : b.dk_raw;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t er = sm.row[wave][8 * (r >> 2) + 4 * hi + (r & 3)];
+    if (er >= 0) {
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) {
+        const int d = 32 * db + (lane & 31);
+        unsafeAtomicAdd(dv_out + er * kD + d, av[db][r]);
+        unsafeAtomicAdd(dk_out + er * kD + d, ak[db][r] * b.scale);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 bool backward_eligible(const Params &p) { return p.head_dim == kD && !p.cmp_fp8; }
@@ -532,21 +872,103 @@ bool backward_pairs_eligible(const Params &p) {
          2 * ((int64_t)p.topk + p.window) <= kPairRows;
 }
 
-hipError_t launch_backward(const Params &p, const BwdParams &b, bool pairs, hipStream_t stream) {
+namespace {
+struct KvSizes {
+  int32_t nb_raw, nb_cmp, ng_raw, ng_cmp, nch, gp;
+  bool bitmap;
+};
+KvSizes kv_sizes(const Params &p) {
+  KvSizes z;
+  z.nb_raw = (int32_t)(((int64_t)p.raw_pt_stride * p.page_size + 31) / 32);
+  z.nb_cmp = p.ratio > 0 ? (int32_t)(((int64_t)p.cmp_pt_stride * p.page_size + 31) / 32) : 0;
+  z.ng_raw = (z.nb_raw + 3) / 4;
+  z.ng_cmp = (z.nb_cmp + 3) / 4;
+  z.nch = (p.num_queries + kKvQ - 1) / kKvQ;
+  z.gp = (p.group + 63) / 64 * 64;
+  z.bitmap = p.ratio > 0 && p.topk > 0;
+  return z;
+}
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+bool backward_kv_eligible(const Params &p) {
+  if (!backward_eligible(p) || p.query_seq == nullptr || p.query_pos == nullptr) return false;
+  const KvSizes z = kv_sizes(p);
+  return (!z.bitmap || z.nb_cmp <= kBmWords) &&
+         (int64_t)p.num_seqs * (z.ng_raw + z.ng_cmp) * p.hkv * ((z.nch + 7) / 8 * 8) <= 0x7FFFFFFFLL;
+}
+
+size_t backward_kv_workspace(const Params &p, void *base, BwdKvPlan *pl, BwdParams *b) {
+  const KvSizes z = kv_sizes(p);
+  const size_t heads = (size_t)p.num_queries * p.hkv * z.gp;
+  const size_t n_bm = z.bitmap ? (size_t)p.num_queries * z.nb_cmp : 0;
+  const size_t cap_extra = z.bitmap ? (size_t)p.num_queries * p.topk : 0;
+  size_t at = up256((size_t)p.num_queries * p.hq * sizeof(float));  // the sink partials
+  const size_t o_lse = at;
+  at += up256(heads * sizeof(float));
+  const size_t o_delta = at;
+  at += up256(heads * sizeof(float));
+  const size_t o_bm = at;
+  at += up256(n_bm * sizeof(uint32_t));
+  const size_t o_n = at;
+  at += 256;
+  const size_t o_extra = at;
+  at += up256(cap_extra * sizeof(int2));
+  if (base != nullptr) {
+    uint8_t *w = static_cast<uint8_t *>(base);
+    pl->nb_raw = z.nb_raw;
+    pl->nb_cmp = z.nb_cmp;
+    pl->ng_raw = z.ng_raw;
+    pl->ng_cmp = z.ng_cmp;
+    pl->nch = z.nch;
+    pl->bitmap = reinterpret_cast<uint32_t *>(w + o_bm);
+    pl->n_extra = reinterpret_cast<int32_t *>(w + o_n);
+    pl->extra = reinterpret_cast<int2 *>(w + o_extra);
+    pl->cap_extra = (int32_t)std::min<size_t>(cap_extra, 0x7FFFFFFF);
+    b->lse2_ws = reinterpret_cast<float *>(w + o_lse);
+    b->delta_ws = reinterpret_cast<float *>(w + o_delta);
+    b->gp = z.gp;
+  }
+  return at;
+}
+
+hipError_t launch_backward(const Params &p, const BwdParams &b, bool pairs, const BwdKvPlan *kv,
+                           hipStream_t stream) {
   if (!backward_eligible(p) || (pairs && !backward_pairs_eligible(p))) return hipErrorInvalidValue;
+  if (kv != nullptr && (!backward_kv_eligible(p) || b.lse2_ws == nullptr)) return hipErrorInvalidValue;
   if (p.num_queries == 0) return hipSuccess;
   const int64_t hblocks = (p.group + 63) / 64;
+  hipError_t e = hipSuccess;
+  if (kv != nullptr && p.ratio > 0 && p.topk > 0) {
+    // the listed groups' bitmaps and the extras list
+    hipLaunchKernelGGL(bwd_extras_zero_kernel, dim3(1), dim3(64), 0, stream, kv->n_extra);
+    hipLaunchKernelGGL(bwd_bitmap_kernel, dim3((unsigned)p.num_queries), dim3(256), 0, stream, p, *kv);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (pairs) {
     const int64_t blocks = (int64_t)((p.num_queries + 1) / 2) * p.hkv * hblocks;
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_bwd_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, p, b);
+    if (kv != nullptr)
+      hipLaunchKernelGGL((attn_bwd_kernel<2, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p, b);
+    else
+      hipLaunchKernelGGL((attn_bwd_kernel<2, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p, b);
   } else {
     const int64_t blocks = (int64_t)p.num_queries * p.hkv * hblocks;
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_bwd_kernel<1>, dim3((unsigned)blocks), dim3(128), 0, stream, p, b);
+    if (kv != nullptr)
+      hipLaunchKernelGGL((attn_bwd_kernel<1, false>), dim3((unsigned)blocks), dim3(128), 0, stream, p, b);
+    else
+      hipLaunchKernelGGL((attn_bwd_kernel<1, true>), dim3((unsigned)blocks), dim3(128), 0, stream, p, b);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (kv != nullptr && kv->ng_raw + kv->ng_cmp > 0) {
+    const int64_t blocks = (int64_t)p.num_seqs * (kv->ng_raw + kv->ng_cmp) * p.hkv * ((kv->nch + 7) / 8 * 8);
+    hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, b, *kv);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (b.dsink != nullptr && b.dsink_part != nullptr) {
     hipLaunchKernelGGL(sink_reduce_kernel, dim3((unsigned)p.hq), dim3(256), 0, stream, b.dsink_part, p.num_queries,
                        p.hq, b.dsink);

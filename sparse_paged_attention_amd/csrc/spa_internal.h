@@ -97,11 +97,33 @@ struct BwdParams {
   float *dsink_part;                  // [Nq, Hq] scratch, or null (no sink gradient)
   float *dsink;                       // [Hq], or null
   float scale;
+  float *lse2_ws, *delta_ws;          // [Nq, Hkv, gp] LSE log2(e) and Delta per head, or null
+  int32_t gp;                         // heads per KV head padded to 32
+};
+
+// Work plan of the KV-block pass (dK and dV summed per block of 32 rows of
+// one sequence's raw or compressed rows, four blocks per workgroup, over
+// slices of the queries).  Carved from the caller's workspace by
+// backward_kv_workspace.
+struct BwdKvPlan {
+  int32_t nb_raw, nb_cmp;             // blocks per sequence
+  int32_t ng_raw, ng_cmp;             // groups of four blocks per sequence
+  int32_t nch;                        // query slices
+  uint32_t *bitmap;                   // [Nq, nb_cmp] listed groups (top-k layers)
+  int32_t *n_extra;                   // repeated listings: count
+  int2 *extra;                        // and (query, group) entries
+  int32_t cap_extra;
 };
 bool backward_eligible(const Params &p);
+// the KV-block path: a prefill call (D 128, bf16 caches) whose compressed
+// blocks per sequence fit the plan's bitmap
+bool backward_kv_eligible(const Params &p);
+// Workspace bytes of the KV-block path (the sink partials included); with
+// base non-null, also carves `pl` and the LSE / Delta arrays of `b` from it.
+size_t backward_kv_workspace(const Params &p, void *base, BwdKvPlan *pl, BwdParams *b);
 // query pairs (four waves, the union of two KV sets): a prefill call with a
 // top-k list or no compressed part and 2 * (topk + window) <= kPairRowsMax
 bool backward_pairs_eligible(const Params &p);
-hipError_t launch_backward(const Params &p, const BwdParams &b, bool pairs, hipStream_t stream);
+hipError_t launch_backward(const Params &p, const BwdParams &b, bool pairs, const BwdKvPlan *kv, hipStream_t stream);
 
 }  // namespace spa

@@ -38,7 +38,7 @@ def _dO(p, seed):
     return synth.f32_to_bf16_bits(rng.standard_normal(p.q.shape).astype(np.float32))
 
 
-def _run(p, dO_bits, want_dsink=True, repeat=1, qpb=0):
+def _run(p, dO_bits, want_dsink=True, repeat=1, qpb=0, fused=False):
     from sparse_paged_attention_amd import api
     dp = api.DeviceProblem.from_problem(p)
     o, lse = api.forward(dp)
@@ -46,7 +46,8 @@ def _run(p, dO_bits, want_dsink=True, repeat=1, qpb=0):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     g = None
     for _ in range(repeat):
-        g = api.backward(dp, o, lse, d_o, err_flag=err, want_dsink=want_dsink, grads=g, queries_per_block=qpb)
+        g = api.backward(dp, o, lse, d_o, err_flag=err, want_dsink=want_dsink, grads=g, queries_per_block=qpb,
+                         fused=fused)
     torch.cuda.synchronize()
     out = {k: (None if v is None else v.cpu().numpy().astype(np.float64)) for k, v in g.items()
            if not k.startswith("_")}
@@ -115,11 +116,11 @@ def _close(name, got, ref, bound):
         announce(f"  {name}: max |err| / bound = {np.max(np.abs(got - ref)[nz] / bound[nz]):.3f}")
 
 
-def _check(p, label, seed=1, want_dsink=True, repeat=1, qpb=0):
+def _check(p, label, seed=1, want_dsink=True, repeat=1, qpb=0, fused=False):
     announce(f"backward {label}: Nq={p.num_queries} Hq={p.num_q_heads} Hkv={p.num_kv_heads} "
-             f"ratio={p.ratio} topk={p.topk} W={p.window} qpb={qpb}")
+             f"ratio={p.ratio} topk={p.topk} W={p.window} qpb={qpb} fused={fused}")
     dO = _dO(p, seed)
-    got, err = _run(p, dO, want_dsink, repeat, qpb)
+    got, err = _run(p, dO, want_dsink, repeat, qpb, fused)
     ref = attention_backward(p, dO)
     bd = _bounds(p, dO)
     _close("dq", got["dq"], ref.dq, bd["dq"])
@@ -131,12 +132,15 @@ def _check(p, label, seed=1, want_dsink=True, repeat=1, qpb=0):
     return err
 
 
-@pytest.mark.parametrize("qpb", [0, 1])
-def test_backward_prefill_csa(qpb):
-    """Query pairs (the library's choice here) and one query per workgroup."""
+@pytest.mark.parametrize("qpb,fused", [(0, False), (1, False), (0, True), (1, True)])
+def test_backward_prefill_csa(qpb, fused):
+    """Query pairs (the library's choice here) and one query per workgroup,
+    each with dK and dV from the KV-block pass (the workspace the library
+    asks for) or from the fused kernel's atomics (a workspace that holds
+    only the sink partials)."""
     p = synth.make_problem("bwd_csa", "prefill", [1500], 64, 1, 128, 16, 128, 4, 256, seed=81,
                            query_positions=[(0, t) for t in range(1400, 1464)], selection="score")
-    assert _check(p, "prefill csa", qpb=qpb) == 0
+    assert _check(p, "prefill csa", qpb=qpb, fused=fused) == 0
 
 
 def test_backward_pairs_across_sequences_and_odd_count():
@@ -151,8 +155,9 @@ def test_backward_pairs_across_sequences_and_odd_count():
 
 def test_backward_group_listed_twice_pairs_match_single():
     """A list that names a group twice is outside the oracle's contract;
-    both backward layouts count the entry twice, as the forward does (the
-    pair path falls back to the two lists one after the other)."""
+    every backward path counts the entry twice, as the forward does (the
+    pair path falls back to the two lists one after the other; the
+    KV-block pass takes the repeat as an extra item)."""
     from sparse_paged_attention_amd import api
     p = synth.make_problem("bwd_dup", "prefill", [700], 64, 1, 128, 16, 64, 4, 32, seed=90,
                            query_positions=[(0, t) for t in range(600, 608)], selection="random")
@@ -162,14 +167,15 @@ def test_backward_group_listed_twice_pairs_match_single():
     d_o = torch.from_numpy(_dO(p, 3).view(np.int16)).cuda().view(torch.bfloat16)
     announce("backward: a group listed twice, pairs vs single")
     res = []
-    for qpb in (2, 1):
-        g = api.backward(dp, o, lse, d_o, queries_per_block=qpb)
+    for qpb, fused in ((2, False), (1, False), (1, True), (2, True)):
+        g = api.backward(dp, o, lse, d_o, queries_per_block=qpb, fused=fused)
         torch.cuda.synchronize()
         res.append({k: v.cpu().numpy() for k, v in g.items() if v is not None and not k.startswith("_")})
-    for k in res[0]:
-        a, b = res[0][k], res[1][k]
-        scale = float(np.max(np.abs(b))) or 1.0
-        assert np.max(np.abs(a - b)) <= 1e-5 * scale, k
+    for other in res[1:]:
+        for k in res[0]:
+            a, b = res[0][k], other[k]
+            scale = float(np.max(np.abs(b))) or 1.0
+            assert np.max(np.abs(a - b)) <= 1e-5 * scale, k
 
 
 def test_backward_decode_two_head_blocks():
@@ -241,6 +247,7 @@ def test_backward_short_lists_and_bad_ids_flagged():
 
 def test_backward_full_prefill_csa():
     """The workload bench.py times (prefill CSA, 2560 queries), every
-    element against the oracle under the same bound."""
+    element against the oracle under the same bound, on the path bench.py
+    times (the KV-block pass)."""
     p = synth.make_workload("prefill_csa")
     assert _check(p, "prefill_csa full", seed=5) == 0
