@@ -64,7 +64,11 @@ constexpr int kTileB = kPT * kRowB;
 constexpr int kBRows = 512;                // rows translated per chunk (one query per workgroup)
 constexpr int kPairRows = kPairRowsMax;    // rows of a query pair's list (one chunk)
 constexpr int kBmWords = 1024;             // bitmap words per query: groups < 32768
-constexpr int kBStages = 2;
+// K and V tile stages: two with the dK and dV part (its atomics share the
+// load counter); three without it, two tiles' loads in flight and two
+// workgroups per CU, so one's setup runs under the other's tiles
+template <bool DKV>
+constexpr int kBStages = DKV ? 2 : 3;
 constexpr int64_t kCmpBit = int64_t(1) << 62;
 
 // NQ queries per workgroup (1, or 2 for a prefill query pair); 2 NQ waves,
@@ -75,8 +79,8 @@ struct BwdSmem {
   static constexpr int kRows = NQ == 1 ? kBRows : kPairRows;
   union {
     struct {
-      alignas(16) uint8_t k[kBStages][kTileB];
-      alignas(16) uint8_t v[kBStages][kTileB];
+      alignas(16) uint8_t k[kBStages<DKV>][kTileB];
+      alignas(16) uint8_t v[kBStages<DKV>][kTileB];
     } t;
     uint32_t bm[2][kBmWords];              // query pair setup: each query's selected groups
   } u;
@@ -232,7 +236,7 @@ __device__ int32_t pair_rows(const Params &p, Smem &sm, int32_t i0, int32_t i1, 
 }
 
 template <int NQ, bool DKV>
-__global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams b) {
+__global__ __launch_bounds__(128 * NQ, DKV ? 1 : 2) void attn_bwd_kernel(Params p, BwdParams b) {
   constexpr int NT = 128 * NQ;
   constexpr int NW = 2 * NQ;                 // waves
   constexpr int kRowsPerWave = kPT / NW;     // tile rows each wave loads
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams 
     const int32_t ntiles = (n + kPT - 1) / kPT;
 
     auto issue = [&](int j) {
-      const int st = j % kBStages;
+      const int st = j % kBStages<DKV>;
 #pragma unroll
       for (int q4 = 0; q4 < kRowsPerWave / 4; ++q4) {
         const int rr = kRowsPerWave * wave + 4 * q4;
@@ -408,33 +412,65 @@ __global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams 
       else return ((sm.flg[r] >> qw) & 1u) != 0;
     };
 
-    issue(0);
+    constexpr int NS = kBStages<DKV>;
+    constexpr int kLoads = 2 * (kRowsPerWave / 4);   // this wave's direct loads per tile
+    for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t);
     for (int j = 0; j < ntiles; ++j) {
       // tile j is in (this wave's loads, then everyone's), and every wave is
-      // done with tile j-1, whose stage the next loads refill; the wait also
-      // covers the previous tile's atomics
-      wait_vmcnt<0>();
+      // done with tile j-1, whose stage the next loads refill.  With dK and
+      // dV the wait also covers the previous tile's atomics; without, the
+      // loads of the tiles after j stay in flight
+      if constexpr (DKV) {
+        wait_vmcnt<0>();
+      } else {
+        const int pending = min(NS - 2, ntiles - 1 - j);
+        if (pending >= 4) wait_vmcnt<4 * kLoads>();
+        else if (pending == 3) wait_vmcnt<3 * kLoads>();
+        else if (pending == 2) wait_vmcnt<2 * kLoads>();
+        else if (pending == 1) wait_vmcnt<kLoads>();
+        else wait_vmcnt<0>();
+      }
       block_sync();
-      if (j + 1 < ntiles) issue(j + 1);
-      const int st = j % kBStages;
+      if (j + NS - 1 < ntiles) issue(j + NS - 1);
+      const int st = j % NS;
       const uint8_t *Kt = sm.u.t.k[st];
       const uint8_t *Vt = sm.u.t.v[st];
       const bool lvalid = in_set(kPT * j + (lane & 31));
       const uint32_t tm = (uint32_t)__ballot(lane < 32 && lvalid);
 
-      // scores and dP in both orientations
+      // scores and dP in both orientations (without dK and dV, the head-
+      // column ones only)
       f32x16 s_rh = f32x16{}, s_hr = f32x16{}, dp_rh = f32x16{}, dp_hr = f32x16{};
+      bf16x8 ktf[kD / 32][2];                // K^T fragments of dQ^T += K^T dS^T
+      if constexpr (DKV) {
 #pragma unroll
-      for (int kk = 0; kk < kD / 16; ++kk) {
-        const bf16x8 kf = row_frag(Kt, lane, kk);
-        s_rh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s_rh, 0, 0, 0);
-        if constexpr (DKV) s_hr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kf, s_hr, 0, 0, 0);
-      }
+        for (int kk = 0; kk < kD / 16; ++kk) {
+          const bf16x8 kf = row_frag(Kt, lane, kk);
+          s_rh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s_rh, 0, 0, 0);
+          s_hr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kf, s_hr, 0, 0, 0);
+        }
 #pragma unroll
-      for (int kk = 0; kk < kD / 16; ++kk) {
-        const bf16x8 vf = row_frag(Vt, lane, kk);
-        dp_rh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[kk], dp_rh, 0, 0, 0);
-        if constexpr (DKV) dp_hr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dof[kk], vf, dp_hr, 0, 0, 0);
+        for (int kk = 0; kk < kD / 16; ++kk) {
+          const bf16x8 vf = row_frag(Vt, lane, kk);
+          dp_rh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[kk], dp_rh, 0, 0, 0);
+          dp_hr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dof[kk], vf, dp_hr, 0, 0, 0);
+        }
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) ktf[db][k2] = tr_frag(Kt, lane, db, k2);
+      } else {
+        // two workgroups share each CU, so one's fragment reads run under
+        // the other's products; S and dP alternate
+#pragma unroll
+        for (int kk = 0; kk < kD / 16; ++kk) {
+          s_rh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Kt, lane, kk), qf[kk], s_rh, 0, 0, 0);
+          dp_rh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Vt, lane, kk), dof[kk], dp_rh, 0, 0, 0);
+        }
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) ktf[db][k2] = tr_frag(Kt, lane, db, k2);
       }
       // head-column layout: value r is row 8(r/4) + 4hi + r%4 of the tile
       bf16x8 dsb[2];
@@ -449,7 +485,7 @@ __global__ __launch_bounds__(128 * NQ) void attn_bwd_kernel(Params p, BwdParams 
       for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
-          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Kt, lane, db, k2), dsb[k2], dqa[db], 0, 0, 0);
+          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[db][k2], dsb[k2], dqa[db], 0, 0, 0);
       if constexpr (!DKV) continue;
       // row-column layout: value r is head 8(r/4) + 4hi + r%4 of the wave
       bf16x8 pb[2], dsh[2];
