@@ -505,8 +505,8 @@ def run_topk(workload, *, steps=200, warmup=20, cpu_budget=0.0, eager_only=False
                                                         else "graph replay of the step (one kernel)"),
                      "algorithmic_bytes_per_launch": read_b + write_b},
         "cpu_baseline": cpu,
-    } | {"_traffic": measured_traffic(workload, {"rows": rows, "k": k, "order": order}, TOPK_SOURCES,
-                                      ("rows", "k", "order"))}
+    } | {"_traffic": measured_traffic(workload if order == "score" else f"{workload}.id",
+                                      {"rows": rows, "k": k, "order": order}, TOPK_SOURCES, ("rows", "k", "order"))}
 
 
 def run_backward(workload, *, steps=20, warmup=3, cpu_budget=0.0, rotate_mb=640.0, eager_only=False):
