@@ -67,7 +67,10 @@ def attention_kernel(p, splits, hpb, qpb, cus=256):
         return "attn_pair_kernel<3>"
     rows_wgs = p.num_queries * p.num_kv_heads * -(-(p.num_q_heads // p.num_kv_heads) // 32)
     if decode_ok and S == 1 and rows_wgs <= cus:
-        return "attn_decode_rows_kernel<true>" if p.cmp_fp8 else "attn_decode_rows_kernel<false>"
+        if p.cmp_fp8:
+            return "attn_decode_rows_kernel<true, false>"
+        # bf16 pages and room for twice the workgroups: each forms half of O's dimensions
+        return "attn_decode_rows_kernel<false, true>" if 2 * rows_wgs <= cus else "attn_decode_rows_kernel<false, false>"
     if decode_ok:
         return "attn_decode_kernel<true>" if p.cmp_fp8 else "attn_decode_kernel<false>"
     return "attn_fwd_kernel"

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(128 * NQ, DKV ? 1 : 2) void attn_bwd_kernel(Params 
   __shared__ BwdSmem<NQ, DKV> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qw = wave >> 1;                  // the wave's query (0 with one query per workgroup)
   const int hw = wave & 1;                   // the wave's head half
   const int hi = lane >> 5;
@@ -396,10 +396,15 @@ __global__ __launch_bounds__(128 * NQ, DKV ? 1 : 2) void attn_bwd_kernel(Params 
 
     auto issue = [&](int j) {
       const int st = j % kBStages<DKV>;
+      // every row first: the loads' memory clobber keeps a later LDS read
+      // from starting ahead of them
+      int64_t ers[kRowsPerWave / 4];
+#pragma unroll
+      for (int q4 = 0; q4 < kRowsPerWave / 4; ++q4) ers[q4] = sm.row[kPT * j + kRowsPerWave * wave + 4 * q4 + lane / kChunks];
 #pragma unroll
       for (int q4 = 0; q4 < kRowsPerWave / 4; ++q4) {
         const int rr = kRowsPerWave * wave + 4 * q4;
-        const int64_t er = sm.row[kPT * j + rr + lane / kChunks];
+        const int64_t er = ers[q4];
         const bool cmp = (er & kCmpBit) != 0;
         const int64_t off = (er & ~kCmpBit) * kRowB + csrc[q4];
         dma16(er >= 0 ? (cmp ? kcmp : kraw) + off : kZeroRow + csrc[q4], sm.u.t.k[st] + rr * kRowB);

@@ -95,7 +95,7 @@ void attn_decode_kernel(const Params p) {
   __shared__ DecodeSmem<FP8> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
   const int32_t S = p.num_splits;
 
@@ -237,13 +237,15 @@ void attn_decode_kernel(const Params p) {
   auto issue = [&](int j) {
     const int st = j % NST;
     if (FP8 && j < nf8) {
+      // both rows first: the loads' memory clobber keeps a later LDS read
+      // from starting ahead of them
       const int64_t er = sm.row[kPT * j + 8 * wave + lane / 8];
+      const int64_t es = wave == 0 ? sm.row[kPT * j + (lane & 31)] : -1;
       const int64_t off = (er & ~kCmpBit) * kD + (lane % 8) * 16;
       uint8_t *dst = sm.f8[FP8 ? st : 0] + wave * 1024;
       dma16(er >= 0 ? kcmp + off : kZeroRow + (lane % 8) * 16, dst);
       dma16(er >= 0 ? vcmp + off : kZeroRow + (lane % 8) * 16, dst + kF8TileB);
       if (wave == 0) {
-        const int64_t es = sm.row[kPT * j + (lane & 31)];
         const float *scl = lane < 32 ? p.k_cmp_scale : p.v_cmp_scale;
         dma4(es >= 0 ? (const void *)(scl + (es & ~kCmpBit)) : (const void *)(kZeroRow + 4 * (lane & 31)),
              sm.f8s[FP8 ? st : 0]);

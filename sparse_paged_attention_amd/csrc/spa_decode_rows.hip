@@ -54,37 +54,57 @@ constexpr int kPtLds = 2048;               // page-table entries staged in LDS
 constexpr int kWSt = 2;                    // LDS stages per wave
 constexpr int64_t kCmpBit = int64_t(1) << 62;
 
+// DH: the workgroup forms one half of O's dimensions and stages only that
+// half of each V row (128 bytes).
+// DH also gives each wave three stages (two tiles' loads in flight while
+// it computes one); the list and page-table rows, read only while the rows
+// are formed, share the stages' memory.
+template <bool DH>
 struct RowsSmem {
+  static constexpr int kVRowB = DH ? kRowB / 2 : kRowB;
+  static constexpr int kOD = DH ? kD / 2 : kD;        // output dimensions of the workgroup
+  static constexpr int kSt = DH ? 3 : kWSt;           // LDS stages per wave
   union {
     struct {
-      alignas(16) uint8_t k[kWaves][kWSt][kTileB];
-      alignas(16) uint8_t v[kWaves][kWSt][kTileB];
+      alignas(16) uint8_t k[kWaves][kSt][kTileB];
+      alignas(16) uint8_t v[kWaves][kSt][kPT * kVRowB];
     } t;
-    alignas(16) float acc[kWaves][kD / 32][16][64];   // the waves' O^T: [wave][d block][value][lane]
+    struct {
+      alignas(16) int32_t ids[kRowsMax];    // the list row
+      alignas(16) int32_t pt[kPtLds];       // raw page-table row, then the compressed one
+    } s;
+    alignas(16) float acc[kWaves][kOD / 32][16][64];   // the waves' O^T: [wave][d block][value][lane]
   } u;
   alignas(16) float f8s[kWaves][kWSt][64];  // e4m3 tiles: 32 k scales, then 32 v scales
   alignas(16) int64_t row[kRowsMax];        // pool rows, padded to whole tiles
-  alignas(16) int32_t ids[kRowsMax];        // the list row
-  alignas(16) int32_t pt[kPtLds];           // raw page-table row, then the compressed one
   float mw[kWaves][64];                     // the waves' m and l per lane
   float lw[kWaves][64];
 };
 
-template <bool FP8>
+template <bool FP8, bool DH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void attn_decode_rows_kernel(const Params p) {
-  __shared__ RowsSmem sm;
+  static_assert(!(FP8 && DH), "e4m3 tiles widen whole rows");
+  using Smem = RowsSmem<DH>;
+  constexpr int kVRowB = Smem::kVRowB;
+  constexpr int kVChunks = kVRowB / 16;
+  constexpr int kOD = Smem::kOD;
+  __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
 
-  // workgroup -> (unit u = query * Hkv + KV head, head block hb): the head
-  // blocks of a unit share the workgroup index mod 8, hence the XCD
+  // workgroup -> (unit u = query * Hkv + KV head, head block hb, dimension
+  // half dh): the workgroups of a unit share the workgroup index mod 8,
+  // hence the XCD
   const int32_t nhb = (p.group + kHeads - 1) / kHeads;
   const int32_t units = p.num_queries * p.hkv;
-  const int32_t y = (int32_t)(blockIdx.x >> 3);
+  const int32_t y0 = (int32_t)(blockIdx.x >> 3);
+  const int32_t dh = DH ? (y0 & 1) : 0;
+  const int32_t y = DH ? (y0 >> 1) : y0;
   const int32_t hb = y % nhb;
+  const bool lead = hb == 0 && dh == 0;      // raises the error bits
   const int32_t u = (y / nhb) * 8 + (int32_t)(blockIdx.x & 7);
   if (u >= units) return;                    // padding of the grid to whole groups of 8
   const int32_t g = u % p.hkv;
@@ -100,7 +120,7 @@ void attn_decode_rows_kernel(const Params p) {
   if (topk > 0) {
     for (int c = wave; 64 * c < topk; c += kWaves) {
       const int e = 64 * c + lane;
-      dma4(e < topk ? (const void *)(p.cmp_idx + (int64_t)i * topk + e) : (const void *)kZeroRow, &sm.ids[64 * c]);
+      dma4(e < topk ? (const void *)(p.cmp_idx + (int64_t)i * topk + e) : (const void *)kZeroRow, &sm.u.s.ids[64 * c]);
     }
   }
   const int32_t nr = p.raw_pt_stride;
@@ -112,7 +132,7 @@ void attn_decode_rows_kernel(const Params p) {
       const void *src = k < nr        ? (const void *)(p.raw_pt + (int64_t)b * nr + k)
                         : k < nr + nc ? (const void *)(p.cmp_pt + (int64_t)b * nc + (k - nr))
                                       : (const void *)kZeroRow;
-      dma4(src, &sm.pt[64 * c]);
+      dma4(src, &sm.u.s.pt[64 * c]);
     }
   }
   const int hl = hb * kHeads + (lane & 31);  // head within the KV group
@@ -132,11 +152,11 @@ void attn_decode_rows_kernel(const Params p) {
   block_sync();                              // list and page-table rows in LDS
   const int32_t len_b = __builtin_amdgcn_readfirstlane(meta);
   const int32_t cnt_i = has_list ? __builtin_amdgcn_readlane(meta, 1) : 0;
-  const QueryKV kv = query_kv_of(p, b, len_b - 1, len_b, cnt_i, tid == 0 && hb == 0);
+  const QueryKV kv = query_kv_of(p, b, len_b - 1, len_b, cnt_i, tid == 0 && lead);
 
   // ---- the rows: the selected groups, then (from the next tile edge with
   // e4m3 pages) the window
-  if (topk == 0 && kv.n_sel > cap && tid == 0 && hb == 0) flag_error(p, kErrPage);   // groups past the table
+  if (topk == 0 && kv.n_sel > cap && tid == 0 && lead) flag_error(p, kErrPage);   // groups past the table
   const int32_t Uc = (int32_t)min((int64_t)kv.n_sel, cap);
   const int32_t wbase = FP8 ? round_up(Uc, kPT) : Uc;  // first window row
   const int32_t U = min(wbase + kv.win_len, kRowsMax);
@@ -148,32 +168,32 @@ void attn_decode_rows_kernel(const Params p) {
       const bool cmp = r < Uc;
       int32_t x = -1, col = -1;
       if (r < U && (r < Uc || r >= wbase)) {
-        x = cmp ? (topk > 0 ? sm.ids[r] : r) : kv.win_lo + (r - wbase);
+        x = cmp ? (topk > 0 ? sm.u.s.ids[r] : r) : kv.win_lo + (r - wbase);
         if (cmp && (x < 0 || x >= kv.n_c)) {
-          if (hb == 0) flag_error(p, kErrCmpId);
+          if (lead) flag_error(p, kErrCmpId);
           x = -1;
         }
         if (x >= 0) {
           col = pow2 ? x >> p.page_shift : x / P;
           if (col >= (cmp ? nc : nr)) {
-            if (hb == 0) flag_error(p, kErrPage);
+            if (lead) flag_error(p, kErrPage);
             x = -1;
           }
         }
       }
       int64_t er = -1;
       if (x >= 0) {
-        const int32_t page = stage_pt ? sm.pt[cmp ? nr + col : col]
+        const int32_t page = stage_pt ? sm.u.s.pt[cmp ? nr + col : col]
                                       : (cmp ? p.cmp_pt + (int64_t)b * nc : p.raw_pt + (int64_t)b * nr)[col];
         if (page >= 0 && (int64_t)page < (cmp ? p.cmp_pages : p.raw_pages))
           er = (((int64_t)page * P + (x - col * P)) * p.hkv + g) | (cmp ? kCmpBit : 0);
-        else if (hb == 0)
+        else if (lead)
           flag_error(p, kErrPage);
       }
       sm.row[r] = er;
     }
   }
-  block_sync();                              // rows in LDS
+  block_sync();                              // rows in LDS; the list and page-table rows are dead
 
   // ---- this wave's tiles: j = wave + 4t, stage t % 2
   const uint8_t *const kraw = in_sgpr(p.k_raw), *const vraw = in_sgpr(p.v_raw);
@@ -181,15 +201,20 @@ void attn_decode_rows_kernel(const Params p) {
   const int32_t ntw = T > wave ? (T - wave + kWaves - 1) / kWaves : 0;
   auto tile_of = [&](int t) { return wave + kWaves * t; };
   auto is_f8 = [&](int t) { return FP8 && tile_of(t) < nf8; };
+  constexpr int NST = Smem::kSt;
   auto issue = [&](int t) {
     const int j = tile_of(t);
-    const int st = t % kWSt;
+    const int st = t % NST;
+    // every row of the tile is read before the first load: the loads' memory
+    // clobber keeps a later LDS read from starting ahead of them
     if (FP8 && j < nf8) {
       // e4m3: 8 rows of 128 bytes per load into the upper half of the stage
+      int64_t e8[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) e8[n] = sm.row[kPT * j + 8 * n + lane / 8];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int r = 8 * n + lane / 8;
-        const int64_t er = sm.row[kPT * j + r];
+        const int64_t er = e8[n];
         const int64_t off = (er & ~kCmpBit) * kD + (lane % 8) * 16;
         const uint8_t *z = kZeroRow + (lane % 8) * 16;
         dma16(er >= 0 ? kcmp + off : z, sm.u.t.k[wave][st] + kTileB / 2 + 8 * n * kD);
@@ -201,39 +226,63 @@ void attn_decode_rows_kernel(const Params p) {
            sm.f8s[wave][st]);
       return;
     }
+    int64_t ek[8], ev[4];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) ek[n] = sm.row[kPT * j + 4 * n + lane / kChunks];
+    if constexpr (DH) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) ev[n] = sm.row[kPT * j + 8 * n + lane / kVChunks];
+    }
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const int r = 4 * n + lane / kChunks;
-      const int64_t er = sm.row[kPT * j + r];
+      const int64_t er = ek[n];
       const int cs = ((lane % kChunks) ^ swz<kChunks>(r)) * 16;
       const bool cmp = (er & kCmpBit) != 0;
       const int64_t off = (er & ~kCmpBit) * kRowB + cs;
       dma16(er >= 0 ? (cmp ? kcmp : kraw) + off : kZeroRow + cs, sm.u.t.k[wave][st] + 4 * n * kRowB);
-      dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + cs, sm.u.t.v[wave][st] + 4 * n * kRowB);
+      if constexpr (!DH)
+        dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + cs, sm.u.t.v[wave][st] + 4 * n * kRowB);
+    }
+    if constexpr (DH) {
+      // the workgroup's half of each V row: 8 rows of 128 bytes per load
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int r = 8 * n + lane / kVChunks;
+        const int64_t er = ev[n];
+        const int cs = ((lane % kVChunks) ^ swz<kVChunks>(r)) * 16;
+        const bool cmp = (er & kCmpBit) != 0;
+        const int64_t off = (er & ~kCmpBit) * kRowB + kVRowB * dh + cs;
+        dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + cs, sm.u.t.v[wave][st] + 8 * n * kVRowB);
+      }
     }
   };
+  constexpr int kLoads = DH ? 12 : 16;       // direct loads of a bf16 tile
   const bool fnuz = FP8 && p.cmp_fnuz != 0;
 
   float m = sink == -INFINITY ? -INFINITY : sink * kLog2e;
   float l = (sink != -INFINITY && hi == 0) ? 1.f : 0.f;   // exp2(sink - m) = 1, counted once per head
-  f32x16 acc[kD / 32];
+  f32x16 acc[kOD / 32];
 #pragma unroll
-  for (int db = 0; db < kD / 32; ++db) acc[db] = f32x16{};
+  for (int db = 0; db < kOD / 32; ++db) acc[db] = f32x16{};
 
   if (ntw > 0) issue(0);
   if (ntw > 1) issue(1);
   for (int t = 0; t < ntw; ++t) {
     const int j = tile_of(t);
-    const int st = t % kWSt;
+    const int st = t % NST;
     const bool f8 = is_f8(t);
     // this wave's loads of tile j are complete (those of its next tile may
     // still be in flight: 16, or 9 for an e4m3 tile)
     if (t + 1 < ntw) {
       if (is_f8(t + 1)) wait_vmcnt<9>();
-      else wait_vmcnt<16>();
+      else wait_vmcnt<kLoads>();
     } else {
       wait_vmcnt<0>();
     }
+    // three stages: tile t+2 takes the stage of tile t-1, whose LDS reads
+    // are complete, and loads while tile t computes
+    if (NST == 3 && t + 2 < ntw) issue(t + 2);
     uint8_t *Kt = sm.u.t.k[wave][st];
     uint8_t *Vt = sm.u.t.v[wave][st];
     if (FP8 && f8) {
@@ -268,12 +317,12 @@ void attn_decode_rows_kernel(const Params p) {
         kf[kk] = *(const bf16x8 *)(Kt + r * kRowB + ((c ^ swz<kChunks>(r)) * 16));
       }
     }
-    i16x8 vf[kD / 32][2];
+    i16x8 vf[kOD / 32][2];
     {
       const int G = lane >> 4;
       const int L = lane & 15;
 #pragma unroll
-      for (int db = 0; db < kD / 32; ++db)
+      for (int db = 0; db < kOD / 32; ++db)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           i16x4 h[2];
@@ -281,7 +330,7 @@ void attn_decode_rows_kernel(const Params p) {
           for (int rw = 0; rw < 2; ++rw) {
             const int row = 16 * k2 + 8 * rw + 4 * (G >> 1) + (L >> 2);
             const int d = 32 * db + 16 * (G & 1) + 4 * (L & 3);
-            const int off = row * kRowB + (((d >> 3) ^ swz<kChunks>(row)) * 16) + (L & 1) * 8;
+            const int off = row * kVRowB + (((d >> 3) ^ swz<kVChunks>(row)) * 16) + (L & 1) * 8;
             h[rw] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(Vt + off));
           }
           vf[db][k2] = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -297,9 +346,9 @@ void attn_decode_rows_kernel(const Params p) {
         vs[4 * q4] = v4.x, vs[4 * q4 + 1] = v4.y, vs[4 * q4 + 2] = v4.z, vs[4 * q4 + 3] = v4.w;
       }
     }
-    // every LDS read of the stage is in: the stage takes tile t+2
+    // every LDS read of the stage is in: with two stages it takes tile t+2
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (t + 2 < ntw) issue(t + 2);
+    if (NST == 2 && t + 2 < ntw) issue(t + 2);
 
     f32x16 s = f32x16{};
 #pragma unroll
@@ -319,7 +368,7 @@ void attn_decode_rows_kernel(const Params p) {
       m = need ? tmax : m;
       l *= alpha;
 #pragma unroll
-      for (int db = 0; db < kD / 32; ++db) acc[db] *= alpha;
+      for (int db = 0; db < kOD / 32; ++db) acc[db] *= alpha;
     }
     const float negm = m == -INFINITY ? 0.f : -m;
     bf16x8 pb[2];
@@ -330,23 +379,25 @@ void attn_decode_rows_kernel(const Params p) {
       pb[q >> 3][q & 7] = (__bf16)((FP8 && f8) ? pr * vs[q] : pr);
     }
 #pragma unroll
-    for (int db = 0; db < kD / 32; ++db)
+    for (int db = 0; db < kOD / 32; ++db)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[db][k2]), pb[k2], acc[db],
                                                          0, 0, 0);
   }
 
-  // ---- the four states meet: wave w forms dimensions 32w .. 32w+31,
+  // ---- the four states meet: wave w forms dimensions 32w .. 32w+31 of
+  // the workgroup's (two waves with half of the dimensions),
   // O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, LSE = (M + log2 L) ln 2
   block_sync();                              // every wave is done with its stages
 #pragma unroll
-  for (int db = 0; db < kD / 32; ++db)
+  for (int db = 0; db < kOD / 32; ++db)
 #pragma unroll
     for (int q = 0; q < 16; ++q) sm.u.acc[wave][db][q][lane] = acc[db][q];
   sm.mw[wave][lane] = m;
   sm.lw[wave][lane] = l;
   block_sync();
+  if (wave >= kOD / 32) return;
   float M = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kWaves; ++s) M = fmaxf(M, sm.mw[s][lane]);
@@ -366,7 +417,7 @@ void attn_decode_rows_kernel(const Params p) {
   const float lse = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
   if (!hvalid) return;
   const int64_t orow = (int64_t)i * p.hq + (int64_t)g * p.group + hl;
-  uint16_t *out = p.o + orow * kD + 32 * wave;
+  uint16_t *out = p.o + orow * kD + kOD * dh + 32 * wave;
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
     uint2 w;
@@ -374,7 +425,7 @@ void attn_decode_rows_kernel(const Params p) {
     w.y = bf16_bits(o[4 * i4 + 2] * inv) | (bf16_bits(o[4 * i4 + 3] * inv) << 16);
     *(uint2 *)(out + 8 * i4 + 4 * hi) = w;
   }
-  if (wave == 0 && hi == 0 && p.lse != nullptr) p.lse[orow] = lse;
+  if (wave == 0 && hi == 0 && dh == 0 && p.lse != nullptr) p.lse[orow] = lse;
 }
 
 }  // namespace
@@ -386,16 +437,18 @@ bool decode_rows_eligible(const Params &p) {
   return crow + p.window <= kRowsMax && (p.topk == 0 || p.topk <= kRowsMax);
 }
 
-hipError_t launch_decode_rows(const Params &p, hipStream_t stream) {
+hipError_t launch_decode_rows(const Params &p, bool halves, hipStream_t stream) {
   if (p.num_queries == 0) return hipSuccess;
-  if (!decode_rows_eligible(p)) return hipErrorInvalidConfiguration;
+  if (!decode_rows_eligible(p) || (halves && p.cmp_fp8)) return hipErrorInvalidConfiguration;
   const int64_t units = (int64_t)p.num_queries * p.hkv;
-  const int64_t grid = (units + 7) / 8 * 8 * ((p.group + kHeads - 1) / kHeads);
+  const int64_t grid = (units + 7) / 8 * 8 * ((p.group + kHeads - 1) / kHeads) * (halves ? 2 : 1);
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   if (p.cmp_fp8)
-    hipLaunchKernelGGL(attn_decode_rows_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_decode_rows_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  else if (halves)
+    hipLaunchKernelGGL((attn_decode_rows_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(attn_decode_rows_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_decode_rows_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

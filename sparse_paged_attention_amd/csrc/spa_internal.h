@@ -68,8 +68,10 @@ hipError_t launch_decode(const Params &p, hipStream_t stream);
 // Decode in one KV pass per query (spa_decode_rows.hip): D 128, one slice,
 // bf16 or e4m3 compressed pages; one workgroup per (query, KV head, block of
 // 32 query heads) whose waves split the rows, their states combined in LDS.
+// halves (bf16 pages): two workgroups per such block, each forming half of
+// O's dimensions from all of K and its half of V.
 bool decode_rows_eligible(const Params &p);
-hipError_t launch_decode_rows(const Params &p, hipStream_t stream);
+hipError_t launch_decode_rows(const Params &p, bool halves, hipStream_t stream);
 // 512-wide heads over a shared latent cache (spa_latent.hip): bf16, k_raw ==
 // v_raw and k_cmp == v_cmp; one workgroup per (query, KV head, 64-head block,
 // KV slice); with several slices it writes sink-free partials (plain order).

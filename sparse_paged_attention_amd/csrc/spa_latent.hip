@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
   __shared__ LatentSmem<FP8> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave >> 2;                  // head group
   const int dq = wave & 3;                   // dimension quarter
   const int hi = lane >> 5;
@@ -123,10 +123,15 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
   // L's chunk is logical chunk 16 (L / 16) + ((L % 16) ^ swz(row))
   auto issue = [&](int j) {
     const int st = j % kLStages;
+    // every row first: the loads' memory clobber keeps a later LDS read
+    // from starting ahead of them
+    int64_t ers[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) ers[n] = sm.row[kPT * j + 4 * wave + n];
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int r = 4 * wave + n;
-      const int64_t er = sm.row[kPT * j + r];
+      const int64_t er = ers[n];
       const int cs = (lane >> 4) * kQB + (((lane & 15) ^ swz<16>(r)) * 16);
       const bool cmp = (er & kCmpBit) != 0;
       dma16(er >= 0 ? (cmp ? kcmp : kraw) + (er & ~kCmpBit) * kRowB + cs : kZeroRow + (cs & (kQB - 1)),
@@ -139,15 +144,18 @@ __global__ __launch_bounds__(kLThreads) void attn_latent_kernel(Params p) {
   // also loads the 32 scales
   auto issue_f8 = [&](int j) {
     const int st = j % kLStages;
+    int64_t ers[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) ers[n] = sm.row[kPT * j + 4 * wave + 2 * n + (lane >> 5)];
+    const int64_t es = (wave == 0 && lane < kPT) ? sm.row[kPT * j + lane] : -1;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      const int r = 4 * wave + 2 * n + (lane >> 5);
-      const int64_t er = sm.row[kPT * j + r];
+      const int64_t er = ers[n];
       dma16(er >= 0 ? kcmp + (er & ~kCmpBit) * kD + (lane & 31) * 16 : kZeroRow + (lane & 15) * 16,
             sm.kv[st] + kF8Off + (4 * wave + 2 * n) * kD);
     }
     if (wave == 0) {
-      const int64_t er = lane < kPT ? sm.row[kPT * j + lane] : -1;
+      const int64_t er = es;
       dma4(er >= 0 ? (const void *)(kscale + (er & ~kCmpBit)) : (const void *)(kZeroRow + 4 * lane),
            sm.f8s[FP8 ? st : 0]);
     }

@@ -32,8 +32,11 @@ def test_kernel_names_follow_the_selection():
     fp8 = synth.make_workload("mixed_fp8", batch=2)
     assert bench.attention_kernel(fp8, 8, 0, 0) == "attn_decode_kernel<true>"
     # one slice of 512 listed + 128 window rows: the one-pass decode kernel
-    assert bench.attention_kernel(dec, 1, 0, 0) == "attn_decode_rows_kernel<false>"
-    assert bench.attention_kernel(fp8, 1, 0, 0) == "attn_decode_rows_kernel<true>"
+    assert bench.attention_kernel(dec, 1, 0, 0) == "attn_decode_rows_kernel<false, true>"
+    assert bench.attention_kernel(fp8, 1, 0, 0) == "attn_decode_rows_kernel<true, false>"
+    # 64 queries: the 32-head workgroups fit once, not twice
+    mid = synth.make_workload("decode_csa", batch=64)
+    assert bench.attention_kernel(mid, 1, 0, 0, cus=256) == "attn_decode_rows_kernel<false, false>"
     # a batch whose 32-head workgroups exceed the CUs keeps the 128-head kernel
     big = synth.make_workload("decode_csa", batch=128)
     assert bench.attention_kernel(big, 1, 0, 0, cus=256) == "attn_decode_kernel<false>"

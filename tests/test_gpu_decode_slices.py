@@ -156,6 +156,13 @@ def test_one_pass_kernel_workloads(name):
     check_against_oracle(synth.make_workload(name), num_splits=1, label=f"{name} one pass")
 
 
+def test_one_pass_kernel_full_width():
+    """64 queries: the one-pass workgroups fit the chip once, not twice, so
+    each forms all of O's dimensions (smaller batches split them in two)."""
+    p = synth.make_workload("decode_csa", batch=64)
+    check_against_oracle(p, num_splits=1, label="decode_csa b64 one pass, whole rows")
+
+
 def test_one_pass_kernel_edges():
     """Heads per KV group not a multiple of 32 (the last head block partial),
     two KV heads, a batch that is not a multiple of 8 (the grid is padded),
