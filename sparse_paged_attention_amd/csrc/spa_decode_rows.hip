@@ -190,7 +190,17 @@ void attn_decode_rows_kernel(const Params p) {
         else if (lead)
           flag_error(p, kErrPage);
       }
-      sm.row[r] = er;
+      if constexpr (FP8) {
+        sm.row[r] = er;
+      } else {
+        // bf16 pages: the row's K byte address, its pool in the two low
+        // bits (rows are 16-byte aligned): 0 raw, 1 compressed, 2 masked
+        // (the zero row)
+        const bool cmpr = (er & kCmpBit) != 0;
+        const uint64_t base = (uint64_t)(uintptr_t)(cmpr ? p.k_cmp : p.k_raw);
+        sm.row[r] = er < 0 ? (int64_t)((uint64_t)(uintptr_t)kZeroRow | 2u)
+                           : (int64_t)((base + (uint64_t)(er & ~kCmpBit) * kRowB) | (cmpr ? 1u : 0u));
+      }
     }
   }
   block_sync();                              // rows in LDS; the list and page-table rows are dead
@@ -200,6 +210,13 @@ void attn_decode_rows_kernel(const Params p) {
   const uint8_t *const kcmp = in_sgpr(p.k_cmp), *const vcmp = in_sgpr(p.v_cmp);
   const int32_t ntw = T > wave ? (T - wave + kWaves - 1) / kWaves : 0;
   auto tile_of = [&](int t) { return wave + kWaves * t; };
+  // V byte address of a row from its stored K address (bf16 pages)
+  const int64_t dv_raw = vraw - kraw, dv_cmp = vcmp - kcmp;
+  auto v_of = [&](uint64_t a) -> const uint8_t * {
+    const uint32_t tag = (uint32_t)a & 3u;
+    return (const uint8_t *)(uintptr_t)((a & ~(uint64_t)3) + (uint64_t)(tag == 0 ? dv_raw : tag == 1 ? dv_cmp : 0));
+  };
+  auto row_valid = [&](int64_t v) -> bool { return FP8 ? v >= 0 : ((uint32_t)v & 3u) != 2u; };
   auto is_f8 = [&](int t) { return FP8 && tile_of(t) < nf8; };
   constexpr int NST = Smem::kSt;
   auto issue = [&](int t) {
@@ -212,6 +229,7 @@ void attn_decode_rows_kernel(const Params p) {
       int64_t e8[4];
 #pragma unroll
       for (int n = 0; n < 4; ++n) e8[n] = sm.row[kPT * j + 8 * n + lane / 8];
+      const int64_t es = sm.row[kPT * j + (lane & 31)];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int64_t er = e8[n];
@@ -220,7 +238,6 @@ void attn_decode_rows_kernel(const Params p) {
         dma16(er >= 0 ? kcmp + off : z, sm.u.t.k[wave][st] + kTileB / 2 + 8 * n * kD);
         dma16(er >= 0 ? vcmp + off : z, sm.u.t.v[wave][st] + kTileB / 2 + 8 * n * kD);
       }
-      const int64_t es = sm.row[kPT * j + (lane & 31)];
       const float *scl = lane < 32 ? p.k_cmp_scale : p.v_cmp_scale;
       dma4(es >= 0 ? (const void *)(scl + (es & ~kCmpBit)) : (const void *)(kZeroRow + 4 * (lane & 31)),
            sm.f8s[wave][st]);
@@ -238,22 +255,24 @@ void attn_decode_rows_kernel(const Params p) {
       const int r = 4 * n + lane / kChunks;
       const int64_t er = ek[n];
       const int cs = ((lane % kChunks) ^ swz<kChunks>(r)) * 16;
-      const bool cmp = (er & kCmpBit) != 0;
-      const int64_t off = (er & ~kCmpBit) * kRowB + cs;
-      dma16(er >= 0 ? (cmp ? kcmp : kraw) + off : kZeroRow + cs, sm.u.t.k[wave][st] + 4 * n * kRowB);
-      if constexpr (!DH)
+      if constexpr (FP8) {
+        const bool cmp = (er & kCmpBit) != 0;
+        const int64_t off = (er & ~kCmpBit) * kRowB + cs;
+        dma16(er >= 0 ? (cmp ? kcmp : kraw) + off : kZeroRow + cs, sm.u.t.k[wave][st] + 4 * n * kRowB);
         dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + cs, sm.u.t.v[wave][st] + 4 * n * kRowB);
+      } else {
+        const uint64_t a = (uint64_t)er;
+        dma16((const uint8_t *)(uintptr_t)(a & ~(uint64_t)3) + cs, sm.u.t.k[wave][st] + 4 * n * kRowB);
+        if constexpr (!DH) dma16(v_of(a) + cs, sm.u.t.v[wave][st] + 4 * n * kRowB);
+      }
     }
     if constexpr (DH) {
       // the workgroup's half of each V row: 8 rows of 128 bytes per load
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int r = 8 * n + lane / kVChunks;
-        const int64_t er = ev[n];
         const int cs = ((lane % kVChunks) ^ swz<kVChunks>(r)) * 16;
-        const bool cmp = (er & kCmpBit) != 0;
-        const int64_t off = (er & ~kCmpBit) * kRowB + kVRowB * dh + cs;
-        dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + cs, sm.u.t.v[wave][st] + 8 * n * kVRowB);
+        dma16(v_of((uint64_t)ev[n]) + kVRowB * dh + cs, sm.u.t.v[wave][st] + 8 * n * kVRowB);
       }
     }
   };
@@ -307,7 +326,7 @@ void attn_decode_rows_kernel(const Params p) {
         }
       asm volatile("" ::: "memory");
     }
-    const uint32_t tm = (uint32_t)__ballot(lane < 32 && sm.row[kPT * j + (lane & 31)] >= 0);
+    const uint32_t tm = (uint32_t)__ballot(lane < 32 && row_valid(sm.row[kPT * j + (lane & 31)]));
     bf16x8 kf[kD / 16];
     {
       const int r = lane & 31;
