@@ -67,10 +67,10 @@ def attention_kernel(p, splits, hpb, qpb, cus=256):
         return "attn_pair_kernel<3>"
     rows_wgs = p.num_queries * p.num_kv_heads * -(-(p.num_q_heads // p.num_kv_heads) // 32)
     if decode_ok and S == 1 and rows_wgs <= cus:
-        if p.cmp_fp8:
-            return "attn_decode_rows_kernel<true, false>"
-        # bf16 pages and room for twice the workgroups: each forms half of O's dimensions
-        return "attn_decode_rows_kernel<false, true>" if 2 * rows_wgs <= cus else "attn_decode_rows_kernel<false, false>"
+        # room for twice the workgroups: each forms half of O's dimensions
+        b = lambda x: "true" if x else "false"
+        return (f"attn_decode_rows_kernel<{b(p.cmp_fp8)}, {b(2 * rows_wgs <= cus)}, "
+                f"{b(p.cmp_fp8 and p.cmp_fp8_fnuz)}>")
     if decode_ok:
         return "attn_decode_kernel<true>" if p.cmp_fp8 else "attn_decode_kernel<false>"
     return "attn_fwd_kernel"
@@ -207,7 +207,7 @@ def parse_args(argv=None):
 
 
 DEFAULTS = {   # (num_splits, heads_per_block, queries_per_block) per workload; 0 = library choice
-    "decode_csa": (1, 0, 0), "decode_hca": (1, 0, 0), "mixed_fp8": (8, 0, 0), "prefill_csa": (1, 0, 0),
+    "decode_csa": (1, 0, 0), "decode_hca": (1, 0, 0), "mixed_fp8": (1, 0, 0), "prefill_csa": (1, 0, 0),
     "tiny": (1, 0, 0), "decode_latent": (4, 0, 0),
 }
 

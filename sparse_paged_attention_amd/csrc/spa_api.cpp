@@ -240,9 +240,9 @@ spa_status run_forward(const spa_fwd_args *a, bool decode, void *stream, void *s
   const int64_t rows_wgs = (int64_t)a->num_queries * a->num_kv_heads * ((p.group + 31) / 32);
   const bool dec_rows = dec && a->num_splits == 1 && spa::decode_rows_eligible(p) &&
                         rows_wgs <= spa::device_cu_count();
-  // bf16 pages, and the workgroups fit twice over: each takes half of O's
-  // dimensions (all of K, half of each V row)
-  const bool dec_halves = dec_rows && !p.cmp_fp8 && 2 * rows_wgs <= spa::device_cu_count();
+  // the workgroups fit twice over: each takes half of O's dimensions (all
+  // of K, half of each V row)
+  const bool dec_halves = dec_rows && 2 * rows_wgs <= spa::device_cu_count();
   const bool latent = a->head_dim == 512;
   hipError_t e = latent  ? spa::launch_latent(p, s)
                  : pairs ? spa::launch_prefill_pairs(p, s)

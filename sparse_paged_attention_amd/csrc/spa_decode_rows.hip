@@ -26,10 +26,12 @@
 //
 // A bf16 tile: 8 direct 1 KiB loads per side (lane L of load n: row
 // 4n + L / 16, logical chunk (L % 16) ^ swz(row)).  An e4m3 tile: 4 loads
-// per side of 8 rows each into the upper half of the side's stage, and one
-// load of the 32 k and 32 v scales; the wave then reads all its codes and
-// widens them exactly to bf16 over the whole stage.  The k scale multiplies
-// the fp32 scores and the v scale p before its bf16 rounding.
+// per side of 8 rows of 128 codes each (lane L of load n: row 8n + L / 8,
+// 16-byte piece (L % 8) ^ f8_swz(row)), and one load of the 32 k and 32 v
+// scales.  The codes stay in LDS as they are: the wave reads each MFMA
+// operand's 8 codes (V's through the 8-bit transpose read) and widens them
+// exactly to bf16 in registers.  The k scale multiplies the fp32 scores and
+// the v scale p before its bf16 rounding.
 
 #include <hip/hip_runtime.h>
 
@@ -48,6 +50,16 @@ constexpr int kPT = 32;                    // rows per tile
 constexpr int kTileB = kPT * kRowB;        // one side of a tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+
+// e4m3 tile rows (128 bytes): logical 16-byte piece c of row r sits at
+// piece c ^ f8_swz(r), so the 8 rows that one 16-lane group of the V
+// transpose read touches fall in distinct banks, and the 32 rows of a K
+// operand read in 16 distinct bank groups instead of two.
+__device__ __forceinline__ int f8_swz(int r) { return (r >> 1) & 7; }
+// The same for the 64-byte half rows of V's codes that a workgroup forming
+// half of O stages: the 16 rows of a transpose read's k block fall in
+// distinct banks for each piece.
+__device__ __forceinline__ int f8h_swz(int r) { return (r >> 2) & 3; }
 constexpr int kHeads = 32;                 // query heads per workgroup
 constexpr int kRowsMax = kDecodeRowsMax;
 constexpr int kPtLds = 2048;               // page-table entries staged in LDS
@@ -75,16 +87,16 @@ struct RowsSmem {
     } s;
     alignas(16) float acc[kWaves][kOD / 32][16][64];   // the waves' O^T: [wave][d block][value][lane]
   } u;
-  alignas(16) float f8s[kWaves][kWSt][64];  // e4m3 tiles: 32 k scales, then 32 v scales
+  alignas(16) float f8s[kWaves][kSt][64];   // e4m3 tiles: 32 k scales, then 32 v scales
   alignas(16) int64_t row[kRowsMax];        // pool rows, padded to whole tiles
   float mw[kWaves][64];                     // the waves' m and l per lane
   float lw[kWaves][64];
 };
 
-template <bool FP8, bool DH>
+template <bool FP8, bool DH, bool FNUZ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void attn_decode_rows_kernel(const Params p) {
-  static_assert(!(FP8 && DH), "e4m3 tiles widen whole rows");
+  static_assert(FP8 || !FNUZ, "FNUZ is an e4m3 format");
   using Smem = RowsSmem<DH>;
   constexpr int kVRowB = Smem::kVRowB;
   constexpr int kVChunks = kVRowB / 16;
@@ -225,18 +237,31 @@ void attn_decode_rows_kernel(const Params p) {
     // every row of the tile is read before the first load: the loads' memory
     // clobber keeps a later LDS read from starting ahead of them
     if (FP8 && j < nf8) {
-      // e4m3: 8 rows of 128 bytes per load into the upper half of the stage
-      int64_t e8[4];
+      // e4m3: 8 rows of 128 codes per load, pieces swizzled by f8_swz; with
+      // DH, V's half rows: 16 rows of 64 codes per load, swizzled by f8h_swz
+      int64_t e8[4], eh[2];
 #pragma unroll
       for (int n = 0; n < 4; ++n) e8[n] = sm.row[kPT * j + 8 * n + lane / 8];
+      if constexpr (DH) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) eh[n] = sm.row[kPT * j + 16 * n + lane / 4];
+      }
       const int64_t es = sm.row[kPT * j + (lane & 31)];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int64_t er = e8[n];
-        const int64_t off = (er & ~kCmpBit) * kD + (lane % 8) * 16;
+        const int64_t off = (er & ~kCmpBit) * kD + (((lane % 8) ^ f8_swz(8 * n + lane / 8)) * 16);
         const uint8_t *z = kZeroRow + (lane % 8) * 16;
-        dma16(er >= 0 ? kcmp + off : z, sm.u.t.k[wave][st] + kTileB / 2 + 8 * n * kD);
-        dma16(er >= 0 ? vcmp + off : z, sm.u.t.v[wave][st] + kTileB / 2 + 8 * n * kD);
+        dma16(er >= 0 ? kcmp + off : z, sm.u.t.k[wave][st] + 8 * n * kD);
+        if constexpr (!DH) dma16(er >= 0 ? vcmp + off : z, sm.u.t.v[wave][st] + 8 * n * kD);
+      }
+      if constexpr (DH) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const int64_t er = eh[n];
+          const int64_t off = (er & ~kCmpBit) * kD + kD / 2 * dh + (((lane % 4) ^ f8h_swz(16 * n + lane / 4)) * 16);
+          dma16(er >= 0 ? vcmp + off : kZeroRow + (lane % 4) * 16, sm.u.t.v[wave][st] + 16 * n * (kD / 2));
+        }
       }
       const float *scl = lane < 32 ? p.k_cmp_scale : p.v_cmp_scale;
       dma4(es >= 0 ? (const void *)(scl + (es & ~kCmpBit)) : (const void *)(kZeroRow + 4 * (lane & 31)),
@@ -259,7 +284,8 @@ void attn_decode_rows_kernel(const Params p) {
         const bool cmp = (er & kCmpBit) != 0;
         const int64_t off = (er & ~kCmpBit) * kRowB + cs;
         dma16(er >= 0 ? (cmp ? kcmp : kraw) + off : kZeroRow + cs, sm.u.t.k[wave][st] + 4 * n * kRowB);
-        dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + cs, sm.u.t.v[wave][st] + 4 * n * kRowB);
+        if constexpr (!DH)
+          dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + cs, sm.u.t.v[wave][st] + 4 * n * kRowB);
       } else {
         const uint64_t a = (uint64_t)er;
         dma16((const uint8_t *)(uintptr_t)(a & ~(uint64_t)3) + cs, sm.u.t.k[wave][st] + 4 * n * kRowB);
@@ -272,12 +298,20 @@ void attn_decode_rows_kernel(const Params p) {
       for (int n = 0; n < 4; ++n) {
         const int r = 8 * n + lane / kVChunks;
         const int cs = ((lane % kVChunks) ^ swz<kVChunks>(r)) * 16;
-        dma16(v_of((uint64_t)ev[n]) + kVRowB * dh + cs, sm.u.t.v[wave][st] + 8 * n * kVRowB);
+        const uint8_t *src;
+        if constexpr (FP8) {
+          const int64_t er = ev[n];
+          src = er >= 0 ? ((er & kCmpBit) != 0 ? vcmp : vraw) + (er & ~kCmpBit) * kRowB + kVRowB * dh + cs
+                        : kZeroRow + cs;
+        } else {
+          src = v_of((uint64_t)ev[n]) + kVRowB * dh + cs;
+        }
+        dma16(src, sm.u.t.v[wave][st] + 8 * n * kVRowB);
       }
     }
   };
   constexpr int kLoads = DH ? 12 : 16;       // direct loads of a bf16 tile
-  const bool fnuz = FP8 && p.cmp_fnuz != 0;
+  constexpr int kLoads8 = DH ? 7 : 9;        // and of an e4m3 tile
 
   float m = sink == -INFINITY ? -INFINITY : sink * kLog2e;
   float l = (sink != -INFINITY && hi == 0) ? 1.f : 0.f;   // exp2(sink - m) = 1, counted once per head
@@ -292,9 +326,9 @@ void attn_decode_rows_kernel(const Params p) {
     const int st = t % NST;
     const bool f8 = is_f8(t);
     // this wave's loads of tile j are complete (those of its next tile may
-    // still be in flight: 16, or 9 for an e4m3 tile)
+    // still be in flight: kLoads, or kLoads8 for an e4m3 tile)
     if (t + 1 < ntw) {
-      if (is_f8(t + 1)) wait_vmcnt<9>();
+      if (is_f8(t + 1)) wait_vmcnt<kLoads8>();
       else wait_vmcnt<kLoads>();
     } else {
       wait_vmcnt<0>();
@@ -304,40 +338,51 @@ void attn_decode_rows_kernel(const Params p) {
     if (NST == 3 && t + 2 < ntw) issue(t + 2);
     uint8_t *Kt = sm.u.t.k[wave][st];
     uint8_t *Vt = sm.u.t.v[wave][st];
-    if (FP8 && f8) {
-      // widen the codes over the whole stage: all of this wave's codes are
-      // read before any bf16 write (one wave's LDS operations are in order)
-      uint2 cw[2][8];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int idx = lane + 64 * k;             // row idx / 16, piece idx % 16
-          cw[s][k] = *(const uint2 *)((s ? Vt : Kt) + kTileB / 2 + (idx >> 4) * kD + (idx & 15) * 8);
-        }
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int idx = lane + 64 * k;
-          const int r = idx >> 4, piece = idx & 15;
-          *(uint4 *)((s ? Vt : Kt) + r * kRowB + ((piece ^ swz<kChunks>(r)) * 16)) = widen8_e4m3(cw[s][k], fnuz);
-        }
-      asm volatile("" ::: "memory");
-    }
     const uint32_t tm = (uint32_t)__ballot(lane < 32 && row_valid(sm.row[kPT * j + (lane & 31)]));
     bf16x8 kf[kD / 16];
-    {
+    i16x8 vf[kOD / 32][2];
+    if (FP8 && f8) {
+      // e4m3 codes straight into the MFMA operands: K's A fragment is 8
+      // codes of one row; V's is one dimension over the 8 rows that P's
+      // fragment holds (rows 4hi .. 4hi+3 and 8+4hi .. 8+4hi+3 of the 16),
+      // which the 8-bit transpose read gathers: output lane L's byte b comes
+      // from input lane 2b + L / 8, so input lanes 2b and 2b+1 point at the
+      // codes of the b-th of those rows for the 16-lane group's 16 dimensions
+      uint2 kc[kD / 16];
+      v2i32 vc[kOD / 32][2];
+      const int r = lane & 31;
+#pragma unroll
+      for (int kk = 0; kk < kD / 16; ++kk)
+        kc[kk] = *(const uint2 *)(Kt + r * kD + ((kk ^ f8_swz(r)) * 16) + 8 * hi);
+      const int G = lane >> 4;
+      const int L = lane & 15;
+#pragma unroll
+      for (int db = 0; db < kOD / 32; ++db)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int b8 = L >> 1;
+          const int row = 16 * k2 + 4 * (G >> 1) + 8 * (b8 >> 2) + (b8 & 3);
+          const int piece = 2 * db + (G & 1);
+          // V's codes: whole rows, or with DH the workgroup's 64-code halves
+          const int voff = DH ? row * (kD / 2) + ((piece ^ f8h_swz(row)) * 16)
+                              : row * kD + ((piece ^ f8_swz(row)) * 16);
+          vc[db][k2] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_t *)(Vt + voff + (L & 1) * 8));
+        }
+#pragma unroll
+      for (int kk = 0; kk < kD / 16; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, widen8_e4m3<FNUZ>(kc[kk]));
+#pragma unroll
+      for (int db = 0; db < kOD / 32; ++db)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+          vf[db][k2] = __builtin_bit_cast(
+              i16x8, widen8_e4m3<FNUZ>(make_uint2((uint32_t)vc[db][k2][0], (uint32_t)vc[db][k2][1])));
+    } else {
       const int r = lane & 31;
 #pragma unroll
       for (int kk = 0; kk < kD / 16; ++kk) {
         const int c = 2 * kk + hi;
         kf[kk] = *(const bf16x8 *)(Kt + r * kRowB + ((c ^ swz<kChunks>(r)) * 16));
       }
-    }
-    i16x8 vf[kOD / 32][2];
-    {
       const int G = lane >> 4;
       const int L = lane & 15;
 #pragma unroll
@@ -458,16 +503,17 @@ bool decode_rows_eligible(const Params &p) {
 
 hipError_t launch_decode_rows(const Params &p, bool halves, hipStream_t stream) {
   if (p.num_queries == 0) return hipSuccess;
-  if (!decode_rows_eligible(p) || (halves && p.cmp_fp8)) return hipErrorInvalidConfiguration;
+  if (!decode_rows_eligible(p)) return hipErrorInvalidConfiguration;
   const int64_t units = (int64_t)p.num_queries * p.hkv;
   const int64_t grid = (units + 7) / 8 * 8 * ((p.group + kHeads - 1) / kHeads) * (halves ? 2 : 1);
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  if (p.cmp_fp8)
-    hipLaunchKernelGGL((attn_decode_rows_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-  else if (halves)
-    hipLaunchKernelGGL((attn_decode_rows_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_decode_rows_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  auto kernel = p.cmp_fp8 ? (p.cmp_fnuz ? (halves ? attn_decode_rows_kernel<true, true, true>
+                                                  : attn_decode_rows_kernel<true, false, true>)
+                                        : (halves ? attn_decode_rows_kernel<true, true, false>
+                                                  : attn_decode_rows_kernel<true, false, false>))
+                : halves ? attn_decode_rows_kernel<false, true, false>
+                         : attn_decode_rows_kernel<false, false, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -16,7 +16,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32_t;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -132,20 +134,23 @@ __device__ __forceinline__ uint32_t pack_bf16_hi(float lo, float hi) {
 // Eight e4m3 codes (little-endian in w) widened exactly to bf16, packed two
 // per word.  OCP: v_cvt_pk_f32_fp8.  FNUZ (bias 8, no infinities, one NaN):
 // code c is the OCP value of c halved, except 0x7F / 0xFF (+-240, OCP NaN)
-// and 0x80 (NaN, OCP -0).  Every such value is a bf16 value.
-__device__ __forceinline__ uint4 widen8_e4m3(uint2 w, bool fnuz) {
+// and 0x80 (NaN, OCP -0), fixed by selects.  Every such value is a bf16
+// value.
+template <bool FNUZ>
+__device__ __forceinline__ uint4 widen8_e4m3(uint2 w) {
   const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
   const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
   const f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
   const f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
   float f[8] = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-  if (fnuz) {
+  if constexpr (FNUZ) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t c = ((i < 4 ? w.x : w.y) >> (8 * (i & 3))) & 0xFFu;
-      f[i] = (c & 0x7Fu) == 0x7Fu ? ((c & 0x80u) ? -240.f : 240.f)
-             : c == 0x80u          ? __builtin_bit_cast(float, 0x7FC00000u)
-                                   : 0.5f * f[i];
+      const float s240 = __builtin_bit_cast(float, 0x43700000u | ((c & 0x80u) << 24));   // +-240
+      const float h = 0.5f * f[i];
+      f[i] = (c & 0x7Fu) == 0x7Fu ? s240 : h;
+      f[i] = c == 0x80u ? __builtin_bit_cast(float, 0x7FC00000u) : f[i];
     }
   }
   uint4 o;
@@ -154,6 +159,10 @@ __device__ __forceinline__ uint4 widen8_e4m3(uint2 w, bool fnuz) {
   o.z = (__builtin_bit_cast(uint32_t, f[4]) >> 16) | (__builtin_bit_cast(uint32_t, f[5]) & 0xFFFF0000u);
   o.w = (__builtin_bit_cast(uint32_t, f[6]) >> 16) | (__builtin_bit_cast(uint32_t, f[7]) & 0xFFFF0000u);
   return o;
+}
+
+__device__ __forceinline__ uint4 widen8_e4m3(uint2 w, bool fnuz) {
+  return fnuz ? widen8_e4m3<true>(w) : widen8_e4m3<false>(w);
 }
 
 __device__ __forceinline__ int round_up(int x, int m) { return (x + m - 1) / m * m; }

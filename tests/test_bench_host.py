@@ -32,14 +32,19 @@ def test_kernel_names_follow_the_selection():
     fp8 = synth.make_workload("mixed_fp8", batch=2)
     assert bench.attention_kernel(fp8, 8, 0, 0) == "attn_decode_kernel<true>"
     # one slice of 512 listed + 128 window rows: the one-pass decode kernel
-    assert bench.attention_kernel(dec, 1, 0, 0) == "attn_decode_rows_kernel<false, true>"
-    assert bench.attention_kernel(fp8, 1, 0, 0) == "attn_decode_rows_kernel<true, false>"
+    assert bench.attention_kernel(dec, 1, 0, 0) == "attn_decode_rows_kernel<false, true, false>"
+    assert bench.attention_kernel(fp8, 1, 0, 0) == "attn_decode_rows_kernel<true, true, false>"
     # 64 queries: the 32-head workgroups fit once, not twice
     mid = synth.make_workload("decode_csa", batch=64)
-    assert bench.attention_kernel(mid, 1, 0, 0, cus=256) == "attn_decode_rows_kernel<false, false>"
+    assert bench.attention_kernel(mid, 1, 0, 0, cus=256) == "attn_decode_rows_kernel<false, false, false>"
     # a batch whose 32-head workgroups exceed the CUs keeps the 128-head kernel
     big = synth.make_workload("decode_csa", batch=128)
     assert bench.attention_kernel(big, 1, 0, 0, cus=256) == "attn_decode_kernel<false>"
+    fnuz = synth.make_problem("fnuz", "decode", [3000, 700], 128, 1, 128, 64, 128, 4, 512, seed=44, cmp_fp8=True,
+                              fp8_format="fnuz")
+    assert bench.attention_kernel(fnuz, 1, 0, 0) == "attn_decode_rows_kernel<true, true, true>"
+    fp8_64 = synth.make_workload("mixed_fp8", batch=64)
+    assert bench.attention_kernel(fp8_64, 1, 0, 0, cus=256) == "attn_decode_rows_kernel<true, false, false>"
     lat = synth.make_workload("decode_latent", batch=2)
     assert bench.attention_kernel(lat, 4, 0, 0) == "attn_latent_kernel"
 
@@ -61,6 +66,11 @@ def test_algorithmic_work_separate_and_shared_rows():
     # Q + O bf16, LSE, 640 entries of K and V rows (2 x 128 x 2 B), 512 list ids
     assert b == 2 * (128 * 128 * 2 * 2 + 128 * 4 + 640 * 512 + 512 * 4)
     assert f == 4 * 128 * 128 * 2 * 640 and n == 1280
+    fnuz = synth.make_problem("fnuz", "decode", [3000, 700], 128, 1, 128, 64, 128, 4, 512, seed=44, cmp_fp8=True,
+                              fp8_format="fnuz")
+    assert bench.attention_kernel(fnuz, 1, 0, 0) == "attn_decode_rows_kernel<true, true, true>"
+    fp8_64 = synth.make_workload("mixed_fp8", batch=64)
+    assert bench.attention_kernel(fp8_64, 1, 0, 0, cus=256) == "attn_decode_rows_kernel<true, false, false>"
     lat = synth.make_workload("decode_latent", batch=2)
     b2, _, _ = bench.algorithmic_work(lat, _counts(lat))
     # one shared 512-wide row per entry

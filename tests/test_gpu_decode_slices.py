@@ -163,6 +163,18 @@ def test_one_pass_kernel_full_width():
     check_against_oracle(p, num_splits=1, label="decode_csa b64 one pass, whole rows")
 
 
+def test_one_pass_e4m3_full_width():
+    """e4m3 pages, OCP and FNUZ, at batches whose one-pass workgroups fit the
+    chip once (each forms all of O's dimensions from whole rows of V's codes),
+    and the FNUZ pages at a small batch (half of each V row's codes)."""
+    p = synth.make_workload("mixed_fp8", batch=64)
+    check_against_oracle(p, num_splits=1, label="mixed_fp8 b64 one pass, whole rows")
+    rng = np.random.default_rng(65)
+    f = _decode("rows_fnuz_wide", rng.integers(600, 6000, size=40), 128, 1, 64, 128, 4, 512, seed=65, cmp_fp8=True,
+                fp8_format="fnuz", selection="random")
+    check_against_oracle(f, num_splits=1, label="one pass fnuz, whole rows")
+
+
 def test_one_pass_kernel_edges():
     """Heads per KV group not a multiple of 32 (the last head block partial),
     two KV heads, a batch that is not a multiple of 8 (the grid is padded),
