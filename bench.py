@@ -52,7 +52,7 @@ def attention_kernel(p, splits, hpb, qpb, cus=256):
     the selection in spa_api.cpp (for a decode the library sizes itself: the
     one-pass kernel with one slice, the slice kernel with several)."""
     if p.head_dim == 512:
-        return "attn_latent_kernel"
+        return "attn_latent_kernel<true>" if p.cmp_fp8 else "attn_latent_kernel<false>"
     pairs_ok = (p.mode == "prefill" and p.head_dim == 128 and not p.cmp_fp8 and splits == 1
                 and (p.ratio == 0 or p.topk > 0) and 2 * (p.topk + p.window) <= PAIR_ROWS_MAX)
     pairs = pairs_ok and (qpb == 2 or (qpb == 0 and hpb != 32))

@@ -46,7 +46,7 @@ def test_kernel_names_follow_the_selection():
     fp8_64 = synth.make_workload("mixed_fp8", batch=64)
     assert bench.attention_kernel(fp8_64, 1, 0, 0, cus=256) == "attn_decode_rows_kernel<true, false, false>"
     lat = synth.make_workload("decode_latent", batch=2)
-    assert bench.attention_kernel(lat, 4, 0, 0) == "attn_latent_kernel"
+    assert bench.attention_kernel(lat, 4, 0, 0) == "attn_latent_kernel<false>"
 
 
 def _counts(p):
