@@ -168,8 +168,11 @@ typedef struct spa_fwd_args {
 
 /* Bytes of workspace the call needs: 0 when num_splits == 1, otherwise the
    sink-free split partials f32 O [S, Nq, Hq, D] and f32 LSE [S, Nq, Hq]
-   (the LSE at a 256-byte boundary; no initial contents needed).
-   Returns 0 for a NULL or inconsistent argument block. */
+   (the LSE at a 256-byte boundary; no initial contents needed): the buffer
+   between a KV-split decode and its reduce in the decode trace of the ATOM PR
+   "test: add block-level DeepSeek-V4 attention test", section "What this
+   test actually drives".  Returns 0 for a NULL or inconsistent argument
+   block. */
 size_t attn_workspace_size(const spa_fwd_args *args);
 
 /* Decode: one query per sequence at position seq_lens[b] - 1
@@ -215,11 +218,16 @@ spa_status attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t 
                           const float *sink, void *o_out, float *lse_out, void *stream);
 
 /* Gather metadata, computed on the device by the same translation code the
-   attention kernels use: for each query, rows_out[i, :] holds the physical
+   attention kernels use (the paged offsets that the ATOM PR "test: add
+   block-level DeepSeek-V4 attention test" packs from the selected ids before
+   the attention, sections "What this test actually drives" and "Why it
+   drives the real metadata builder"): for each query, rows_out[i, :] holds the physical
    row index (within its pool) of every KV entry in canonical order — the
    n_sel compressed rows, then the win_len window rows — padded with -1 up to
    cap; counts_out[i] = {win_lo, win_len, n_c, n_sel}.  A masked (invalid)
-   entry is reported as -2.  `decode` selects the decode query convention.
+   entry is reported as -2.  `decode` (nonzero) selects the decode query
+   convention of attn_fwd_decode (query i of sequence i at seq_lens[i] - 1;
+   query_seq and query_pos must be NULL); zero, that of attn_fwd_prefill.
    rows_out int64 [Nq, cap], counts_out int32 [Nq, 4] (device).  Entries past
    cap are not written; cap >= window + max list length suffices. */
 spa_status attn_build_gather(const spa_fwd_args *args, int32_t decode, int32_t cap,
@@ -304,7 +312,9 @@ typedef struct spa_bwd_grads {
 size_t attn_bwd_workspace_size(const spa_fwd_args *args);
 spa_status attn_bwd(const spa_fwd_args *args, const spa_bwd_grads *grads, void *stream);
 
-/* Message for the last non-OK status returned on this thread ("" if none). */
+/* Message for the last non-OK status returned on this thread ("" if none):
+   the reason behind the distinct status of each fault class (RL-Kernel joint
+   attention PR, review of the guard matrix). */
 const char *attn_last_error(void);
 
 /* Library ABI version (this header: 1). */
