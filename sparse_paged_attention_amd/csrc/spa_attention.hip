@@ -59,7 +59,8 @@
 //
 // FP8 (OCP e4m3) compressed rows land in an LDS staging area, together with
 // their fp32 per-token scales, and are widened to bf16 exactly (every e4m3
-// value is a bf16 value) by v_cvt_pk_f32_fp8; the scales are applied in fp32
+// value is a bf16 value) by v_cvt_scalef32_pk_bf16_fp8 at scale 1 (FNUZ codes
+// through v_cvt_pk_f32_fp8 and fix-ups); the scales are applied in fp32
 // to the scores (k) and to P (v), so the MFMAs see the exact codes.
 //
 // Invalid metadata (a listed id that is not a complete group, a page id

@@ -132,18 +132,28 @@ __device__ __forceinline__ uint32_t pack_bf16_hi(float lo, float hi) {
 }
 
 // Eight e4m3 codes (little-endian in w) widened exactly to bf16, packed two
-// per word.  OCP: v_cvt_pk_f32_fp8.  FNUZ (bias 8, no infinities, one NaN):
-// code c is the OCP value of c halved, except 0x7F / 0xFF (+-240, OCP NaN)
-// and 0x80 (NaN, OCP -0), fixed by selects.  Every such value is a bf16
-// value.
+// per word.  OCP: the scaled conversion with scale 1 (gfx950) turns two codes
+// into two bf16 values in one instruction; every OCP e4m3 value is a bf16
+// value, so nothing rounds.  FNUZ (bias 8, no infinities, one NaN): code c is
+// the OCP value of c halved, except 0x7F / 0xFF (+-240, OCP NaN) and 0x80
+// (NaN, OCP -0), fixed by selects on the OCP values widened to fp32 by
+// v_cvt_pk_f32_fp8.  Every such value is a bf16 value.
 template <bool FNUZ>
 __device__ __forceinline__ uint4 widen8_e4m3(uint2 w) {
-  const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-  const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-  const f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-  const f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-  float f[8] = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-  if constexpr (FNUZ) {
+  if constexpr (!FNUZ) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.0f, true);
+    return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                      __builtin_bit_cast(uint32_t, d));
+  } else {
+    const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+    const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    const f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+    const f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    float f[8] = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t c = ((i < 4 ? w.x : w.y) >> (8 * (i & 3))) & 0xFFu;
@@ -152,13 +162,13 @@ __device__ __forceinline__ uint4 widen8_e4m3(uint2 w) {
       f[i] = (c & 0x7Fu) == 0x7Fu ? s240 : h;
       f[i] = c == 0x80u ? __builtin_bit_cast(float, 0x7FC00000u) : f[i];
     }
+    uint4 o;
+    o.x = (__builtin_bit_cast(uint32_t, f[0]) >> 16) | (__builtin_bit_cast(uint32_t, f[1]) & 0xFFFF0000u);
+    o.y = (__builtin_bit_cast(uint32_t, f[2]) >> 16) | (__builtin_bit_cast(uint32_t, f[3]) & 0xFFFF0000u);
+    o.z = (__builtin_bit_cast(uint32_t, f[4]) >> 16) | (__builtin_bit_cast(uint32_t, f[5]) & 0xFFFF0000u);
+    o.w = (__builtin_bit_cast(uint32_t, f[6]) >> 16) | (__builtin_bit_cast(uint32_t, f[7]) & 0xFFFF0000u);
+    return o;
   }
-  uint4 o;
-  o.x = (__builtin_bit_cast(uint32_t, f[0]) >> 16) | (__builtin_bit_cast(uint32_t, f[1]) & 0xFFFF0000u);
-  o.y = (__builtin_bit_cast(uint32_t, f[2]) >> 16) | (__builtin_bit_cast(uint32_t, f[3]) & 0xFFFF0000u);
-  o.z = (__builtin_bit_cast(uint32_t, f[4]) >> 16) | (__builtin_bit_cast(uint32_t, f[5]) & 0xFFFF0000u);
-  o.w = (__builtin_bit_cast(uint32_t, f[6]) >> 16) | (__builtin_bit_cast(uint32_t, f[7]) & 0xFFFF0000u);
-  return o;
 }
 
 __device__ __forceinline__ uint4 widen8_e4m3(uint2 w, bool fnuz) {
