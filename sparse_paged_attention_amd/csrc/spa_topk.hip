@@ -27,10 +27,13 @@
 // above T and the first ones equal to T are then ranked in ascending id
 // order by ballots and one exchange of per-wave counts.  In id order each
 // selected id is then written at its rank directly.  In score order the selected
-// (key, id) pairs are ordered as (key << 32 | ~id), descending: up to 512
-// by a bitonic network within each wave over runs of 128 in registers, then
-// each pair's position from binary searches of the other runs; more by one
-// bitonic network over the workgroup.  Longer rows run the same select with
+// (key, id) pairs are ordered as (key << 32 | ~id), descending: up to 512,
+// in a launch with at most as many rows as compute units, by one bitonic
+// network over the workgroup (lanes exchange by DPP and swizzles, waves
+// through LDS), the shortest chain; in a larger launch by a bitonic network
+// within each wave over runs of 128 in registers, then each pair's position
+// from binary searches of the other runs, the least work; more than 512 by
+// one bitonic network over the workgroup.  Longer rows run the same select with
 // histograms of the whole workgroup over the scores in memory.
 
 #include <hip/hip_runtime.h>
@@ -378,11 +381,12 @@ __device__ __forceinline__ int32_t count_above(const unsigned long long *run, un
 }
 
 // Orders up to 512 selected pairs (sel[0, kk)) and writes the ids of the
-// first k positions (-1 past kk): wave w sorts entries [128w, 128w + 128) in
+// first k positions (-1 past kk), with the least work (for launches with more
+// rows than compute units): wave w sorts entries [128w, 128w + 128) in
 // registers, and after one barrier each entry's position is its place in
 // its own run plus the entries above it in the other runs, found by binary
 // search; the id is written there directly.
-__device__ __forceinline__ void rank_write(unsigned long long *sel, int32_t kk, int32_t k, int32_t *out) {
+__device__ __forceinline__ void rank_write_runs(unsigned long long *sel, int32_t kk, int32_t k, int32_t *out) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t runs = (kk + 127) >> 7;
@@ -411,9 +415,88 @@ __device__ __forceinline__ void rank_write(unsigned long long *sel, int32_t kk, 
   for (int32_t i = kk + tid; i < k; i += kTkThreads) out[i] = -1;
 }
 
+// One compare-exchange step (block size SIZE, stride S) of the bitonic
+// network over the 512 entries of a workgroup: entry i = 128 w + 64 r + lane
+// is v[r] of wave w's lane.  A block of SIZE entries is ordered descending
+// where (i & SIZE) == 0, so the last step leaves all 512 descending.  Strides
+// below 64 pair lanes of a wave, 64 pairs the two registers of a lane, and
+// 128 and 256 pair waves through LDS (buf: 512 entries).
+template <int SIZE, int S>
+__device__ __forceinline__ void bitonic512_step(unsigned long long (&v)[2], int wave, unsigned long long *buf) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (S >= 128) {
+    // pairs of waves: wave w's entries meet wave w ^ (S / 128)'s
+#pragma unroll
+    for (int r = 0; r < 2; ++r) buf[128 * wave + 64 * r + lane] = v[r];
+    __syncthreads();
+    unsigned long long w[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) w[r] = buf[(128 * wave + 64 * r + lane) ^ S];
+    __syncthreads();                         // the next exchange rewrites buf
+    const bool desc = ((128 * wave) & SIZE) == 0;
+    const bool lower = ((128 * wave) & S) == 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const unsigned long long a = v[r], b = w[r];
+      v[r] = (desc == lower) ? (a > b ? a : b) : (a < b ? a : b);
+    }
+  } else if constexpr (S == 64) {
+    // SIZE >= 128: the direction is the wave's
+    const bool desc = ((128 * wave) & SIZE) == 0;
+    const unsigned long long a = v[0], b = v[1];
+    const bool gt = a > b;
+    v[0] = (gt == desc) ? a : b;
+    v[1] = (gt == desc) ? b : a;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      uint64_t desc;
+      if constexpr (SIZE <= 32) desc = lanes_bit_clear(SIZE);
+      else desc = (((128 * wave + 64 * r) & SIZE) == 0) ? ~0ull : 0ull;
+      const uint64_t take_max = ~(lanes_bit_clear(S) ^ desc);
+      const unsigned long long a = v[r];
+      const unsigned long long b = ((unsigned long long)xor_lane<S>((uint32_t)(a >> 32)) << 32) |
+                                   xor_lane<S>((uint32_t)a);
+      const bool keep = (a > b) == __builtin_amdgcn_inverse_ballot_w64(take_max);
+      v[r] = keep ? a : b;
+    }
+  }
+  if constexpr (S > 1) bitonic512_step<SIZE, S / 2>(v, wave, buf);
+}
+
+template <int SIZE>
+__device__ __forceinline__ void bitonic512_sort(unsigned long long (&v)[2], int wave, unsigned long long *buf) {
+  bitonic512_step<SIZE, SIZE / 2>(v, wave, buf);
+  if constexpr (SIZE < 512) bitonic512_sort<SIZE * 2>(v, wave, buf);
+}
+
+// The same, with the shortest chain (for launches with at most as many rows
+// as compute units, where each row's latency is the call's): one bitonic
+// network over the workgroup's 512 entries, padding 0 (below every selected
+// pair, as ~id has its top bit set) sorting last; position i is then entry i.
+__device__ __forceinline__ void rank_write_net(unsigned long long *sel, int32_t kk, int32_t k, int32_t *out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  unsigned long long v[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int32_t i = 128 * wave + 64 * r + lane;
+    v[r] = i < kk ? sel[i] : 0ull;
+  }
+  __syncthreads();                           // sel is the exchange buffer from here
+  bitonic512_sort<2>(v, wave, sel);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int32_t i = 128 * wave + 64 * r + lane;
+    if (i < kk) out[i] = (int32_t)(~(uint32_t)(v[r] & 0xFFFFFFFFull));
+  }
+  for (int32_t i = kk + tid; i < k; i += kTkThreads) out[i] = -1;
+}
+
 template <int R, bool BY_ID>
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float *scores, int64_t ld, const int32_t *n_valid,
-                                                        int32_t k, int32_t *ids_out, int32_t *cnt_out) {
+                                                        int32_t k, int32_t *ids_out, int32_t *cnt_out,
+                                                        int32_t few_rows) {
   __shared__ TopkSmem sm;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -464,7 +547,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float *scores, i
   __syncthreads();
   // -- sort the kk selected pairs, descending, and write the ids
   if (kk <= 512) {
-    rank_write(sm.sel, kk, k, out);
+    if (few_rows) rank_write_net(sm.sel, kk, k, out);
+    else rank_write_runs(sm.sel, kk, k, out);
   } else if (kk <= 1024) {
     sort_write<4>(sm.sel, kk, k, out);
   } else {
@@ -481,8 +565,12 @@ hipError_t launch_topk(const float *scores, int64_t ld, const int32_t *n_valid, 
   if (k < 1 || k > kTopkMax) return hipErrorInvalidValue;
   auto kernel = ld <= 4 * kTkThreads ? (by_id ? topk_kernel<4, true> : topk_kernel<4, false>)
                                      : (by_id ? topk_kernel<16, true> : topk_kernel<16, false>);
+  // rows that leave compute units idle: the shortest sort chain; more rows:
+  // the sort with the least work
+  const int32_t cus = device_cu_count();
+  const int32_t few_rows = (cus > 0 && rows <= cus) ? 1 : 0;
   hipLaunchKernelGGL(kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream, scores, ld, n_valid, k, ids_out,
-                     cnt_out);
+                     cnt_out, few_rows);
   return hipGetLastError();
 }
 

@@ -108,6 +108,24 @@ def test_topk_then_attention(by_id):
     assert rep.ok, rep
 
 
+@pytest.mark.parametrize("rows", [64, 600])
+def test_topk_both_sort_paths(rows):
+    """A launch with at most as many rows as compute units orders each row's
+    selection with one network over the workgroup, a larger launch with
+    per-wave runs and searches: both on ties, signed zeros, infinities, NaN
+    and subnormals, and on normal scores, with selections of up to 512."""
+    rng = np.random.default_rng(rows)
+    scores = rng.integers(-3, 4, size=(rows, 1024)).astype(np.float32)
+    pool = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e-40, -1e-40], dtype=np.float32)
+    pick = rng.random(scores.shape) < 0.15
+    scores[pick] = rng.choice(pool, size=int(pick.sum()))
+    half = rows // 2
+    scores[half:] = rng.standard_normal((rows - half, 1024)).astype(np.float32)
+    n_valid = rng.integers(0, 1100, size=rows)
+    for k in (100, 512):
+        _check(scores, n_valid, k, f"sort paths rows={rows} k={k}")
+
+
 @pytest.mark.parametrize("shape", ["topk_decode", "topk_prefill"])
 def test_topk_bench_shapes(shape):
     """The two shapes bench.py times, with its seed and launch: 32 rows of
