@@ -67,15 +67,15 @@ constexpr int kWSt = 2;                    // LDS stages per wave
 constexpr int64_t kCmpBit = int64_t(1) << 62;
 
 // DH: the workgroup forms one half of O's dimensions and stages only that
-// half of each V row (128 bytes).
-// DH also gives each wave three stages (two tiles' loads in flight while
-// it computes one); the list and page-table rows, read only while the rows
-// are formed, share the stages' memory.
+// half of each V row (128 bytes).  The list and page-table rows, read only
+// while the rows are formed, share the stages' memory.  Two stages per wave
+// (one tile's loads in flight while the other computes): a third stage, with
+// two tiles' loads in flight, was no faster and slowed the e4m3 pages.
 template <bool DH>
 struct RowsSmem {
   static constexpr int kVRowB = DH ? kRowB / 2 : kRowB;
   static constexpr int kOD = DH ? kD / 2 : kD;        // output dimensions of the workgroup
-  static constexpr int kSt = DH ? 3 : kWSt;           // LDS stages per wave
+  static constexpr int kSt = kWSt;                    // LDS stages per wave
   union {
     struct {
       alignas(16) uint8_t k[kWaves][kSt][kTileB];
@@ -333,9 +333,6 @@ void attn_decode_rows_kernel(const Params p) {
     } else {
       wait_vmcnt<0>();
     }
-    // three stages: tile t+2 takes the stage of tile t-1, whose LDS reads
-    // are complete, and loads while tile t computes
-    if (NST == 3 && t + 2 < ntw) issue(t + 2);
     uint8_t *Kt = sm.u.t.k[wave][st];
     uint8_t *Vt = sm.u.t.v[wave][st];
     const uint32_t tm = (uint32_t)__ballot(lane < 32 && row_valid(sm.row[kPT * j + (lane & 31)]));
@@ -410,9 +407,9 @@ void attn_decode_rows_kernel(const Params p) {
         vs[4 * q4] = v4.x, vs[4 * q4 + 1] = v4.y, vs[4 * q4 + 2] = v4.z, vs[4 * q4 + 3] = v4.w;
       }
     }
-    // every LDS read of the stage is in: with two stages it takes tile t+2
+    // every LDS read of the stage is in: it takes tile t+2
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (NST == 2 && t + 2 < ntw) issue(t + 2);
+    if (t + 2 < ntw) issue(t + 2);
 
     f32x16 s = f32x16{};
 #pragma unroll
