@@ -208,7 +208,7 @@ def parse_args(argv=None):
 
 DEFAULTS = {   # (num_splits, heads_per_block, queries_per_block) per workload; 0 = library choice
     "decode_csa": (1, 0, 0), "decode_hca": (1, 0, 0), "mixed_fp8": (1, 0, 0), "prefill_csa": (1, 0, 0),
-    "tiny": (1, 0, 0), "decode_latent": (4, 0, 0),
+    "tiny": (1, 0, 0), "decode_latent": (5, 0, 0),
 }
 
 
