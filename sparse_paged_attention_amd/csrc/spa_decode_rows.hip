@@ -202,16 +202,15 @@ void attn_decode_rows_kernel(const Params p) {
         else if (lead)
           flag_error(p, kErrPage);
       }
-      if constexpr (FP8) {
-        sm.row[r] = er;
-      } else {
-        // bf16 pages: the row's K byte address, its pool in the two low
-        // bits (rows are 16-byte aligned): 0 raw, 1 compressed, 2 masked
-        // (the zero row)
+      {
+        // the row's K byte address (bf16 rows kRowB bytes apart, e4m3 code
+        // rows kD), its pool in the two low bits (rows are 16-byte aligned):
+        // 0 raw, 1 compressed, 2 masked (the zero row)
         const bool cmpr = (er & kCmpBit) != 0;
         const uint64_t base = (uint64_t)(uintptr_t)(cmpr ? p.k_cmp : p.k_raw);
+        const uint64_t stride = (FP8 && cmpr) ? kD : kRowB;
         sm.row[r] = er < 0 ? (int64_t)((uint64_t)(uintptr_t)kZeroRow | 2u)
-                           : (int64_t)((base + (uint64_t)(er & ~kCmpBit) * kRowB) | (cmpr ? 1u : 0u));
+                           : (int64_t)((base + (uint64_t)(er & ~kCmpBit) * stride) | (cmpr ? 1u : 0u));
       }
     }
   }
@@ -222,13 +221,13 @@ void attn_decode_rows_kernel(const Params p) {
   const uint8_t *const kcmp = in_sgpr(p.k_cmp), *const vcmp = in_sgpr(p.v_cmp);
   const int32_t ntw = T > wave ? (T - wave + kWaves - 1) / kWaves : 0;
   auto tile_of = [&](int t) { return wave + kWaves * t; };
-  // V byte address of a row from its stored K address (bf16 pages)
+  // V byte address of a row from its stored K address
   const int64_t dv_raw = vraw - kraw, dv_cmp = vcmp - kcmp;
   auto v_of = [&](uint64_t a) -> const uint8_t * {
     const uint32_t tag = (uint32_t)a & 3u;
     return (const uint8_t *)(uintptr_t)((a & ~(uint64_t)3) + (uint64_t)(tag == 0 ? dv_raw : tag == 1 ? dv_cmp : 0));
   };
-  auto row_valid = [&](int64_t v) -> bool { return FP8 ? v >= 0 : ((uint32_t)v & 3u) != 2u; };
+  auto row_valid = [&](int64_t v) -> bool { return ((uint32_t)v & 3u) != 2u; };
   auto is_f8 = [&](int t) { return FP8 && tile_of(t) < nf8; };
   constexpr int NST = Smem::kSt;
   auto issue = [&](int t) {
@@ -247,24 +246,30 @@ void attn_decode_rows_kernel(const Params p) {
         for (int n = 0; n < 2; ++n) eh[n] = sm.row[kPT * j + 16 * n + lane / 4];
       }
       const int64_t es = sm.row[kPT * j + (lane & 31)];
+      // an e4m3 tile's rows are compressed (K codes at the stored address,
+      // V codes the pools' K-to-V distance on) or masked (the zero row, whose
+      // first 128 bytes every piece below stays within)
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const int64_t er = e8[n];
-        const int64_t off = (er & ~kCmpBit) * kD + (((lane % 8) ^ f8_swz(8 * n + lane / 8)) * 16);
-        const uint8_t *z = kZeroRow + (lane % 8) * 16;
-        dma16(er >= 0 ? kcmp + off : z, sm.u.t.k[wave][st] + 8 * n * kD);
-        if constexpr (!DH) dma16(er >= 0 ? vcmp + off : z, sm.u.t.v[wave][st] + 8 * n * kD);
+        const uint64_t a = (uint64_t)e8[n];
+        const uint8_t *src =
+            (const uint8_t *)(uintptr_t)(a & ~(uint64_t)3) + (((lane % 8) ^ f8_swz(8 * n + lane / 8)) * 16);
+        dma16(src, sm.u.t.k[wave][st] + 8 * n * kD);
+        if constexpr (!DH) dma16(src + ((a & 3u) == 1u ? dv_cmp : 0), sm.u.t.v[wave][st] + 8 * n * kD);
       }
       if constexpr (DH) {
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-          const int64_t er = eh[n];
-          const int64_t off = (er & ~kCmpBit) * kD + kD / 2 * dh + (((lane % 4) ^ f8h_swz(16 * n + lane / 4)) * 16);
-          dma16(er >= 0 ? vcmp + off : kZeroRow + (lane % 4) * 16, sm.u.t.v[wave][st] + 16 * n * (kD / 2));
+          const uint64_t a = (uint64_t)eh[n];
+          const uint8_t *src = (const uint8_t *)(uintptr_t)(a & ~(uint64_t)3) + ((a & 3u) == 1u ? dv_cmp : 0) +
+                               kD / 2 * dh + (((lane % 4) ^ f8h_swz(16 * n + lane / 4)) * 16);
+          dma16(src, sm.u.t.v[wave][st] + 16 * n * (kD / 2));
         }
       }
+      // the row's scale, its index from the code address
       const float *scl = lane < 32 ? p.k_cmp_scale : p.v_cmp_scale;
-      dma4(es >= 0 ? (const void *)(scl + (es & ~kCmpBit)) : (const void *)(kZeroRow + 4 * (lane & 31)),
+      const uint64_t row8 = (((uint64_t)es & ~(uint64_t)3) - (uint64_t)(uintptr_t)kcmp) / kD;
+      dma4(((uint32_t)es & 3u) == 1u ? (const void *)(scl + row8) : (const void *)(kZeroRow + 4 * (lane & 31)),
            sm.f8s[wave][st]);
       return;
     }
@@ -280,17 +285,9 @@ void attn_decode_rows_kernel(const Params p) {
       const int r = 4 * n + lane / kChunks;
       const int64_t er = ek[n];
       const int cs = ((lane % kChunks) ^ swz<kChunks>(r)) * 16;
-      if constexpr (FP8) {
-        const bool cmp = (er & kCmpBit) != 0;
-        const int64_t off = (er & ~kCmpBit) * kRowB + cs;
-        dma16(er >= 0 ? (cmp ? kcmp : kraw) + off : kZeroRow + cs, sm.u.t.k[wave][st] + 4 * n * kRowB);
-        if constexpr (!DH)
-          dma16(er >= 0 ? (cmp ? vcmp : vraw) + off : kZeroRow + cs, sm.u.t.v[wave][st] + 4 * n * kRowB);
-      } else {
-        const uint64_t a = (uint64_t)er;
-        dma16((const uint8_t *)(uintptr_t)(a & ~(uint64_t)3) + cs, sm.u.t.k[wave][st] + 4 * n * kRowB);
-        if constexpr (!DH) dma16(v_of(a) + cs, sm.u.t.v[wave][st] + 4 * n * kRowB);
-      }
+      const uint64_t a = (uint64_t)er;
+      dma16((const uint8_t *)(uintptr_t)(a & ~(uint64_t)3) + cs, sm.u.t.k[wave][st] + 4 * n * kRowB);
+      if constexpr (!DH) dma16(v_of(a) + cs, sm.u.t.v[wave][st] + 4 * n * kRowB);
     }
     if constexpr (DH) {
       // the workgroup's half of each V row: 8 rows of 128 bytes per load
@@ -298,15 +295,7 @@ void attn_decode_rows_kernel(const Params p) {
       for (int n = 0; n < 4; ++n) {
         const int r = 8 * n + lane / kVChunks;
         const int cs = ((lane % kVChunks) ^ swz<kVChunks>(r)) * 16;
-        const uint8_t *src;
-        if constexpr (FP8) {
-          const int64_t er = ev[n];
-          src = er >= 0 ? ((er & kCmpBit) != 0 ? vcmp : vraw) + (er & ~kCmpBit) * kRowB + kVRowB * dh + cs
-                        : kZeroRow + cs;
-        } else {
-          src = v_of((uint64_t)ev[n]) + kVRowB * dh + cs;
-        }
-        dma16(src, sm.u.t.v[wave][st] + 8 * n * kVRowB);
+        dma16(v_of((uint64_t)ev[n]) + kVRowB * dh + cs, sm.u.t.v[wave][st] + 8 * n * kVRowB);
       }
     }
   };

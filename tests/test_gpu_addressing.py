@@ -115,8 +115,11 @@ def test_decode_kernel_beyond_4gib(splits):
     _forward_check(synth.make_workload("decode_csa", batch=4), f"decode S{splits}", num_splits=splits)
 
 
-def test_decode_kernel_e4m3_beyond_4gib():
-    _forward_check(synth.make_workload("mixed_fp8", batch=3), "decode e4m3 S4", num_splits=4)
+@pytest.mark.parametrize("splits", [1, 4])
+def test_decode_kernel_e4m3_beyond_4gib(splits):
+    """S 1: the one-pass kernel (e4m3 rows kept as code addresses); S 4: the
+    slice kernel and the merge."""
+    _forward_check(synth.make_workload("mixed_fp8", batch=3), f"decode e4m3 S{splits}", num_splits=splits)
 
 
 def test_decode_all_groups_beyond_4gib():
