@@ -396,9 +396,9 @@ void attn_decode_rows_kernel(const Params p) {
         vs[4 * q4] = v4.x, vs[4 * q4 + 1] = v4.y, vs[4 * q4 + 2] = v4.z, vs[4 * q4 + 3] = v4.w;
       }
     }
-    // every LDS read of the stage is in: it takes tile t+2
+    // every LDS read of the stage is in (tile t+2 takes it once tile t's
+    // products are issued, so that its loads do not hold them back)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (t + 2 < ntw) issue(t + 2);
 
     f32x16 s = f32x16{};
 #pragma unroll
@@ -434,6 +434,7 @@ void attn_decode_rows_kernel(const Params p) {
       for (int k2 = 0; k2 < 2; ++k2)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[db][k2]), pb[k2], acc[db],
                                                          0, 0, 0);
+    if (t + 2 < ntw) issue(t + 2);
   }
 
   // ---- the four states meet: wave w forms dimensions 32w .. 32w+31 of
