@@ -228,16 +228,19 @@ def eager_ms(launch, n):
     return ms, np.array([ms])
 
 
-def graph_replay_ms(launch, steps, reps=1, rounds=2):
+def graph_replay_ms(launch, steps, reps=1, rounds=2, warm_s=0.3):
     """Per-call time of `launch(stream, k)` from HIP graph replays.
 
     Call k uses replica k % reps.  The calls are captured in G = ceil(reps /
     steps) graphs of exactly `steps` calls (graph g holds calls g*steps ..
     g*steps + steps - 1), so replaying the graphs in turn reads every replica
-    once before any is read again.  After one untimed replay of every graph,
-    each measurement is one replay of one graph (HIP events on the capture
-    stream); `rounds` passes over the G graphs.  Returns (median ms per call,
-    per-measurement ms per call, G)."""
+    once before any is read again.  The graphs are replayed in turn, untimed,
+    until at least `warm_s` seconds have passed (one pass at least), so that
+    the chip's clocks have settled whatever `steps` is: short passes timed
+    right after the warm-up steps ran up to 17% slower per call on prefill.
+    Then each measurement is one replay of one graph (HIP events on the
+    capture stream); `rounds` passes over the G graphs.  Returns (median ms
+    per call, per-measurement ms per call, G)."""
     import numpy as np
     import torch
     G = max(1, -(-reps // steps))
@@ -255,9 +258,13 @@ def graph_replay_ms(launch, steps, reps=1, rounds=2):
                     launch(cs.cuda_stream, g * steps + k)
             graphs.append(graph)
         torch.cuda.synchronize()
-        for graph in graphs:
-            graph.replay()
-        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while True:
+            for graph in graphs:
+                graph.replay()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= warm_s:
+                break
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * G * rounds)]
         n = 0
         for _ in range(rounds):
